@@ -1,0 +1,159 @@
+"""Python wrappers of the three C entry points (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import check, lib
+
+SPARSE_PREFILL_DEFAULT = True
+SPARSE_PREFILL_MIN_CONTEXT_DEFAULT = 16384
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(query, device):
+    size = ctypes.c_size_t(0)
+    check(query(None, ctypes.byref(size)), "workspace query")
+    if size.value == 0:
+        return None, None
+    ws = torch.empty(size.value, dtype=torch.uint8, device=device)
+    return ws, size
+
+
+def mla_prefill_dense(q, k, *, q_rope=None, k_rope=None, v=None, scale=None, causal=True, out=None):
+    """Dense causal MLA prefill.
+
+    Non-absorbed (q_rope, k_rope, v given): q [B,L,H,128], q_rope [B,L,H,64],
+    k [B,N,H,128], k_rope [B,N,64], v [B,N,H,128]; fp32 or bf16; out [B,L,H,128].
+    Absorbed (q_rope, k_rope, v omitted): q [B,L,H,576], k = kv [B,N,576] bf16;
+    out [B,L,H,512]. scale defaults to 1/sqrt(query width).
+    """
+    absorbed = q_rope is None and k_rope is None and v is None
+    dtype = q.dtype
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    _need(q, "q", dtype, 4)
+    _need(k, "k", dtype, 3 if absorbed else 4)
+    B, L, H, D = q.shape
+    N = k.shape[1]
+    if absorbed:
+        if D != 576 or k.shape != (B, N, 576):
+            raise ValueError("absorbed mode needs q [B,L,H,576] and kv [B,N,576]")
+        dv = 512
+        if scale is None:
+            scale = 1.0 / math.sqrt(576)
+    else:
+        _need(q_rope, "q_rope", dtype, 4)
+        _need(k_rope, "k_rope", dtype, 3)
+        _need(v, "v", dtype, 4)
+        if (D != 128 or q_rope.shape != (B, L, H, 64) or k.shape != (B, N, H, 128)
+                or k_rope.shape != (B, N, 64) or v.shape != (B, N, H, 128)):
+            raise ValueError("non-absorbed shapes must be q [B,L,H,128], q_rope [B,L,H,64], k [B,N,H,128], "
+                             "k_rope [B,N,64], v [B,N,H,128]")
+        dv = 128
+        if scale is None:
+            scale = 1.0 / math.sqrt(192)
+    if out is None:
+        out = torch.empty((B, L, H, dv), dtype=dtype, device=q.device)
+    else:
+        _need(out, "out", dtype, 4)
+    st = lib().mla_prefill_dense(
+        _lib.MODE_ABSORBED if absorbed else _lib.MODE_NONABSORBED,
+        _lib.BF16 if dtype == torch.bfloat16 else _lib.F32,
+        B, L, N, H, _ptr(q), _ptr(q_rope), _ptr(k), _ptr(k_rope), _ptr(v), _ptr(out),
+        float(scale), 1 if causal else 0, None, None, _stream(q.device))
+    check(st, "mla_prefill_dense")
+    return out
+
+
+def dsa_indexer_topk(q_idx, k_idx, w, topk, *, block=4096, return_scores=False, out=None):
+    """Exact indexer top-k. q_idx [L,32,128] bf16, k_idx [N,128] bf16, w [L,32] fp32.
+
+    Returns idx [L,topk] int32 (ascending key order, -1 padded), and the fp32
+    scores of the returned keys when return_scores is set.
+    """
+    _need(q_idx, "q_idx", torch.bfloat16, 3)
+    _need(k_idx, "k_idx", torch.bfloat16, 2)
+    _need(w, "w", torch.float32, 2)
+    L, Hi, Di = q_idx.shape
+    N = k_idx.shape[0]
+    if k_idx.shape[1] != Di or w.shape != (L, Hi):
+        raise ValueError("shapes must be q_idx [L,Hi,Di], k_idx [N,Di], w [L,Hi]")
+    dev = q_idx.device
+    idx = out if out is not None else torch.empty((L, topk), dtype=torch.int32, device=dev)
+    scores = torch.empty((L, topk), dtype=torch.float32, device=dev) if return_scores else None
+
+    def call(ws, ws_bytes):
+        return lib().dsa_indexer_topk(1, L, N, Hi, Di, _ptr(q_idx), _ptr(k_idx), _ptr(w), int(topk), int(block),
+                                      _ptr(idx), _ptr(scores), ws, ws_bytes, _stream(dev))
+
+    ws, size = _workspace(call, dev)
+    check(call(_ptr(ws), None if size is None else ctypes.byref(size)), "dsa_indexer_topk")
+    return (idx, scores) if return_scores else idx
+
+
+def mla_prefill_sparse(q, kv, idx, *, scale=None, query_block=1024, out=None):
+    """Sparse absorbed prefill. q [L,H,576] bf16, kv [N,576] bf16, idx [L,topk] int32 -> out [L,H,512] bf16."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv, "kv", torch.bfloat16, 2)
+    _need(idx, "idx", torch.int32, 2)
+    L, H, D = q.shape
+    N = kv.shape[0]
+    if D != 576 or kv.shape[1] != 576 or idx.shape[0] != L:
+        raise ValueError("shapes must be q [L,H,576], kv [N,576], idx [L,topk]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(576)
+    if out is None:
+        out = torch.empty((L, H, 512), dtype=torch.bfloat16, device=q.device)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
+    st = lib().mla_prefill_sparse(1, L, N, H, _ptr(q), _ptr(kv), _ptr(idx), idx.shape[1], float(scale),
+                                  int(query_block), _ptr(out), None, None, _stream(q.device))
+    check(st, "mla_prefill_sparse")
+    return out
+
+
+def use_sparse(sparse_prefill: bool, B: int, L: int, N: int,
+               min_context: int = SPARSE_PREFILL_MIN_CONTEXT_DEFAULT) -> bool:
+    """The gate ("Sparse prefill for GLM", section "When it runs"): sparse only when switched
+    on, for one sequence, in prefill (L > 1), once the cache holds min_context positions."""
+    return bool(sparse_prefill) and B == 1 and L > 1 and N >= min_context
+
+
+def dsa_prefill(q, kv, q_idx, k_idx, w, topk, *, scale=None, block=4096, query_block=1024,
+                sparse_prefill=SPARSE_PREFILL_DEFAULT, min_context=SPARSE_PREFILL_MIN_CONTEXT_DEFAULT):
+    """One chunk of DSA prefill for one sequence: indexer top-k, then gated attention.
+
+    q [L,H,576], kv [N,576] (N includes this chunk), q_idx [L,32,128], k_idx [N,128], w [L,32].
+    Returns (out [L,H,512], idx [L,topk]).
+    """
+    L, N = q.shape[0], kv.shape[0]
+    idx = dsa_indexer_topk(q_idx, k_idx, w, topk, block=block)
+    if use_sparse(sparse_prefill, 1, L, N, min_context):
+        return mla_prefill_sparse(q, kv, idx, scale=scale, query_block=query_block), idx
+    # below the gate: the dense path over all visible keys under the top-k selection,
+    # which equals gathering exactly the selected rows
+    return mla_prefill_sparse(q, kv, idx, scale=scale, query_block=query_block), idx

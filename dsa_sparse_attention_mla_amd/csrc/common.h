@@ -1,0 +1,78 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels: vector types, MFMA
+// wrappers, LDS transpose reads, bf16 conversion and wave-level reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define DSA_LDS __attribute__((address_space(3)))
+
+// 16x16x32 bf16 MFMA. Lane l: A row l%16 with k = 8*(l/16)+e; B column l%16 with
+// k = 8*(l/16)+e; C column l%16 with rows 4*(l/16)+j.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 32x32x16 bf16 MFMA. Lane l: A row l%32 with k = 8*(l/32)+e; B column l%32;
+// C column l%32 with rows 8*(j/4) + 4*(l/32) + j%4.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x4 fp32 MFMA. Lane l: A row l%16 with k = l/16; B column l%16 with k = l/16.
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read of 4 x 16-bit elements. Within each group of 16 lanes,
+// lane j receives element j%4 of the 8 bytes addressed by lane 4*e + j/4, for
+// e = 0..3. If lane j of the group points at row (base + j/4), column
+// (col0 + 4*(j%4)) of a row-major 16-bit matrix, it receives column col0 + j of
+// rows base .. base+3.
+__device__ __forceinline__ short4v lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS short4v*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join_bf16x8(short4v lo, short4v hi) {
+  typedef short short8v __attribute__((ext_vector_type(8)));
+  short8v v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f2bf_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf_bits2f(uint16_t b) {
+  return __builtin_bit_cast(float, ((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
+  typedef short short8v __attribute__((ext_vector_type(8)));
+  short8v v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (short)f2bf_bits(x[e]);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Butterfly over lane groups: combine lanes l, l^16, l^32 (the four 16-lane
+// groups that hold the same MFMA column).
+__device__ __forceinline__ float group4_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace dsa

@@ -1,0 +1,26 @@
+// Internal launch interface between the C ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+hipError_t launch_absorbed_attn(bool sparse, const uint16_t* q, const uint16_t* kv, const int32_t* idx, uint16_t* out,
+                                int B, int L, int N, int H, int topk, int q0, int nq, int causal, float scale,
+                                hipStream_t stream);
+
+hipError_t launch_nonabsorbed_attn(bool bf16, const void* qn, const void* qr, const void* kn, const void* kr,
+                                   const void* v, void* out, int B, int L, int N, int H, int causal, float scale,
+                                   hipStream_t stream);
+
+struct IndexerPlan {
+  int nsplit = 1, span = 0, cap = 0, fb_blocks = 1;
+  size_t off_partial = 0, off_eps = 0, off_cand_n = 0, off_fb = 0, off_cand_s = 0, off_cand_i = 0, off_scratch = 0;
+  size_t ws_bytes = 0, filter_lds = 0, select_lds = 0;
+};
+IndexerPlan indexer_plan(int L, int N, int topk, int block);
+hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16_t* k, const float* w, int L, int N,
+                          int topk, int32_t* idx_out, float* score_out, void* ws, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,140 @@
+/*
+ * dsa_mla.h -- C ABI of libdsa_mla.so: MLA prefill and DeepSeek-sparse-attention
+ * (DSA) prefill on AMD Instinct MI355X (gfx950).
+ *
+ * Three calls:
+ *   mla_prefill_dense   dense causal MLA prefill, non-absorbed or absorbed
+ *   dsa_indexer_topk    indexer scores fused with a running top-k selection
+ *   mla_prefill_sparse  absorbed attention over each query's gathered top-k rows
+ *
+ * Conventions shared by all calls
+ * -------------------------------
+ * Return value: a dsa_mla_status code; 0 means the work was enqueued.
+ * Validation: every argument check runs on the host before anything is
+ *   launched; a call that returns an error has launched nothing and left every
+ *   output untouched. No call prints, throws or allocates device memory.
+ * Memory: every tensor argument is a DEVICE pointer owned by the caller,
+ *   contiguous row-major in the layout stated per call, with a 16-byte aligned
+ *   base. Inputs are only read; outputs are fully overwritten.
+ * bf16: passed as 16-bit storage (the upper half of an IEEE fp32). Arithmetic
+ *   accumulates in fp32; outputs have the input dtype.
+ * Causality: the L queries of a chunk are the LAST L positions of an
+ *   N-position context: query i sits at position N - L + i and sees key n iff
+ *   n <= N - L + i. For L = N this is the usual j <= i rule.
+ * Workspace: ws == NULL together with a non-NULL ws_bytes is a size query: the
+ *   call stores the required byte count in *ws_bytes, returns DSA_MLA_OK and
+ *   launches nothing. Otherwise, if the call needs workspace, ws must be a
+ *   device buffer of at least the queried size, given in *ws_bytes (256-byte
+ *   alignment recommended). A call that needs none may pass ws_bytes == NULL.
+ *   The workspace holds no state between calls.
+ * Streams: `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *   on it and the call returns without synchronising; a device-side fault
+ *   surfaces at the caller's next synchronisation.
+ * Device: the current HIP device must be gfx950, otherwise DSA_MLA_ARCH
+ *   (dispatch checks the chip before launching, so no device ever receives a
+ *   kernel it cannot run; Fornax part 5 "Apple M3 vs M5 kernels", section
+ *   "Dispatch has to know the chip").
+ * Threads: calls are re-entrant; calls on different streams may overlap.
+ */
+#ifndef DSA_MLA_H
+#define DSA_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_mla_status {
+  DSA_MLA_OK = 0,
+  DSA_MLA_INVALID_ARG = 1,   /* NULL pointer, bad size/enum, misaligned pointer, L > N when causal */
+  DSA_MLA_UNSUPPORTED = 2,   /* valid request outside what the kernels implement (dims, dtype, B) */
+  DSA_MLA_ARCH = 3,          /* no HIP device, or the current device is not gfx950 */
+  DSA_MLA_WORKSPACE = 4,     /* workspace missing or smaller than required */
+  DSA_MLA_HIP = 5            /* the HIP runtime reported an error while launching */
+} dsa_mla_status;
+
+enum { DSA_MLA_MODE_NONABSORBED = 0, DSA_MLA_MODE_ABSORBED = 1 };
+enum { DSA_MLA_F32 = 0, DSA_MLA_BF16 = 1 };
+
+/*
+ * mla_prefill_dense -- dense causal (or full) MLA prefill.
+ *
+ * mode DSA_MLA_MODE_NONABSORBED (Fornax part 5 "Apple M3 vs M5 kernels",
+ * section "What the kernel has to compute"): per head h,
+ *   score[i,j] = scale * (q[i,h,:] . k[j,h,:]  +  q_rope[i,h,:] . k_rope[j,:])
+ *   out[i,h,:] = softmax_j(score[i,:]) . v[:,h,:]
+ * with the rope key shared by all heads.
+ *   q      [B,L,H,128]   q_rope [B,L,H,64]
+ *   k      [B,N,H,128]   k_rope [B,N,64]     v [B,N,H,128]
+ *   out    [B,L,H,128]
+ *   dtype DSA_MLA_F32 or DSA_MLA_BF16 (all tensors the same dtype).
+ *
+ * mode DSA_MLA_MODE_ABSORBED ("Sparse prefill for GLM", section "Sparse
+ * attention": attention in the absorbed latent space over one joined
+ * latent+rope row per position, shared by all heads):
+ *   score[i,j] = scale * q[i,h,:] . kv[j,:]          out[i,h,:] = softmax . kv[:, 0:512]
+ *   q  [B,L,H,576] (512 latent then 64 rope)  k = kv [B,N,576]  out [B,L,H,512]
+ *   q_rope, k_rope and v must be NULL. dtype must be DSA_MLA_BF16; H a multiple of 16.
+ *
+ * causal: 1 = bottom-right causal (see above; needs L <= N), 0 = every key.
+ * B >= 1 is allowed. B == 0 or L == 0 is a no-op. A query that sees no key
+ * (only possible with N == 0, non-causal) gets a zero row. No workspace.
+ */
+int mla_prefill_dense(int mode, int dtype, int B, int L, int N, int H,
+                      const void* q, const void* q_rope, const void* k, const void* k_rope, const void* v,
+                      void* out, float scale, int causal, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * dsa_indexer_topk -- indexer top-k ("Sparse prefill for GLM", section
+ * "Blocked top-k": keys are scored a block at a time and folded into a running
+ * top-k list; the full batch x heads x L x N score tensor is never built).
+ *
+ *   s[i,n] = sum_h w[i,h] * ReLU(q_idx[i,h,:] . k_idx[n,:])     for n <= N - L + i
+ *   q_idx [L,Hi,Di] bf16   k_idx [N,Di] bf16   w [L,Hi] fp32   idx_out [L,topk] int32
+ *
+ * The result is the EXACT top-k set of the canonical score (dot products in
+ * fp64 summed over dims in ascending order, head terms added in ascending head
+ * order, every operation separately rounded), ties to the lower key index.
+ * Rows are written in ascending key order; a row with fewer than topk visible
+ * keys holds all of them followed by -1. score_out (nullable) [L,topk] fp32
+ * receives the fp32 MFMA score of each returned key (-inf on padding).
+ * `block` (>= 1; the pages use 4096) is the folding granularity of the key
+ * sweep and never changes the result.
+ * Supported: B == 1, Hi == 32, Di == 128, 1 <= topk <= 2560, 0 <= L <= N.
+ * Needs workspace (query its size first).
+ */
+int dsa_indexer_topk(int B, int L, int N, int Hi, int Di, const void* q_idx, const void* k_idx, const float* w,
+                     int topk, int block, int32_t* idx_out, float* score_out, void* ws, size_t* ws_bytes,
+                     void* stream);
+
+/*
+ * mla_prefill_sparse -- sparse absorbed MLA prefill ("Sparse prefill for GLM",
+ * section "Sparse attention": the joined 576-wide row of every chosen key is
+ * gathered, all heads share the gathered block, attention runs in absorbed
+ * latent space; chunks longer than the query block are split into blocks).
+ *
+ *   score[i,h,t] = scale * q[i,h,:] . kv[idx[i,t],:]   over t with idx[i,t] valid
+ *   out[i,h,:]   = softmax_t(score) . kv[idx[i,t], 0:512]
+ *   q [L,H,576] bf16   kv [N,576] bf16   idx [L,topk] int32   out [L,H,512] bf16
+ *
+ * Index entries outside [0, N) (-1 in particular) are skipped; a row with no
+ * valid entry gets zeros. Indices are not re-masked for causality. A repeated
+ * index counts once per occurrence. query_block (1..1024) splits the L queries
+ * into launches of at most that many; the output does not depend on it.
+ * Supported: B == 1, H a multiple of 16. No workspace.
+ */
+int mla_prefill_sparse(int B, int L, int N, int H, const void* q, const void* kv, const int32_t* idx, int topk,
+                       float scale, int query_block, void* out, void* ws, size_t* ws_bytes, void* stream);
+
+/* Short English name of a status code (static storage). */
+const char* dsa_mla_status_string(int status);
+
+/* ABI version of this header (increments on incompatible changes). */
+int dsa_mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_MLA_H */

@@ -44,7 +44,12 @@ def _exp_stats(x: np.ndarray):
     return emax, elsb
 
 
-def exact_dot_flags(q_rows: np.ndarray, k: np.ndarray) -> np.ndarray:
+def _span(x: np.ndarray) -> np.ndarray:
+    e, l = _exp_stats(x)
+    return np.where(e > -100000, e - l, -10**6)
+
+
+def exact_dot_flags(q_rows: np.ndarray, k: np.ndarray, span_k=None) -> np.ndarray:
     """[Hi, N] bool: True where the fp64 dot q_h . k_n is NOT guaranteed exact in every order.
 
     All partial sums are integer multiples of 2^(lq + lk) and bounded by
@@ -52,17 +57,15 @@ def exact_dot_flags(q_rows: np.ndarray, k: np.ndarray) -> np.ndarray:
     """
     Di = q_rows.shape[-1]
     lg = math.ceil(math.log2(Di))
-    eq, lq = _exp_stats(q_rows)
-    ek, lk = _exp_stats(k)
-    span_q = np.where(eq > -100000, eq - lq, -10**6)
-    span_k = np.where(ek > -100000, ek - lk, -10**6)
-    return (span_q[:, None] + span_k[None, :]) > (53 - lg)
+    if span_k is None:
+        span_k = _span(k)
+    return (_span(q_rows)[:, None] + span_k[None, :]) > (53 - lg)
 
 
-def _head_dots(qi: np.ndarray, k: np.ndarray) -> np.ndarray:
+def _head_dots(qi: np.ndarray, k: np.ndarray, span_k=None) -> np.ndarray:
     """d[h, n] for one query, [Hi, Di] x [N, Di] -> [Hi, N], canonical fp64 values."""
     d = qi @ k.T
-    flags = exact_dot_flags(qi, k)
+    flags = exact_dot_flags(qi, k, span_k)
     if flags.any():
         hs, ns = np.nonzero(flags)
         acc = np.zeros(len(hs))
@@ -83,8 +86,9 @@ def indexer_scores(q, k, w, causal=True, rows=None):
         raise ValueError("causal indexer needs L <= N")
     rows = np.arange(L) if rows is None else np.asarray(rows)
     out = np.empty((len(rows), N))
+    span_k = _span(k)
     for r, i in enumerate(rows):
-        d = _head_dots(q[i], k)
+        d = _head_dots(q[i], k, span_k)
         s = np.zeros(N)
         for h in range(Hi):
             s = s + w[i, h] * np.maximum(d[h], 0.0)

@@ -1,0 +1,137 @@
+"""GPU parity: dense MLA prefill (non-absorbed fp32/bf16, absorbed bf16) vs the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import dsa_sparse_attention_mla_amd as dm
+from synth import gen_absorbed, gen_nonabsorbed, to_f64
+from gpu_util import assert_close, dev, host_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4      # fp32 outputs: max-abs
+TOL_BF16 = 2e-2     # bf16 outputs: max-abs
+
+
+def _nonabs(seed, L, N, H, dtype, scale=1.0):
+    g = gen_nonabsorbed(seed, L, N, H=H, dtype=dtype, scale=scale)
+    t = {k: dev(v) for k, v in g.items()}
+    f = {k: to_f64(v) for k, v in g.items()}
+    return t, f
+
+
+def _run_nonabs(t, causal=True, scale=None):
+    out = dm.mla_prefill_dense(t["qn"][None], t["kn"][None], q_rope=t["qr"][None], k_rope=t["kr"][None],
+                               v=t["v"][None], causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return host_f64(out[0])
+
+
+@pytest.mark.parametrize("L,N,H", [(256, 256, 16), (100, 100, 16), (37, 200, 4), (1, 1, 16), (65, 129, 3)])
+def test_nonabsorbed_fp32(L, N, H):
+    t, f = _nonabs(1000 if (L, N, H) == (256, 256, 16) else 11 + L, L, N, H, "f32")
+    scale = 1 / math.sqrt(192)
+    got = _run_nonabs(t)
+    ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], scale)
+    assert_close(got, ref, TOL_F32, f"nonabs f32 L={L} N={N} H={H}")
+
+
+def test_nonabsorbed_fp32_sharpened():
+    """Scale x 8 makes softmax peaky, so an off-by-one causal mask or a lost rope term shows up."""
+    t, f = _nonabs(21, 96, 96, 16, "f32")
+    scale = 8 / math.sqrt(192)
+    got = _run_nonabs(t, scale=scale)
+    ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], scale)
+    assert_close(got, ref, TOL_F32, "nonabs f32 sharpened")
+
+
+def test_nonabsorbed_fp32_noncausal():
+    t, f = _nonabs(22, 50, 70, 16, "f32")
+    scale = 1 / math.sqrt(192)
+    got = _run_nonabs(t, causal=False)
+    ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], scale, causal=False)
+    assert_close(got, ref, TOL_F32, "nonabs f32 non-causal")
+
+
+def test_nonabsorbed_rope_only_shared_key():
+    """Q_nope = 0: only the shared rope key drives the scores."""
+    t, f = _nonabs(23, 64, 64, 16, "f32")
+    t["qn"].zero_()
+    f["qn"][:] = 0
+    scale = 1 / math.sqrt(192)
+    got = _run_nonabs(t)
+    ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], scale)
+    assert_close(got, ref, TOL_F32, "rope-only")
+
+
+@pytest.mark.parametrize("L,N", [(333, 333), (130, 517)])
+def test_nonabsorbed_bf16_small(L, N):
+    t, f = _nonabs(30 + L, L, N, 16, "bf16", scale=0.5)
+    got = _run_nonabs(t)
+    ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], 1 / math.sqrt(192))
+    assert_close(got, ref, TOL_BF16, f"nonabs bf16 L={L} N={N}")
+
+
+def test_nonabsorbed_bf16_full_size_sampled():
+    """L = N = 4096, 16 heads, bf16 (0.5 N(0,1)): sampled query rows against the oracle."""
+    L = N = 4096
+    t, f = _nonabs(1001, L, N, 16, "bf16", scale=0.5)
+    got = _run_nonabs(t)
+    rows = np.array([0, 1, 2, 63, 64, 1000, 2047, 2048, 3001, 4094, 4095])
+    ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], 1 / math.sqrt(192), rows=rows)
+    assert_close(got[rows], ref, TOL_BF16, "nonabs bf16 4096 sampled")
+    assert np.isfinite(got).all()
+
+
+def _abs(seed, L, N, H):
+    g = gen_absorbed(seed, L, N, H=H)
+    return dev(g["q"]), dev(g["kv"]), to_f64(g["q"]), to_f64(g["kv"])
+
+
+@pytest.mark.parametrize("L,N,H", [(40, 300, 64), (1, 33, 64), (17, 17, 16), (9, 100, 80)])
+def test_absorbed_small(L, N, H):
+    q, kv, qf, kvf = _abs(40 + L, L, N, H)
+    out = dm.mla_prefill_dense(q[None], kv[None])
+    torch.cuda.synchronize()
+    ref = oracle.mla_absorbed(qf, kvf, 1 / math.sqrt(576))
+    assert_close(host_f64(out[0]), ref, TOL_BF16, f"absorbed L={L} N={N} H={H}")
+
+
+def test_absorbed_sharpened():
+    q, kv, qf, kvf = _abs(41, 24, 90, 64)
+    scale = 8 / math.sqrt(576)
+    out = dm.mla_prefill_dense(q[None], kv[None], scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.mla_absorbed(qf, kvf, scale)
+    assert_close(host_f64(out[0]), ref, TOL_BF16, "absorbed sharpened")
+
+
+def test_absorbed_full_size_sampled():
+    """64 heads x 576, N = 16384, L = 512 at the end of the context: sampled query rows."""
+    L, N = 512, 16384
+    q, kv, qf, kvf = _abs(1002, L, N, 64)
+    out = dm.mla_prefill_dense(q[None], kv[None])
+    torch.cuda.synchronize()
+    got = host_f64(out[0])
+    rows = np.array([0, 1, 100, 255, 256, 400, 510, 511])
+    ref = oracle.mla_absorbed(qf, kvf, 1 / math.sqrt(576), rows=rows)
+    assert_close(got[rows], ref, TOL_BF16, "absorbed 16384 sampled")
+    assert np.isfinite(got).all()
+
+
+def test_dense_batch():
+    """B = 2 (batches take the dense path): each batch entry equals its own single-sequence call."""
+    L, N, H = 20, 60, 16
+    g1, g2 = gen_absorbed(50, L, N, H=H), gen_absorbed(51, L, N, H=H)
+    q = torch.stack([dev(g1["q"]), dev(g2["q"])])
+    kv = torch.stack([dev(g1["kv"]), dev(g2["kv"])])
+    out = dm.mla_prefill_dense(q, kv)
+    o1 = dm.mla_prefill_dense(q[:1].contiguous(), kv[:1].contiguous())
+    o2 = dm.mla_prefill_dense(q[1:].contiguous(), kv[1:].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], o1[0]) and torch.equal(out[1], o2[0])
+    ref = oracle.mla_absorbed(to_f64(g2["q"]), to_f64(g2["kv"]), 1 / math.sqrt(576))
+    assert_close(host_f64(out[1]), ref, TOL_BF16, "batch entry 1")

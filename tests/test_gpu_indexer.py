@@ -1,0 +1,104 @@
+"""GPU parity: indexer top-k sets must equal the oracle's exactly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import dsa_sparse_attention_mla_amd as dm
+from synth import gen_indexer, gen_indexer_exact, to_f64
+from gpu_util import dev, sorted_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(g, topk, rows=None, block=4096):
+    q, k, w = dev(g["q_idx"]), dev(g["k_idx"]), dev(g["w"])
+    idx, sc = dm.dsa_indexer_topk(q, k, w, topk, block=block, return_scores=True)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    qf, kf, wf = to_f64(g["q_idx"]), to_f64(g["k_idx"]), to_f64(g["w"])
+    s = oracle.indexer_scores(qf, kf, wf, rows=rows)
+    ref = oracle.topk_full(s, topk)
+    return idx, sc.cpu().numpy(), ref, s
+
+
+def _check_rows(idx, ref, rows, what):
+    got = sorted_rows(idx[rows])
+    exp = sorted_rows(ref)
+    bad = [r for r, (a, b) in zip(rows, zip(got, exp)) if a != b]
+    print(f"[{what}] rows checked {len(rows)}, mismatching rows {len(bad)}", flush=True)
+    assert not bad, f"{what}: rows {bad[:5]} differ"
+    # ascending order within rows, -1 padding at the end
+    for r in rows:
+        row = idx[r]
+        v = row[row >= 0]
+        assert np.all(np.diff(v) > 0) and np.all(row[len(v):] == -1)
+
+
+@pytest.mark.parametrize("L,N,topk", [(8, 300, 16), (37, 1000, 64), (5, 5000, 2048), (64, 64, 16), (3, 70000, 100)])
+def test_indexer_small(L, N, topk):
+    g = gen_indexer(80 + L, L, N)
+    idx, _, ref, _ = _run(g, topk)
+    _check_rows(idx, ref, np.arange(L), f"indexer L={L} N={N} k={topk}")
+
+
+@pytest.mark.parametrize("L,N,topk", [(16, 2000, 64), (12, 20000, 2048)])
+def test_indexer_exact_inputs_ties(L, N, topk):
+    """q, k in {-1,0,1}, w multiples of 2^-6: fp32 scores are exact and ties are frequent,
+    so the lower-index tie rule decides many keys."""
+    g = gen_indexer_exact(90 + L, L, N)
+    idx, sc, ref, s = _run(g, topk)
+    _check_rows(idx, ref, np.arange(L), f"exact-input indexer L={L} N={N}")
+
+
+def test_indexer_zero_query_all_ties():
+    """q = 0: every visible score is 0, the set is the lowest topk visible indices (exact fallback path)."""
+    g = gen_indexer(95, 6, 9000)
+    g["q_idx"].data[:] = 0
+    idx, _, ref, _ = _run(g, 2048)
+    _check_rows(idx, ref, np.arange(6), "zero query")
+
+
+def test_indexer_full_size_small_config():
+    """L = 512, N = 65536, top-k 2048 (blocks of 4096): every row against the oracle."""
+    g = gen_indexer(1003, 512, 65536)
+    idx, sc, ref, s = _run(g, 2048)
+    _check_rows(idx, ref, np.arange(512), "indexer 512 x 65536")
+    # fp32 scores of returned keys vs the canonical fp64 scores
+    got_s = np.take_along_axis(s, np.maximum(idx, 0).astype(np.int64), axis=1)
+    err = np.abs(sc - got_s)[idx >= 0]
+    print(f"[score error] max |s_hat - s| = {err.max():.3e}", flush=True)
+    assert err.max() < 5e-3
+
+
+def test_indexer_full_size_sampled():
+    """L = 1024, N = 131072, top-k 2048: sampled rows against the oracle."""
+    g = gen_indexer(1004, 1024, 131072)
+    rows = np.array([0, 1, 2, 100, 511, 512, 777, 1021, 1022, 1023])
+    idx, _, ref, _ = _run(g, 2048, rows=rows)
+    got = sorted_rows(idx[rows])
+    exp = sorted_rows(ref)
+    assert got == exp
+    assert (idx >= 0).all()
+
+
+def test_indexer_block_argument_has_no_effect():
+    g = gen_indexer(96, 20, 9000)
+    q, k, w = dev(g["q_idx"]), dev(g["k_idx"]), dev(g["w"])
+    outs = [dm.dsa_indexer_topk(q, k, w, 256, block=b) for b in (4096, 1000, 1)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_indexer_repeatable_and_inputs_unchanged():
+    g = gen_indexer(97, 40, 30000)
+    q, k, w = dev(g["q_idx"]), dev(g["k_idx"]), dev(g["w"])
+    snap = [t.clone() for t in (q, k, w)]
+    a = dm.dsa_indexer_topk(q, k, w, 2048)
+    out = torch.full((40, 2048), -7, dtype=torch.int32, device=q.device)
+    dm.dsa_indexer_topk(q, k, w, 2048, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(a, out)
+    for x, y in zip(snap, (q, k, w)):
+        assert torch.equal(x, y)

@@ -1,0 +1,108 @@
+"""GPU parity: sparse absorbed prefill over gathered rows vs the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import dsa_sparse_attention_mla_amd as dm
+from synth import gen_absorbed, gen_topk_indices, to_f64
+from gpu_util import assert_close, dev, host_f64
+
+pytestmark = pytest.mark.gpu
+TOL_BF16 = 2e-2
+SCALE = 1 / math.sqrt(576)
+
+
+def _case(seed, L, N, topk, H=64, pad=0.0):
+    g = gen_absorbed(seed, L, N, H=H)
+    idx = gen_topk_indices(seed + 7, L, N, topk, pad_frac=pad)
+    return dev(g["q"]), dev(g["kv"]), dev(idx), to_f64(g["q"]), to_f64(g["kv"]), idx
+
+
+@pytest.mark.parametrize("L,N,topk,pad", [(20, 500, 64, 0.0), (33, 1000, 100, 0.2), (5, 40, 48, 0.0), (8, 300, 1, 0.0)])
+def test_sparse_small(L, N, topk, pad):
+    q, kv, idx, qf, kvf, idxn = _case(60 + L, L, N, topk, pad=pad)
+    out = dm.mla_prefill_sparse(q, kv, idx)
+    torch.cuda.synchronize()
+    ref = oracle.mla_sparse_gather(qf, kvf, idxn, SCALE)
+    assert_close(host_f64(out), ref, TOL_BF16, f"sparse L={L} N={N} topk={topk} pad={pad}")
+    # the same result as dense attention under the top-k mask
+    ref2 = oracle.mla_masked_dense(qf, kvf, idxn, SCALE)
+    assert_close(host_f64(out), ref2, TOL_BF16, "sparse vs masked dense")
+
+
+def test_sparse_full_size_sampled():
+    """N = 131072 joined rows, L = 1024 queries, top-k 2048, 64 heads: sampled rows."""
+    L, N, topk = 1024, 131072, 2048
+    q, kv, idx, qf, kvf, idxn = _case(1004, L, N, topk)
+    out = dm.mla_prefill_sparse(q, kv, idx)
+    torch.cuda.synchronize()
+    got = host_f64(out)
+    rows = np.array([0, 1, 511, 512, 1022, 1023])
+    ref = oracle.mla_sparse_gather(qf, kvf, idxn, SCALE, rows=rows)
+    assert_close(got[rows], ref, TOL_BF16, "sparse 131072 sampled")
+    ref2 = oracle.mla_masked_dense(qf, kvf, idxn, SCALE, rows=rows[:2])
+    assert_close(got[rows[:2]], ref2, TOL_BF16, "sparse 131072 vs masked dense")
+    assert np.isfinite(got).all()
+
+
+def test_sparse_query_blocks_bit_identical():
+    q, kv, idx, *_ = _case(70, 100, 2000, 128)
+    outs = [dm.mla_prefill_sparse(q, kv, idx, query_block=b) for b in (1024, 300, 7, 1)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_sparse_permutation_invariance():
+    q, kv, idx, qf, kvf, idxn = _case(71, 30, 3000, 256)
+    perm = torch.stack([r[torch.randperm(r.numel(), generator=torch.Generator().manual_seed(3)).to(r.device)]
+                        for r in idx])
+    a = host_f64(dm.mla_prefill_sparse(q, kv, idx))
+    b = host_f64(dm.mla_prefill_sparse(q, kv, perm.contiguous()))
+    # a different key order changes only the fp32 summation order: at most one bf16 ulp of the output
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(a), np.abs(b)) + 1e-30)) - 7)
+    assert np.all(np.abs(a - b) <= ulp + 1e-6)
+    assert_close(b, oracle.mla_sparse_gather(qf, kvf, idxn, SCALE), TOL_BF16, "permuted rows vs oracle")
+
+
+def test_sparse_short_context_equals_dense():
+    """topk covers every visible key: sparse == dense absorbed attention."""
+    L, N = 16, 64
+    q, kv, _, qf, kvf, _ = _case(72, L, N, N)
+    idxn = gen_topk_indices(5, L, N, N)
+    out = dm.mla_prefill_sparse(q, kv, dev(idxn))
+    dense = dm.mla_prefill_dense(q[None], kv[None])[0]
+    torch.cuda.synchronize()
+    assert_close(host_f64(out), host_f64(dense), 1e-2, "sparse vs GPU dense")
+    assert_close(host_f64(out), oracle.mla_absorbed(qf, kvf, SCALE), TOL_BF16, "short context vs oracle")
+
+
+def test_sparse_invalid_entries_skipped_and_empty_rows_zero():
+    L, N, topk = 6, 50, 8
+    q, kv, _, qf, kvf, _ = _case(73, L, N, topk)
+    idxn = np.full((L, topk), -1, dtype=np.int32)
+    idxn[1, :3] = [0, 7, 49]
+    idxn[2, :4] = [5, 60, -9, 11]        # 60 and -9 are out of range: skipped
+    idxn[3] = np.arange(8) * 6
+    out = host_f64(dm.mla_prefill_sparse(q, kv, dev(idxn)))
+    ref = oracle.mla_sparse_gather(qf, kvf, idxn, SCALE)
+    assert np.all(out[0] == 0) and np.all(out[4] == 0) and np.all(out[5] == 0)
+    assert_close(out, ref, TOL_BF16, "invalid entries")
+
+
+def test_sparse_inputs_unchanged_outputs_overwritten_repeatable():
+    """Inputs are read-only (decode after prefill sees the same cache), every output element is
+    written, and repeated runs are bit-identical."""
+    q, kv, idx, *_ = _case(74, 64, 4000, 512, pad=0.1)
+    snap = [t.clone() for t in (q, kv, idx)]
+    out1 = torch.full((64, 64, 512), float("nan"), dtype=torch.bfloat16, device=q.device)
+    dm.mla_prefill_sparse(q, kv, idx, out=out1)
+    out2 = dm.mla_prefill_sparse(q, kv, idx)
+    torch.cuda.synchronize()
+    for a, b in zip(snap, (q, kv, idx)):
+        assert torch.equal(a, b)
+    assert not torch.isnan(out1).any()
+    assert torch.equal(out1, out2)
