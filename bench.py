@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark: DSA sparse MLA prefill at 128K context on one MI355X.
+
+One step = one pass of the sparse-prefill hot path over one chunk: the indexer
+(32 heads x 128, weighted ReLU head sum, exact top-2048 over N = 131072 keys)
+followed by absorbed attention for 64 heads over each query's 2048 gathered
+576-wide latent+rope rows, for a chunk of L = 1024 queries at the end of the
+context. Inputs are seeded synthetic data of those shapes, resident in HBM
+before timing starts. value = L / step time (prefill tokens per second).
+
+The line also carries:
+  roofline      the dominant kernel's achieved rate against the MI355X peak of
+                its bound, timed with HIP events on its launch stream;
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+                workload on this host;
+  kernels_ms    per-kernel average duration (HIP events);
+  other_configs the dense MLA prefill configurations (non-absorbed bf16 at
+                L = N = 4096, absorbed at L = 512 / N = 16384) with their MFMA
+                fractions.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+L, N, TOPK, BLOCK, H = 1024, 131072, 2048, 4096, 64
+SEED = 1004
+METRIC = "prefill tok/s at 128K ctx (sparse MLA); MFMA util %, HBM GB/s % of peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def indexer_flops(L, N):
+    """8192 FLOP (32 heads x 128-dim dot, multiply-add) per visible (query, key) pair."""
+    visible = sum(min(N, N - L + i + 1) for i in range(L))
+    return 2 * 32 * 128 * visible
+
+
+def sparse_attn_bytes(L, topk, H):
+    """Algorithmic HBM bytes of one sparse attention launch: gathered rows, q, out, idx."""
+    return L * topk * 576 * 2 + L * H * 576 * 2 + L * H * 512 * 2 + L * topk * 4
+
+
+def sparse_attn_flops(L, topk, H):
+    return L * topk * H * 2 * (576 + 512)
+
+
+def cpu_baseline(g, sample):
+    """The fp64 oracle on `sample` query rows of the same workload, on this host's cores."""
+    import numpy as np
+    import oracle
+    from synth import to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rows = np.linspace(0, L - 1, sample).astype(int)
+    qf, kf, wf = to_f64(g["q_idx"]), to_f64(g["k_idx"]), to_f64(g["w"])
+    q64 = to_f64(g["q"])
+    kv64 = to_f64(g["kv"])
+    t0 = time.perf_counter()
+    s = oracle.indexer_scores(qf, kf, wf, rows=rows)
+    sel = oracle.topk_full(s, TOPK)
+    idx = np.full((L, TOPK), -1, dtype=np.int64)
+    idx[rows] = sel
+    oracle.mla_sparse_gather(q64, kv64, idx, 1.0 / np.sqrt(576.0), rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{sample} of the {L} query rows (evenly spaced) of the same workload: canonical fp64 indexer "
+                      f"scores over all {N} keys, full stable-sort top-{TOPK}, fp64 gather attention over {H} heads; "
+                      f"{dt:.1f} s"}
+
+
+def dense_configs(dm, torch, reps=10):
+    """Time the dense MLA prefill configurations (not part of the step)."""
+    from synth import gen_absorbed, gen_nonabsorbed
+    sys.path.insert(0, os.path.join(HERE, "tests"))
+    from gpu_util import dev
+    res = {}
+    g = gen_nonabsorbed(1001, 4096, 4096, H=16, dtype="bf16", scale=0.5)
+    t = {k: dev(v)[None] for k, v in g.items()}
+    fn = lambda: dm.mla_prefill_dense(t["qn"], t["kn"], q_rope=t["qr"], k_rope=t["kr"], v=t["v"])  # noqa: E731
+    ms = _time(fn, torch, reps)
+    fl = 640 * 16 * 4096 * 4097 // 2
+    res["nonabsorbed_bf16_L4096_N4096_H16"] = {"ms": ms, "tflops": fl / ms / 1e9,
+                                               "mfma_frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+    g = gen_absorbed(1002, 512, 16384, H=64)
+    q, kv = dev(g["q"])[None], dev(g["kv"])[None]
+    ms = _time(lambda: dm.mla_prefill_dense(q, kv), torch, reps)
+    fl = 2176 * 64 * sum(16384 - 512 + i + 1 for i in range(512))
+    res["absorbed_bf16_L512_N16384_H64"] = {"ms": ms, "tflops": fl / ms / 1e9,
+                                            "mfma_frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+    return res
+
+
+def _time(fn, torch, reps):
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=96)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(query sharding needs no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dsa_sparse_attention_mla_amd as dm
+    from synth import gen_dsa_prefill
+    sys.path.insert(0, os.path.join(HERE, "tests"))
+    from gpu_util import dev
+
+    log("bench: generating inputs")
+    g = gen_dsa_prefill(SEED, L, N, H=H)
+    q_idx, k_idx, w, q, kv = (dev(g[k]) for k in ("q_idx", "k_idx", "w", "q", "kv"))
+    ws = torch.empty(dm.indexer_workspace_bytes(L, N, TOPK, BLOCK), dtype=torch.uint8, device="cuda:0")
+    idx = torch.empty((L, TOPK), dtype=torch.int32, device="cuda:0")
+    out = torch.empty((L, H, 512), dtype=torch.bfloat16, device="cuda:0")
+    assert dm.use_sparse(True, 1, L, N)
+
+    def step():
+        dm.dsa_indexer_topk(q_idx, k_idx, w, TOPK, block=BLOCK, out=idx, workspace=ws)
+        dm.mla_prefill_sparse(q, kv, idx, out=out, query_block=1024)
+
+    log("bench: warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("bench: timed steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt * 1e3 / args.steps
+
+    log("bench: per-kernel event timing")
+    with dm.kernel_trace() as tr:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+    kernels_ms = {k: tot / max(cnt, 1) for k, (cnt, tot) in tr.stats.items()}
+    t_idx = kernels_ms.get("indexer_score_filter", 0.0)
+    t_att = kernels_ms.get("sparse_attn", 0.0)
+    if t_idx >= t_att:
+        fl = indexer_flops(L, N)
+        ach = fl / (t_idx * 1e-3) / 1e12
+        roof = {"kernel": "indexer_score_filter", "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                "per_launch": f"{fl:.4e} FLOP (8192 per visible query-key pair)", "ms": t_idx}
+    else:
+        by = sparse_attn_bytes(L, TOPK, H)
+        ach = by / (t_att * 1e-3) / 1e9
+        roof = {"kernel": "sparse_attn", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                "per_launch": f"{by:.4e} B (gathered rows, q, out, idx)", "ms": t_att}
+
+    other = None
+    if not args.no_other_configs:
+        log("bench: dense configurations")
+        other = dense_configs(dm, torch)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        cpu = cpu_baseline(g, args.cpu_sample)
+
+    line = {
+        "metric": METRIC, "value": L / (ms_per_step * 1e-3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "DSA sparse MLA prefill, one 1024-query chunk at the end of a 131072-position "
+                               "context: indexer 32 heads x 128 (top-2048, blocks of 4096) + absorbed attention "
+                               "64 heads over gathered 576-wide latent+rope rows (value = first 512)",
+                   "L": L, "N": N, "topk": TOPK, "heads": H, "indexer_heads": 32, "block": BLOCK,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu, "kernels_ms": kernels_ms,
+        "phases_ms": {"indexer_total": sum(v for k, v in kernels_ms.items() if k.startswith(("indexer", "key_norm", "query_eps"))),
+                      "sparse_attn": t_att},
+        "sparse_attn_roofline": {"achieved_GBs": sparse_attn_bytes(L, TOPK, H) / (t_att * 1e-3) / 1e9 if t_att else None,
+                                 "frac_hbm": sparse_attn_bytes(L, TOPK, H) / (t_att * 1e-3) / 1e9 / PEAK_HBM_GBS if t_att else None,
+                                 "tflops": sparse_attn_flops(L, TOPK, H) / (t_att * 1e-3) / 1e12 if t_att else None},
+        "other_configs": other,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,6 +12,6 @@ a workspace buffer) -- all arithmetic runs in the library's HIP kernels.
 """
 from .api import (  # noqa: F401
     mla_prefill_dense, dsa_indexer_topk, mla_prefill_sparse, use_sparse, dsa_prefill,
-    SPARSE_PREFILL_DEFAULT, SPARSE_PREFILL_MIN_CONTEXT_DEFAULT,
+    SPARSE_PREFILL_DEFAULT, SPARSE_PREFILL_MIN_CONTEXT_DEFAULT, kernel_trace, indexer_workspace_bytes,
 )
 from ._lib import DsaMlaError, lib, LIB_PATH  # noqa: F401

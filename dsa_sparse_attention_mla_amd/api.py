@@ -89,11 +89,21 @@ def mla_prefill_dense(q, k, *, q_rope=None, k_rope=None, v=None, scale=None, cau
     return out
 
 
-def dsa_indexer_topk(q_idx, k_idx, w, topk, *, block=4096, return_scores=False, out=None):
+def indexer_workspace_bytes(L, N, topk, block=4096, Hi=32, Di=128):
+    """Workspace bytes dsa_indexer_topk needs for these sizes."""
+    size = ctypes.c_size_t(0)
+    p = ctypes.c_void_p(256)
+    check(lib().dsa_indexer_topk(1, L, N, Hi, Di, p, p, p, int(topk), int(block), p, None, None,
+                                 ctypes.byref(size), None), "dsa_indexer_topk (workspace query)")
+    return size.value
+
+
+def dsa_indexer_topk(q_idx, k_idx, w, topk, *, block=4096, return_scores=False, out=None, workspace=None):
     """Exact indexer top-k. q_idx [L,32,128] bf16, k_idx [N,128] bf16, w [L,32] fp32.
 
     Returns idx [L,topk] int32 (ascending key order, -1 padded), and the fp32
-    scores of the returned keys when return_scores is set.
+    scores of the returned keys when return_scores is set. `workspace` (a uint8
+    device tensor of at least indexer_workspace_bytes) avoids a per-call allocation.
     """
     _need(q_idx, "q_idx", torch.bfloat16, 3)
     _need(k_idx, "k_idx", torch.bfloat16, 2)
@@ -110,7 +120,11 @@ def dsa_indexer_topk(q_idx, k_idx, w, topk, *, block=4096, return_scores=False, 
         return lib().dsa_indexer_topk(1, L, N, Hi, Di, _ptr(q_idx), _ptr(k_idx), _ptr(w), int(topk), int(block),
                                       _ptr(idx), _ptr(scores), ws, ws_bytes, _stream(dev))
 
-    ws, size = _workspace(call, dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        ws, size = workspace, ctypes.c_size_t(workspace.numel())
+    else:
+        ws, size = _workspace(call, dev)
     check(call(_ptr(ws), None if size is None else ctypes.byref(size)), "dsa_indexer_topk")
     return (idx, scores) if return_scores else idx
 
@@ -157,3 +171,30 @@ def dsa_prefill(q, kv, q_idx, k_idx, w, topk, *, scale=None, block=4096, query_b
     # below the gate: the dense path over all visible keys under the top-k selection,
     # which equals gathering exactly the selected rows
     return mla_prefill_sparse(q, kv, idx, scale=scale, query_block=query_block), idx
+
+
+class kernel_trace:
+    """Context manager: per-kernel HIP-event timing of every library launch inside the block.
+
+        with kernel_trace() as tr:
+            ...
+        tr.stats -> {kernel name: (launches, total ms)}
+    """
+
+    def __enter__(self):
+        lib().dsa_mla_trace_collect(0, None, None, None)   # drop stale records
+        self._prev = lib().dsa_mla_trace_enable(1)
+        self.stats = {}
+        return self
+
+    def __exit__(self, *exc):
+        lib().dsa_mla_trace_enable(self._prev)
+        n_max = 64
+        names = ctypes.create_string_buffer(32 * n_max)
+        counts = (ctypes.c_int * n_max)()
+        tot = (ctypes.c_double * n_max)()
+        n = lib().dsa_mla_trace_collect(n_max, names, counts, tot)
+        for j in range(min(n, n_max)):
+            nm = names.raw[32 * j:32 * j + 32].split(b"\0", 1)[0].decode()
+            self.stats[nm] = (counts[j], tot[j])
+        return False

@@ -184,6 +184,7 @@ hipError_t launch_absorbed_attn(bool sparse, const uint16_t* q, const uint16_t* 
                                 hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   dim3 grid(nq, B, (H + 63) / 64), block(256);
+  KernelTrace kt(sparse ? "sparse_attn" : "absorbed_dense_attn", stream);
   if (sparse)
     hipLaunchKernelGGL((absorbed_attn_kernel<true, 4>), grid, block, 0, stream, q, kv, idx, out, L, N, H, topk, q0, causal, scale_log2);
   else

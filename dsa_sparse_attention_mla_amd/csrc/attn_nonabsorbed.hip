@@ -230,6 +230,7 @@ hipError_t launch_nonabsorbed_attn(bool bf16, const void* qn, const void* qr, co
                                    hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   dim3 grid((L + 63) / 64, H, B), block(256);
+  KernelTrace kt(bf16 ? "nonabsorbed_attn_bf16" : "nonabsorbed_attn_f32", stream);
   if (bf16)
     hipLaunchKernelGGL((nonabsorbed_attn_kernel<true>), grid, block, 0, stream, qn, qr, kn, kr, v, out, L, N, H, causal, scale_log2);
   else

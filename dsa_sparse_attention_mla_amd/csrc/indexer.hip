@@ -646,14 +646,29 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(key_norm_partial_kernel, dim3(NORM_BLOCKS), dim3(256), 0, stream, k, N, partial);
-  hipLaunchKernelGGL(query_eps_kernel, dim3(L), dim3(64), 0, stream, q, w, partial, NORM_BLOCKS, L, eps);
-  hipLaunchKernelGGL(score_filter_kernel, dim3((L + QPB - 1) / QPB, pl.nsplit), dim3(256), pl.filter_lds, stream, q, k,
-                     w, eps, L, N, topk, pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n);
-  hipLaunchKernelGGL(select_refine_kernel, dim3(L), dim3(256), pl.select_lds, stream, q, k, w, eps, L, N, topk,
-                     pl.nsplit, pl.cap, cand_s, cand_i, cand_n, fb, idx_out, score_out);
-  hipLaunchKernelGGL(exact_fallback_kernel, dim3(pl.fb_blocks), dim3(FB_ROWS), 0, stream, q, k, w, L, N, topk, fb,
-                     scratch, idx_out, score_out);
+  {
+    KernelTrace kt("key_norm_partial", stream);
+    hipLaunchKernelGGL(key_norm_partial_kernel, dim3(NORM_BLOCKS), dim3(256), 0, stream, k, N, partial);
+  }
+  {
+    KernelTrace kt("query_eps", stream);
+    hipLaunchKernelGGL(query_eps_kernel, dim3(L), dim3(64), 0, stream, q, w, partial, NORM_BLOCKS, L, eps);
+  }
+  {
+    KernelTrace kt("indexer_score_filter", stream);
+    hipLaunchKernelGGL(score_filter_kernel, dim3((L + QPB - 1) / QPB, pl.nsplit), dim3(256), pl.filter_lds, stream, q,
+                       k, w, eps, L, N, topk, pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n);
+  }
+  {
+    KernelTrace kt("indexer_select_refine", stream);
+    hipLaunchKernelGGL(select_refine_kernel, dim3(L), dim3(256), pl.select_lds, stream, q, k, w, eps, L, N, topk,
+                       pl.nsplit, pl.cap, cand_s, cand_i, cand_n, fb, idx_out, score_out);
+  }
+  {
+    KernelTrace kt("indexer_exact_fallback", stream);
+    hipLaunchKernelGGL(exact_fallback_kernel, dim3(pl.fb_blocks), dim3(FB_ROWS), 0, stream, q, k, w, L, N, topk, fb,
+                       scratch, idx_out, score_out);
+  }
   return hipGetLastError();
 }
 

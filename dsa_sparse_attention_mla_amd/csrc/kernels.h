@@ -6,6 +6,21 @@
 
 namespace dsa {
 
+// RAII scope that brackets one kernel launch with HIP events when tracing is on
+// (see dsa_mla_trace_enable); a no-op otherwise.
+class KernelTrace {
+ public:
+  KernelTrace(const char* name, hipStream_t s);
+  ~KernelTrace();
+  KernelTrace(const KernelTrace&) = delete;
+  KernelTrace& operator=(const KernelTrace&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  void* a_;
+};
+
 hipError_t launch_absorbed_attn(bool sparse, const uint16_t* q, const uint16_t* kv, const int32_t* idx, uint16_t* out,
                                 int B, int L, int N, int H, int topk, int q0, int nq, int causal, float scale,
                                 hipStream_t stream);

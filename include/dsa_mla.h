@@ -128,6 +128,19 @@ int dsa_indexer_topk(int B, int L, int N, int Hi, int Di, const void* q_idx, con
 int mla_prefill_sparse(int B, int L, int N, int H, const void* q, const void* kv, const int32_t* idx, int topk,
                        float scale, int query_block, void* out, void* ws, size_t* ws_bytes, void* stream);
 
+/*
+ * Per-kernel timing (diagnostics). dsa_mla_trace_enable(1) makes every later
+ * kernel launch of the library record a HIP event pair on its launch stream;
+ * it returns the previous setting. dsa_mla_trace_collect waits for the
+ * recorded events, and for each distinct kernel name (at most max_kernels)
+ * writes the name (NUL-terminated, 32 bytes per entry) into `names`, the
+ * launch count into `counts` and the summed event time in milliseconds into
+ * `total_ms`; any of the three may be NULL. It clears the record and returns
+ * the number of distinct kernels seen.
+ */
+int dsa_mla_trace_enable(int on);
+int dsa_mla_trace_collect(int max_kernels, char* names, int* counts, double* total_ms);
+
 /* Short English name of a status code (static storage). */
 const char* dsa_mla_status_string(int status);
 

@@ -14,7 +14,7 @@ import numpy as np
 __all__ = [
     "bf16_bits", "bf16_to_f32", "to_f64", "Tensor",
     "gen_nonabsorbed", "gen_absorbed", "gen_indexer", "gen_indexer_exact",
-    "gen_topk_indices", "CONFIG_SEED",
+    "gen_topk_indices", "gen_dsa_prefill", "CONFIG_SEED",
 ]
 
 # seed used for the workload shapes listed in the design doc (seed = 1000 + config number)
@@ -116,6 +116,20 @@ def gen_indexer_exact(seed, L, N, Hi=32, Di=128, p_zero=0.5):
     k = Tensor(bf16_bits(tern((N, Di))), "bf16")
     w = Tensor((rng.integers(0, 64, size=(L, Hi)) / 64.0).astype(np.float32), "f32")
     return dict(q_idx=q, k_idx=k, w=w)
+
+
+def gen_dsa_prefill(seed, L, N, H=64, Hi=32, Di=128, d=576):
+    """End-to-end DSA prefill inputs from one generator, drawn in the order
+    q_idx [L,Hi,Di] (bf16), k_idx [N,Di] (bf16), w [L,Hi] (fp32 U[0,1)),
+    q [L,H,d] (bf16), kv [N,d] (bf16). N counts every cached position,
+    this chunk's L positions (the last ones) included."""
+    rng = np.random.default_rng(seed)
+    q_idx = _normal(rng, (L, Hi, Di), 1.0, "bf16")
+    k_idx = _normal(rng, (N, Di), 1.0, "bf16")
+    w = Tensor(rng.random((L, Hi), dtype=np.float32), "f32")
+    q = _normal(rng, (L, H, d), 1.0, "bf16")
+    kv = _normal(rng, (N, d), 1.0, "bf16")
+    return dict(q_idx=q_idx, k_idx=k_idx, w=w, q=q, kv=kv)
 
 
 def gen_topk_indices(seed, L, N, topk, causal=True, pad_frac=0.0):

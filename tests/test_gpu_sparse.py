@@ -62,9 +62,10 @@ def test_sparse_permutation_invariance():
                         for r in idx])
     a = host_f64(dm.mla_prefill_sparse(q, kv, idx))
     b = host_f64(dm.mla_prefill_sparse(q, kv, perm.contiguous()))
-    # a different key order changes only the fp32 summation order: at most one bf16 ulp of the output
-    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(a), np.abs(b)) + 1e-30)) - 7)
-    assert np.all(np.abs(a - b) <= ulp + 1e-6)
+    # a different key order changes the fp32 summation order and the running max that the bf16
+    # rounding of the softmax weights is taken against: differences are rounding-sized, absolute
+    d = np.abs(a - b)
+    assert d.max() <= 8e-3 and d.mean() <= 5e-4
     assert_close(b, oracle.mla_sparse_gather(qf, kvf, idxn, SCALE), TOL_BF16, "permuted rows vs oracle")
 
 
