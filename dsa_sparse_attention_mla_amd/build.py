@@ -18,9 +18,12 @@ LIB = os.path.join(HERE, "libdsa_mla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-# packed fp32 ops are disabled: the compiler would otherwise form v_pk_*_f32 from scalar code
+# packed fp32 ops are disabled: the compiler would otherwise form v_pk_*_f32 from scalar code.
+# MFMA accumulators are kept in ordinary VGPRs (not AGPRs): the online-softmax rescale of the
+# output accumulators then needs no AGPR<->VGPR copies.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wno-unused-command-line-argument"]
 
 

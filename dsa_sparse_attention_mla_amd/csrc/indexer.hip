@@ -34,7 +34,9 @@ namespace {
 constexpr int ID = 128;                 // indexer head dim
 constexpr int IH = 32;                  // indexer heads
 constexpr int TK = 64;                  // keys per tile
-constexpr int KROW = ID * 2 + 16;       // padded LDS key row (272 B)
+constexpr int IDX_STAGE = TK * ID * 2;  // one ring stage: 64 keys x 256 B (swizzled, unpadded)
+constexpr int IDX_NSTAGE = 3;           // ring stages
+constexpr int IDX_AHEAD = IDX_NSTAGE - 1;
 constexpr int QPB = 4;                  // queries per workgroup, one per wave
 constexpr int RANK_CAP = 1024;          // band entries ranked in select_refine
 constexpr int NORM_BLOCKS = 256;
@@ -153,15 +155,25 @@ __device__ float wave_kth_largest(const float* vals, int n, int k, int* hist, in
   return __uint_as_float(prefix);
 }
 
+// Wait until at most n of this wave's vector-memory operations are outstanding.
+__device__ __forceinline__ void idx_wait_vm(int n) {
+  if (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
+
+// Keys stream through a ring of LDS stages filled by direct global->LDS loads,
+// AHEAD tiles ahead of use. Within a stage, key r's 16-byte chunk c sits at chunk
+// slot r*16 + (c ^ (r & 15)), so the 32 keys one MFMA operand read touches fall
+// in distinct banks.
 __global__ __launch_bounds__(256) void score_filter_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int span, int nsplit, int cap,
     float* __restrict__ cand_s, int* __restrict__ cand_i, int* __restrict__ cand_n) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-  unsigned char* ktile = dyn;                                   // [2][TK*KROW]
-  float* cs_all = (float*)(dyn + 2 * TK * KROW);                // [QPB][cap]
-  int* ci_all = (int*)(cs_all + QPB * cap);                     // [QPB][cap]
-  int* hist_all = ci_all + QPB * cap;                           // [QPB][256]
+  unsigned char* ring = dyn;                                          // [NSTAGE][TK*256]
+  float* cs_all = (float*)(dyn + IDX_NSTAGE * IDX_STAGE);             // [QPB][cap]
+  int* ci_all = (int*)(cs_all + QPB * cap);                           // [QPB][cap]
+  int* hist_all = ci_all + QPB * cap;                                 // [QPB][256]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.y;
@@ -190,42 +202,40 @@ __global__ __launch_bounds__(256) void score_filter_kernel(
   int cnt = 0;
   bool ovf = false;
 
-  u32x4 stg[4];
-  auto load_tile = [&](int n0) {
+  // 16 wave instructions of 64 x 16 B fill one stage; wave w issues blocks w, w+4, w+8, w+12
+  auto issue_tile = [&](int n0, int s) {
+    unsigned char* st = ring + s * IDX_STAGE;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c >> 4, col = c & 15;
-      const int n = n0 + r;
-      stg[u] = n < n_hi ? *(const u32x4*)(k + (size_t)n * ID + col * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int s) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = tid + 256 * u;
-      const int r = c >> 4, col = c & 15;
-      *(u32x4*)(ktile + s * TK * KROW + r * KROW + col * 16) = stg[u];
+      const int blk = wave + 4 * u;
+      const int slot = blk * 64 + lane;
+      const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
+      const int n = min(n0 + r, n_hi - 1);          // keys past the range fetch a harmless row
+      __builtin_amdgcn_global_load_lds((const void*)(k + (size_t)n * ID + c * 8),
+                                       (DSA_LDS void*)(st + blk * 1024), 16, 0, 0);
     }
   };
 
   const int ntiles = n_hi > n_lo ? (n_hi - n_lo + TK - 1) / TK : 0;
-  if (ntiles > 0) {
-    load_tile(n_lo);
-    store_tile(0);
-  }
-  __syncthreads();
+  for (int t = 0; t < IDX_AHEAD && t < ntiles; ++t) issue_tile(n_lo + t * TK, t % IDX_NSTAGE);
   for (int t = 0; t < ntiles; ++t) {
-    const int s = t & 1;
+    const int s = t % IDX_NSTAGE;
     const int n0 = n_lo + t * TK;
-    if (t + 1 < ntiles) load_tile(n0 + TK);
+    idx_wait_vm(min(t + IDX_AHEAD - 1, ntiles - 1) - t);
+    __syncthreads();
+    if (t + IDX_AHEAD < ntiles) issue_tile(n0 + IDX_AHEAD * TK, (t + IDX_AHEAD) % IDX_NSTAGE);
+    const unsigned char* st = ring + s * IDX_STAGE;
     float tot[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       f32x16 acc = {};
-      const unsigned char* kp = ktile + s * TK * KROW + (32 * sub + (lane & 31)) * KROW + 16 * (lane >> 5);
+      const int r = 32 * sub + (lane & 31);
+      const unsigned char* kp = st + r * 256;
 #pragma unroll
-      for (int kc = 0; kc < ID / 16; ++kc) acc = mfma32x32x16(qa[kc], *(const bf16x8*)(kp + 32 * kc), acc);
+      for (int kc = 0; kc < ID / 16; ++kc) {
+        const int c = (2 * kc + (lane >> 5)) ^ (r & 15);
+        acc = mfma32x32x16(qa[kc], *(const bf16x8*)(kp + c * 16), acc);
+      }
       float part = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) part = fmaf(wr[j], fmaxf(acc[j], 0.f), part);
@@ -267,8 +277,6 @@ __global__ __launch_bounds__(256) void score_filter_kernel(
         if (cnt > cap - 64) ovf = true;
       }
     }
-    if (t + 1 < ntiles) store_tile(s ^ 1);
-    __syncthreads();
   }
   if (active) {
     const size_t slot = (size_t)i * nsplit + split;
@@ -607,7 +615,7 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   span = (span + TK - 1) / TK * TK;
   pl.nsplit = ns;
   pl.span = span;
-  pl.cap = 3712;
+  pl.cap = 3456;                        // (160 KiB - ring - histograms) / (4 queries x 8 B)
   pl.fb_blocks = L < 32 ? L : 32;
   if (pl.fb_blocks < 1) pl.fb_blocks = 1;
   size_t off = 0;
@@ -620,7 +628,7 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   pl.off_cand_i = take(sizeof(int) * (size_t)L * ns * pl.cap);
   pl.off_scratch = take(sizeof(double) * (size_t)pl.fb_blocks * N);
   pl.ws_bytes = off;
-  pl.filter_lds = 2 * TK * KROW + QPB * pl.cap * 8 + QPB * 256 * 4;
+  pl.filter_lds = IDX_NSTAGE * IDX_STAGE + QPB * pl.cap * 8 + QPB * 256 * 4;
   const size_t M = (size_t)ns * pl.cap;
   pl.select_lds = M * 4 + M * 4 + ((M + 15) & ~(size_t)15) + ((M + 7) & ~(size_t)7) * 2 + RANK_CAP * 8 + RANK_CAP * 4 +
                   RANK_CAP + IH * ID * 2 + 256 * 4 + 8 * 4 + 4 * 4;
