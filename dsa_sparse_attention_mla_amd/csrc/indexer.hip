@@ -35,12 +35,16 @@ constexpr int ID = 128;                 // indexer head dim
 constexpr int IH = 32;                  // indexer heads
 constexpr int TK = 64;                  // keys per tile
 constexpr int IDX_STAGE = TK * ID * 2;  // one ring stage: 64 keys x 256 B (swizzled, unpadded)
-constexpr int IDX_NSTAGE = 3;           // ring stages
-constexpr int IDX_AHEAD = IDX_NSTAGE - 1;
-constexpr int QPB = 4;                  // queries per workgroup, one per wave
+constexpr int QPB = 4;                  // queries per workgroup
+constexpr int IDX_NW = 8;               // waves per score workgroup: 2 per query
+constexpr int RANK_WORDS = 4096;        // bitmap words for ordering the output (131072 keys per window)
 constexpr int RANK_CAP = 1024;          // band entries ranked in select_refine
 constexpr int NORM_BLOCKS = 256;
 constexpr int FB_ROWS = 256;            // block size of the fallback kernel
+// LDS of the refine kernel besides the candidate arrays: band scores/keys/bin values/flags,
+// the staged query, the rank bitmap, rank bases, histogram, scratch
+constexpr size_t SELECT_FIXED = RANK_CAP * 8 + RANK_CAP * 4 + RANK_CAP * 4 + RANK_CAP + IH * ID * 2 + RANK_WORDS * 4 +
+                                256 * 4 + 256 * 4 + 8 * 4 + 8 * 4;
 }  // namespace
 
 __device__ __forceinline__ void wave_sync() {
@@ -111,82 +115,178 @@ __global__ __launch_bounds__(64) void query_eps_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------- 3. score + running candidates
-// Wave-level radix select of the k-th largest non-negative float among n entries.
-__device__ float wave_kth_largest(const float* vals, int n, int k, int* hist, int lane) {
-  uint32_t prefix = 0, pmask = 0;
-  int need = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = lane; b < 256; b += 64) hist[b] = 0;
-    wave_sync();
-    for (int e = lane; e < n; e += 64) {
-      const uint32_t u = __float_as_uint(vals[e]);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
-    }
-    wave_sync();
-    const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-    const int own = h0 + h1 + h2 + h3;
-    int suf = own;  // inclusive suffix sum over lanes (higher lanes hold higher digits)
+__device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_down(suf, off);
-      if (lane + off < 64) suf += v;
-    }
-    const int above = suf - own;
-    const bool here = above < need && suf >= need;
-    int digit = 0, above_d = 0;
-    if (here) {
-      int acc = above;
-      if (acc + h3 >= need) { digit = 4 * lane + 3; above_d = acc; }
-      else { acc += h3;
-        if (acc + h2 >= need) { digit = 4 * lane + 2; above_d = acc; }
-        else { acc += h2;
-          if (acc + h1 >= need) { digit = 4 * lane + 1; above_d = acc; }
-          else { acc += h1; digit = 4 * lane; above_d = acc; } } }
-    }
-    const unsigned long long bm = __ballot(here);
-    const int src = __ffsll((long long)bm) - 1;
-    digit = __shfl(digit, src);
-    above_d = __shfl(above_d, src);
-    prefix |= (uint32_t)digit << shift;
-    pmask |= 255u << shift;
-    need -= above_d;
-    wave_sync();
-  }
-  return __uint_as_float(prefix);
+  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_min(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x = fminf(x, __shfl_xor(x, off));
+  return x;
 }
 
-// Wait until at most n of this wave's vector-memory operations are outstanding.
-__device__ __forceinline__ void idx_wait_vm(int n) {
-  if (n == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+// Bucket of x in a 256-bin linear histogram over [mn, mx]; non-decreasing in x.
+__device__ __forceinline__ int lin_bucket(float x, float mn, float inv_w) {
+  const float f = fminf(fmaxf((x - mn) * inv_w, 0.f), 255.f);   // fmaxf also maps NaN to 0
+  return (int)f;
+}
+
+// Given a 256-bin histogram (higher bin = larger values), find the bin B holding
+// the need-th largest entry: returns B and the number of entries in bins above B.
+// Executed by one wave (lane = 0..63, 4 bins per lane).
+__device__ __forceinline__ void wave_find_bin(const int* hist, int need, int lane, int& bin, int& above_bin) {
+  const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+  const int own = h0 + h1 + h2 + h3;
+  int suf = own;  // inclusive suffix sum over lanes (higher lanes hold higher bins)
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_down(suf, off);
+    if (lane + off < 64) suf += v;
+  }
+  const int above = suf - own;
+  const bool here = above < need && suf >= need;
+  int digit = 0, above_d = 0;
+  if (here) {
+    int acc = above;
+    if (acc + h3 >= need) { digit = 4 * lane + 3; above_d = acc; }
+    else { acc += h3;
+      if (acc + h2 >= need) { digit = 4 * lane + 2; above_d = acc; }
+      else { acc += h2;
+        if (acc + h1 >= need) { digit = 4 * lane + 1; above_d = acc; }
+        else { acc += h1; digit = 4 * lane; above_d = acc; } } }
+  }
+  const unsigned long long bm = __ballot(here);
+  const int src = __ffsll((long long)bm) - 1;
+  bin = __shfl(digit, src);
+  above_bin = __shfl(above_d, src);
+}
+
+// Block-wide helpers for the 512-thread score workgroup.
+__device__ __forceinline__ float block512_max(float x, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_max(x);
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int v = 1; v < IDX_NW; ++v) r = fmaxf(r, red[v]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float block512_min(float x, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_min(x);
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int v = 1; v < IDX_NW; ++v) r = fminf(r, red[v]);
+  __syncthreads();
+  return r;
+}
+
+// Cooperative (all 512 threads) threshold update and in-place compaction of one
+// query's candidate list: tau = a lower bound of the list's k-th largest score
+// (smallest value of the linear-histogram bin holding it), then keep the entries
+// with score >= max(old threshold, tau - band(tau)). Returns the new count.
+template <typename Off>
+__device__ int block_compact(float* cs, Off* co, int cnt, int k, float eps, float& thr, int* hist, int* misc,
+                             float* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float mx = -INFINITY, mn = INFINITY;
+  for (int e = tid; e < cnt; e += 64 * IDX_NW) {
+    const float v = cs[e];
+    mx = fmaxf(mx, v);
+    mn = fminf(mn, v);
+  }
+  mx = block512_max(mx, red);
+  mn = block512_min(mn, red);
+  float tau = mn;
+  if (mx > mn) {
+    const float inv_w = 256.0f / (mx - mn);
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int e = tid; e < cnt; e += 64 * IDX_NW) atomicAdd(&hist[lin_bucket(cs[e], mn, inv_w)], 1);
+    __syncthreads();
+    if (wave == 0) {
+      int bin, above;
+      wave_find_bin(hist, k, lane, bin, above);
+      if (lane == 0) misc[0] = bin;
+    }
+    __syncthreads();
+    const int bin = misc[0];
+    float tb = INFINITY;
+    for (int e = tid; e < cnt; e += 64 * IDX_NW) {
+      const float v = cs[e];
+      if (lin_bucket(v, mn, inv_w) == bin) tb = fminf(tb, v);
+    }
+    tau = block512_min(tb, red);
+  }
+  thr = fmaxf(thr, tau - band_halfwidth(eps, tau));
+  int newc = 0;
+  for (int c0 = 0; c0 < cnt; c0 += 64 * IDX_NW) {
+    const int e = c0 + tid;
+    const bool in = e < cnt;
+    const float v = in ? cs[e] : 0.f;
+    const Off id = in ? co[e] : (Off)0;
+    const bool keep = in && v >= thr;
+    const unsigned long long bm = __ballot(keep);
+    if (lane == 0) misc[8 + wave] = __popcll(bm);
+    __syncthreads();                      // every entry of this chunk has been read
+    int off = newc;
+    for (int x = 0; x < wave; ++x) off += misc[8 + x];
+    if (keep) {
+      const int pos = off + __popcll(bm & ((1ull << lane) - 1ull));
+      cs[pos] = v;
+      co[pos] = id;
+    }
+#pragma unroll
+    for (int x = 0; x < IDX_NW; ++x) newc += misc[8 + x];
+    __syncthreads();
+  }
+  return newc;
 }
 
 // Keys stream through a ring of LDS stages filled by direct global->LDS loads,
-// AHEAD tiles ahead of use. Within a stage, key r's 16-byte chunk c sits at chunk
-// slot r*16 + (c ^ (r & 15)), so the 32 keys one MFMA operand read touches fall
-// in distinct banks.
-__global__ __launch_bounds__(256) void score_filter_kernel(
+// NSTAGE-1 tiles ahead of use. Within a stage, key r's 16-byte chunk c sits at
+// chunk slot r*16 + (c ^ (r & 15)), so the 32 keys one MFMA operand read touches
+// fall in distinct banks. Eight waves: wave w scores query w%4 against key half
+// w/4 (32 keys) of every 64-key tile, so two waves share each SIMD. A query's
+// two waves append survivors (score, key offset within the split) to one LDS
+// list through wave-aggregated atomic slots. When a list nears capacity at a
+// tile boundary, the whole workgroup recomputes that query's threshold from the
+// list and compacts it.
+template <typename Off, int NSTAGE>
+__global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int span, int nsplit, int cap,
     float* __restrict__ cand_s, int* __restrict__ cand_i, int* __restrict__ cand_n) {
+  constexpr int AHEAD = NSTAGE - 1;
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   unsigned char* ring = dyn;                                          // [NSTAGE][TK*256]
-  float* cs_all = (float*)(dyn + IDX_NSTAGE * IDX_STAGE);             // [QPB][cap]
-  int* ci_all = (int*)(cs_all + QPB * cap);                           // [QPB][cap]
-  int* hist_all = ci_all + QPB * cap;                                 // [QPB][256]
+  float* cs_all = (float*)(dyn + NSTAGE * IDX_STAGE);                 // [QPB][cap]
+  Off* co_all = (Off*)(cs_all + QPB * cap);                           // [QPB][cap]
+  int* hist = (int*)(co_all + QPB * cap);                             // [256]
+  int* qcnt = hist + 256;                                             // [QPB]
+  float* qthr = (float*)(qcnt + QPB);                                 // [QPB]
+  int* qovf = (int*)(qthr + QPB);                                     // [QPB]
+  float* qeps = (float*)(qovf + QPB);                                 // [QPB]
+  int* misc = (int*)(qeps + QPB);                                     // [16]
+  float* red = (float*)(misc + 16);                                   // [IDX_NW]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qi = wave & (QPB - 1), kh = wave / QPB;
   const int split = blockIdx.y;
   const int n_lo = split * span;
-  const int i = blockIdx.x * QPB + wave;
+  const int i = blockIdx.x * QPB + qi;
   const bool active = i < L;
   const int ii = active ? i : L - 1;
   const int p = N - L + ii;
   const int ilast = min(L - 1, (int)blockIdx.x * QPB + QPB - 1);
   const int n_hi = min(min(N, n_lo + span), N - L + ilast + 1);
-  float* cs = cs_all + wave * cap;
-  int* ci = ci_all + wave * cap;
-  int* hist = hist_all + wave * 256;
+  float* cs = cs_all + qi * cap;
+  Off* co = co_all + qi * cap;
 
   bf16x8 qa[ID / 16];
   {
@@ -197,17 +297,19 @@ __global__ __launch_bounds__(256) void score_filter_kernel(
   float wr[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) wr[j] = w[(size_t)ii * IH + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)];
-  const float eps = eps_in[ii];
-  float thr = -INFINITY;
-  int cnt = 0;
-  bool ovf = false;
+  if (tid < QPB) {
+    qcnt[tid] = 0;
+    qthr[tid] = -INFINITY;
+    qovf[tid] = 0;
+    qeps[tid] = eps_in[min((int)blockIdx.x * QPB + tid, L - 1)];
+  }
 
-  // 16 wave instructions of 64 x 16 B fill one stage; wave w issues blocks w, w+4, w+8, w+12
+  // 16 wave instructions of 64 x 16 B fill one stage; wave w issues blocks w and w+8
   auto issue_tile = [&](int n0, int s) {
     unsigned char* st = ring + s * IDX_STAGE;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int blk = wave + 4 * u;
+    for (int u = 0; u < 16 / IDX_NW; ++u) {
+      const int blk = wave + IDX_NW * u;
       const int slot = blk * 64 + lane;
       const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
       const int n = min(n0 + r, n_hi - 1);          // keys past the range fetch a harmless row
@@ -217,122 +319,157 @@ __global__ __launch_bounds__(256) void score_filter_kernel(
   };
 
   const int ntiles = n_hi > n_lo ? (n_hi - n_lo + TK - 1) / TK : 0;
-  for (int t = 0; t < IDX_AHEAD && t < ntiles; ++t) issue_tile(n_lo + t * TK, t % IDX_NSTAGE);
+  for (int t = 0; t < AHEAD && t < ntiles; ++t) issue_tile(n_lo + t * TK, t % NSTAGE);
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    const int s = t % IDX_NSTAGE;
+    const int s = t % NSTAGE;
     const int n0 = n_lo + t * TK;
-    idx_wait_vm(min(t + IDX_AHEAD - 1, ntiles - 1) - t);
+    // tiles issued after tile t: min(AHEAD-1, ntiles-1-t), two instructions each per wave
+    const int after = min(t + AHEAD - 1, ntiles - 1) - t;
+    if (after >= 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if (after == 1) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + IDX_AHEAD < ntiles) issue_tile(n0 + IDX_AHEAD * TK, (t + IDX_AHEAD) % IDX_NSTAGE);
-    const unsigned char* st = ring + s * IDX_STAGE;
-    float tot[2];
+    if (t + AHEAD < ntiles) issue_tile(n0 + AHEAD * TK, (t + AHEAD) % NSTAGE);
+    // Compaction at the tile boundary. The shared counts are stable from the barrier
+    // above until the barrier before this tile's appends, so every wave takes the same
+    // decisions, and the cooperative compaction below only writes them after barriers
+    // that every wave has reached.
+    int need = 0;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      f32x16 acc = {};
-      const int r = 32 * sub + (lane & 31);
-      const unsigned char* kp = st + r * 256;
-#pragma unroll
-      for (int kc = 0; kc < ID / 16; ++kc) {
-        const int c = (2 * kc + (lane >> 5)) ^ (r & 15);
-        acc = mfma32x32x16(qa[kc], *(const bf16x8*)(kp + c * 16), acc);
-      }
-      float part = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) part = fmaf(wr[j], fmaxf(acc[j], 0.f), part);
-      tot[sub] = part + __shfl_xor(part, 32);
-    }
-    if (active && !ovf) {
-      const float sv = lane < 32 ? tot[0] : tot[1];
-      const int key = n0 + lane;
-      const bool keep = key < n_hi && key <= p && sv >= thr;
-      const unsigned long long bm = __ballot(keep);
-      if (keep) {
-        const int pos = cnt + __popcll(bm & ((1ull << lane) - 1ull));
-        cs[pos] = sv;
-        ci[pos] = key;
-      }
-      cnt += __popcll(bm);
-      if (cnt > cap - 64) {
-        wave_sync();
-        const float tau = wave_kth_largest(cs, cnt, topk, hist, lane);
-        thr = fmaxf(thr, tau - band_halfwidth(eps, tau));
-        int newc = 0;
-        for (int base = 0; base < cnt; base += 64) {
-          const int e = base + lane;
-          const bool in = e < cnt;
-          const float v = in ? cs[e] : 0.f;
-          const int id = in ? ci[e] : 0;
-          const bool kp2 = in && v >= thr;
-          const unsigned long long m2 = __ballot(kp2);
-          wave_sync();
-          if (kp2) {
-            const int pos = newc + __popcll(m2 & ((1ull << lane) - 1ull));
-            cs[pos] = v;
-            ci[pos] = id;
-          }
-          newc += __popcll(m2);
-          wave_sync();
+    for (int x = 0; x < QPB; ++x) need |= ((qcnt[x] > cap - 2 * 64) && !qovf[x]) << x;
+    if (need) {
+      __syncthreads();
+#pragma unroll 1
+      for (int x = 0; x < QPB; ++x) {
+        if (!((need >> x) & 1)) continue;
+        float thr = qthr[x];
+        const int newc = block_compact<Off>(cs_all + x * cap, co_all + x * cap, qcnt[x], topk, qeps[x], thr,
+                                            hist, misc, red);
+        if (tid == 0) {
+          qcnt[x] = newc;
+          qthr[x] = thr;
+          qovf[x] = newc > cap - 2 * 64;
         }
-        cnt = newc;
-        if (cnt > cap - 64) ovf = true;
+        __syncthreads();
+      }
+    }
+    const float thr = qthr[qi];
+    const bool ovf = qovf[qi] != 0;
+
+    const unsigned char* st = ring + s * IDX_STAGE;
+    const int r = 32 * kh + (lane & 31);
+    const unsigned char* kp = st + r * 256;
+    bf16x8 kf[ID / 16];                  // all operand reads in flight before the MFMA chain
+#pragma unroll
+    for (int kc = 0; kc < ID / 16; ++kc) kf[kc] = *(const bf16x8*)(kp + (((2 * kc + (lane >> 5)) ^ (r & 15)) * 16));
+    f32x16 acc = {};
+#pragma unroll
+    for (int kc = 0; kc < ID / 16; ++kc) acc = mfma32x32x16(qa[kc], kf[kc], acc);
+    // ReLU as an integer max on the bit pattern (exact for every non-NaN float, -0 -> +0),
+    // then the weighted head sum in two interleaved chains
+    float pa = 0.f, pb = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      pa = fmaf(wr[j], __int_as_float(max(__float_as_int(acc[j]), 0)), pa);
+      pb = fmaf(wr[j + 1], __int_as_float(max(__float_as_int(acc[j + 1]), 0)), pb);
+    }
+    const float part = pa + pb;
+    // lanes l and l^32 hold the two halves of the heads of the same key
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    const float sv = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int key = n0 + r;
+    const bool keep = active && !ovf && lane < 32 && key < n_hi && key <= p && sv >= thr;
+    // every wave has taken this tile's compaction decisions before any count changes
+    __syncthreads();
+    const unsigned long long bm = __ballot(keep);
+    if (bm) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&qcnt[qi], (int)__popcll(bm));
+      base = __shfl(base, 0);
+      if (keep) {
+        const int pos = base + __popcll(bm & ((1ull << lane) - 1ull));
+        cs[pos] = sv;
+        co[pos] = (Off)(key - n_lo);
       }
     }
   }
+  __syncthreads();
   if (active) {
     const size_t slot = (size_t)i * nsplit + split;
-    wave_sync();
-    for (int e = lane; e < cnt; e += 64) {
+    const int cnt = qcnt[qi];
+    for (int e = lane + 64 * kh; e < cnt; e += 64 * (IDX_NW / QPB)) {
       cand_s[slot * cap + e] = cs[e];
-      cand_i[slot * cap + e] = ci[e];
+      cand_i[slot * cap + e] = n_lo + (int)co[e];
     }
-    if (lane == 0) cand_n[slot] = ovf ? -1 : cnt;
+    if (kh == 0 && lane == 0) cand_n[slot] = qovf[qi] ? -1 : cnt;
   }
 }
 
 // ---------------------------------------------------------------- 4. select + band refine
-// Block-level (256 threads) radix select of the k-th largest non-negative float.
-__device__ float block_kth_largest(const float* vals, int n, int k, int* hist, int* bcast) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
-  int need = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
-    for (int e = tid; e < n; e += 256) {
-      const uint32_t u = __float_as_uint(vals[e]);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      const int lane = tid;
-      const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-      const int own = h0 + h1 + h2 + h3;
-      int suf = own;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_down(suf, off);
-        if (lane + off < 64) suf += v;
-      }
-      const int above = suf - own;
-      if (above < need && suf >= need) {
-        int acc = above, digit, above_d;
-        if (acc + h3 >= need) { digit = 4 * lane + 3; above_d = acc; }
-        else { acc += h3;
-          if (acc + h2 >= need) { digit = 4 * lane + 2; above_d = acc; }
-          else { acc += h2;
-            if (acc + h1 >= need) { digit = 4 * lane + 1; above_d = acc; }
-            else { acc += h1; digit = 4 * lane; above_d = acc; } } }
-        bcast[0] = digit;
-        bcast[1] = above_d;
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)bcast[0] << shift;
-    pmask |= 255u << shift;
-    need -= bcast[1];
-    __syncthreads();
+// Block-level (256 threads) exact k-th largest of vals[0..n) (finite, n >= k):
+// linear histogram to find the bin, then an exact rank count inside the bin.
+// Returns false (and nothing) when the bin holds more than cap_bin entries.
+__device__ bool block_kth_exact(const float* vals, int n, int k, int* hist, int* misc, float* red,
+                                float* bin_vals, int cap_bin, float& out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float mx = -INFINITY, mn = INFINITY;
+  for (int e = tid; e < n; e += 256) {
+    const float v = vals[e];
+    mx = fmaxf(mx, v);
+    mn = fminf(mn, v);
   }
-  return __uint_as_float(prefix);
+  mx = wave_max(mx);
+  mn = wave_min(mn);
+  if (lane == 0) { red[wave] = mx; red[4 + wave] = mn; }
+  hist[tid] = 0;
+  if (tid == 0) misc[2] = 0;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  mn = fminf(fminf(red[4], red[5]), fminf(red[6], red[7]));
+  if (!(mx > mn)) {
+    out = mx;
+    __syncthreads();
+    return true;
+  }
+  const float inv_w = 256.0f / (mx - mn);
+  for (int e = tid; e < n; e += 256) atomicAdd(&hist[lin_bucket(vals[e], mn, inv_w)], 1);
+  __syncthreads();
+  if (wave == 0) {
+    int bin, above;
+    wave_find_bin(hist, k, lane, bin, above);
+    if (lane == 0) { misc[0] = bin; misc[1] = above; }
+  }
+  __syncthreads();
+  const int bin = misc[0], need = k - misc[1];
+  for (int e = tid; e < n; e += 256) {
+    const float v = vals[e];
+    if (lin_bucket(v, mn, inv_w) == bin) {
+      const int slot = atomicAdd(&misc[2], 1);
+      if (slot < cap_bin) bin_vals[slot] = v;
+    }
+  }
+  __syncthreads();
+  const int nb = misc[2];
+  if (nb > cap_bin) {
+    __syncthreads();
+    return false;
+  }
+  // the need-th largest inside the bin: the largest v with #{u >= v} >= need
+  float best = -INFINITY;
+  for (int e = tid; e < nb; e += 256) {
+    const float v = bin_vals[e];
+    int c = 0;
+    for (int f = 0; f < nb; ++f) c += bin_vals[f] >= v;
+    if (c >= need) best = fmaxf(best, v);
+  }
+  best = wave_max(best);
+  __syncthreads();
+  if (lane == 0) red[wave] = best;
+  __syncthreads();
+  out = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return true;
 }
 
 // Canonical fp64 score of key n for query i, computed by 32 lanes (one head
@@ -366,17 +503,20 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     int* __restrict__ fb_flag, int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   const int M_cap = nsplit * cap;
-  float* vs = (float*)dyn;                       // [M_cap] candidate scores
-  int* vi = (int*)(vs + M_cap);                  // [M_cap] candidate keys
-  unsigned char* cls = (unsigned char*)(vi + M_cap);   // [M_cap] 0 out, 1 in, 2 band
-  short* bid = (short*)(cls + ((M_cap + 15) & ~15));   // [M_cap] band id
+  float* vs = (float*)dyn;                              // [M_cap] candidate scores
+  int* vi = (int*)(vs + M_cap);                         // [M_cap] candidate keys
+  unsigned char* cls = (unsigned char*)(vi + M_cap);    // [M_cap] 0 out, 1 in, 2 band
+  short* bid = (short*)(cls + ((M_cap + 15) & ~15));    // [M_cap] band id
   double* bscore = (double*)(bid + ((M_cap + 7) & ~7)); // [RANK_CAP]
-  int* bkey = (int*)(bscore + RANK_CAP);          // [RANK_CAP]
-  unsigned char* bsel = (unsigned char*)(bkey + RANK_CAP);  // [RANK_CAP]
-  uint16_t* qrow = (uint16_t*)(bsel + RANK_CAP);  // [IH*ID]
-  int* hist = (int*)(qrow + IH * ID);             // [256]
-  int* misc = hist + 256;                         // [8]
-  int* wave_tot = misc + 8;                       // [4]
+  int* bkey = (int*)(bscore + RANK_CAP);                // [RANK_CAP]
+  float* binv = (float*)(bkey + RANK_CAP);              // [RANK_CAP] values of the threshold bin
+  unsigned char* bsel = (unsigned char*)(binv + RANK_CAP);  // [RANK_CAP]
+  uint16_t* qrow = (uint16_t*)(bsel + RANK_CAP);        // [IH*ID]
+  uint32_t* bitmap = (uint32_t*)(qrow + IH * ID);       // [RANK_WORDS]
+  int* tbase = (int*)(bitmap + RANK_WORDS);             // [256] per-thread rank bases
+  int* hist = tbase + 256;                              // [256]
+  int* misc = hist + 256;                               // [8]
+  float* red = (float*)(misc + 8);                      // [8]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = blockIdx.x;
@@ -385,7 +525,6 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
   int32_t* orow = idx_out + (size_t)i * topk;
   float* srow = score_out ? score_out + (size_t)i * topk : nullptr;
 
-  // gather candidate lists (ascending key order within and across splits)
   int M = 0;
   bool overflow = false;
   for (int sp = 0; sp < nsplit; ++sp) {
@@ -400,17 +539,18 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     if (tid == 0) fb_flag[i] = 1;
     return;
   }
-  if (tid == 0) fb_flag[i] = 0;
   __syncthreads();
 
   const float eps = eps_in[i];
-  int need_band = 0;
-  float tk = 0.f;
   if (nv <= topk) {
     // every visible key is in the list (the filter threshold never rose)
     for (int e = tid; e < M; e += 256) cls[e] = 1;
   } else {
-    tk = block_kth_largest(vs, M, topk, hist, misc);
+    float tk;
+    if (!block_kth_exact(vs, M, topk, hist, misc, red, binv, RANK_CAP, tk)) {
+      if (tid == 0) fb_flag[i] = 1;
+      return;
+    }
     const float hw = band_halfwidth(eps, tk);
     const float hi = tk + hw, lo = tk - hw;
     if (tid == 0) { misc[2] = 0; misc[3] = 0; }
@@ -428,12 +568,11 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     }
     __syncthreads();
     const int n_in = misc[2], nb = misc[3];
-    need_band = topk - n_in;
+    const int need_band = topk - n_in;
     if (nb > RANK_CAP || need_band < 0 || need_band > nb) {
       if (tid == 0) fb_flag[i] = 1;
       return;
     }
-    // stage the query (bf16) for the canonical re-score
     for (int e = tid; e < IH * ID / 8; e += 256)
       *(u32x4*)(qrow + 8 * e) = *(const u32x4*)(q + (size_t)i * IH * ID + 8 * e);
     __syncthreads();
@@ -442,45 +581,75 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     for (int b0 = wave * 2; b0 < nb; b0 += 8) {
       const int b = b0 + half;
       const int n = b < nb ? bkey[b] : bkey[0];
-      const double s = canonical_score_32lanes(qrow, k, wrow, n, l32, half * 32);
-      if (b < nb && l32 == 0) bscore[b] = s;
+      const double sc = canonical_score_32lanes(qrow, k, wrow, n, l32, half * 32);
+      if (b < nb && l32 == 0) bscore[b] = sc;
     }
     __syncthreads();
     for (int b = tid; b < nb; b += 256) {
-      const double s = bscore[b];
+      const double sc = bscore[b];
       const int key = bkey[b];
       int r = 0;
       for (int o = 0; o < nb; ++o) {
         const double so = bscore[o];
-        r += (so > s) || (so == s && bkey[o] < key);
+        r += (so > sc) || (so == sc && bkey[o] < key);
       }
       bsel[b] = r < need_band;
     }
     __syncthreads();
   }
+  if (tid == 0) fb_flag[i] = 0;
 
-  // stable compaction of kept candidates, in candidate (= ascending key) order
-  int base = 0;
-  for (int c0 = 0; c0 < M; c0 += 256) {
-    const int e = c0 + tid;
-    bool keep = false;
-    if (e < M) keep = cls[e] == 1 || (cls[e] == 2 && bsel[bid[e]]);
-    const unsigned long long bm = __ballot(keep);
-    if (lane == 0) wave_tot[wave] = __popcll(bm);
+  // Emit the kept keys in ascending order: for each window of RANK_WORDS*32 keys,
+  // mark kept keys in a bitmap; a key's output slot is the number of kept keys
+  // below it (prefix popcounts).
+  int done = 0;
+  for (int w0 = 0; w0 < N; w0 += RANK_WORDS * 32) {
+    for (int x = tid; x < RANK_WORDS; x += 256) bitmap[x] = 0u;
     __syncthreads();
-    int off = base;
-    for (int x = 0; x < wave; ++x) off += wave_tot[x];
-    if (keep) {
-      const int pos = off + __popcll(bm & ((1ull << lane) - 1ull));
-      if (pos < topk) {
-        orow[pos] = vi[e];
-        if (srow) srow[pos] = vs[e];
+    for (int e = tid; e < M; e += 256) {
+      const int key = vi[e];
+      const bool kept = cls[e] == 1 || (cls[e] == 2 && bsel[bid[e]]);
+      if (kept && key >= w0 && key < w0 + RANK_WORDS * 32)
+        atomicOr(&bitmap[(key - w0) >> 5], 1u << ((key - w0) & 31));
+    }
+    __syncthreads();
+    constexpr int WPT = RANK_WORDS / 256;        // words per thread
+    int own = 0;
+#pragma unroll
+    for (int x = 0; x < WPT; ++x) own += __popc(bitmap[tid * WPT + x]);
+    int incl = own;                              // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) misc[4 + wave] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int x = 0; x < wave; ++x) wbase += misc[4 + x];
+    tbase[tid] = wbase + incl - own;
+    const int total = misc[4] + misc[5] + misc[6] + misc[7];
+    __syncthreads();
+    for (int e = tid; e < M; e += 256) {
+      const int key = vi[e];
+      const bool kept = cls[e] == 1 || (cls[e] == 2 && bsel[bid[e]]);
+      if (kept && key >= w0 && key < w0 + RANK_WORDS * 32) {
+        const int word = (key - w0) >> 5, bit = (key - w0) & 31;
+        const int owner = word / WPT;
+        int rank = tbase[owner];
+        for (int x = owner * WPT; x < word; ++x) rank += __popc(bitmap[x]);
+        rank += __popc(bitmap[word] & ((1u << bit) - 1u));
+        const int pos = done + rank;
+        if (pos < topk) {
+          orow[pos] = key;
+          if (srow) srow[pos] = vs[e];
+        }
       }
     }
-    base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+    done += total;
     __syncthreads();
   }
-  for (int e = base + tid; e < topk; e += 256) {
+  for (int e = done + tid; e < topk; e += 256) {
     orow[e] = -1;
     if (srow) srow[e] = -INFINITY;
   }
@@ -611,11 +780,22 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   ns = ns > 3 ? 3 : ns;                 // the refine kernel holds nsplit * cap candidates in LDS
   ns = ns > max_by_n ? max_by_n : ns;
   if (ns < 1) ns = 1;
+  // 16-bit key offsets (and a 4-stage ring) when every split spans at most 65536 keys
+  const int ns16 = (N + 65535) / 65536;
+  if (ns16 <= 3 && ns < ns16) ns = ns16;
   int span = (N + ns - 1) / ns;
   span = (span + TK - 1) / TK * TK;
   pl.nsplit = ns;
   pl.span = span;
-  pl.cap = 3456;                        // (160 KiB - ring - histograms) / (4 queries x 8 B)
+  pl.small_off = span <= 65536;
+  pl.nstage = pl.small_off ? 4 : 3;
+  // candidate capacity: what the LDS holds after the ring, per query, in multiples of 64
+  const size_t fixed = (size_t)pl.nstage * IDX_STAGE + 256 * 4 + 4 * QPB * 4 + 16 * 4 + IDX_NW * 4;
+  const size_t per = QPB * (4 + (pl.small_off ? 2 : 4));
+  pl.cap = (int)(((163840 - fixed) / per) / 64 * 64);
+  // the refine kernel holds nsplit * cap candidates (11 bytes each) next to SELECT_FIXED bytes
+  const int cap_sel = (int)(((163840 - SELECT_FIXED) / 11 / ns) / 64 * 64);
+  if (pl.cap > cap_sel) pl.cap = cap_sel;
   pl.fb_blocks = L < 32 ? L : 32;
   if (pl.fb_blocks < 1) pl.fb_blocks = 1;
   size_t off = 0;
@@ -628,10 +808,9 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   pl.off_cand_i = take(sizeof(int) * (size_t)L * ns * pl.cap);
   pl.off_scratch = take(sizeof(double) * (size_t)pl.fb_blocks * N);
   pl.ws_bytes = off;
-  pl.filter_lds = IDX_NSTAGE * IDX_STAGE + QPB * pl.cap * 8 + QPB * 256 * 4;
+  pl.filter_lds = fixed + per * pl.cap;
   const size_t M = (size_t)ns * pl.cap;
-  pl.select_lds = M * 4 + M * 4 + ((M + 15) & ~(size_t)15) + ((M + 7) & ~(size_t)7) * 2 + RANK_CAP * 8 + RANK_CAP * 4 +
-                  RANK_CAP + IH * ID * 2 + 256 * 4 + 8 * 4 + 4 * 4;
+  pl.select_lds = M * 4 + M * 4 + ((M + 15) & ~(size_t)15) + ((M + 7) & ~(size_t)7) * 2 + SELECT_FIXED;
   return pl;
 }
 
@@ -648,7 +827,11 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
   hipError_t e;
   static bool attr_set = false;
   if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)score_filter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    e = hipFuncSetAttribute((const void*)score_filter_kernel<uint16_t, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)score_filter_kernel<int, 3>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute((const void*)select_refine_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
@@ -664,8 +847,13 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
   }
   {
     KernelTrace kt("indexer_score_filter", stream);
-    hipLaunchKernelGGL(score_filter_kernel, dim3((L + QPB - 1) / QPB, pl.nsplit), dim3(256), pl.filter_lds, stream, q,
-                       k, w, eps, L, N, topk, pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n);
+    const dim3 grid((L + QPB - 1) / QPB, pl.nsplit), block(64 * IDX_NW);
+    if (pl.small_off)
+      hipLaunchKernelGGL((score_filter_kernel<uint16_t, 4>), grid, block, pl.filter_lds, stream, q, k, w, eps, L, N,
+                         topk, pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n);
+    else
+      hipLaunchKernelGGL((score_filter_kernel<int, 3>), grid, block, pl.filter_lds, stream, q, k, w, eps, L, N, topk,
+                         pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n);
   }
   {
     KernelTrace kt("indexer_select_refine", stream);
