@@ -122,12 +122,12 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const int seg_base = SPARSE ? seg * SEG : 0;
     const int seg_cnt = SPARSE ? min(SEG, count - seg_base) : count;
     if (SPARSE) {
-      __syncthreads();                               // the previous segment's indices are no longer read
+      lds_barrier();                               // the previous segment's indices are no longer read
       for (int e = tid; e < seg_cnt; e += 64 * NW) {
         const int x = irow[seg_base + e];
         sidx[e] = (x >= 0 && x < N) ? x : -1;
       }
-      __syncthreads();
+      lds_barrier();
     }
     const int ntiles = (seg_cnt + T - 1) / T;
     for (int t = 0; t < AHEAD && t < ntiles; ++t) issue_tile(t, t % NSTAGE, seg_base, seg_cnt);
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
       const int s = t % NSTAGE;
       const int after = min(t + AHEAD - 1, ntiles - 1) - t;   // tiles issued after tile t
       wait_vm(after * nblk_w);
-      __syncthreads();                               // tile t is in LDS; stage of tile t-1 is free
+      lds_barrier();                               // tile t is in LDS; stage of tile t-1 is free
       if (t + AHEAD < ntiles) issue_tile(t + AHEAD, (t + AHEAD) % NSTAGE, seg_base, seg_cnt);
 
       const unsigned char* st = ring + (size_t)s * STAGE;
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
       // swap partial scores with the other half of this head group; both sum in the same order
       xch[(wave * 2 + 0) * 64 + lane] = sacc[0];
       xch[(wave * 2 + 1) * 64 + lane] = sacc[1];
-      __syncthreads();
+      lds_barrier();
       {
         const int pw = wave ^ 4;
         const f32x4 o0 = xch[(pw * 2 + 0) * 64 + lane], o1 = xch[(pw * 2 + 1) * 64 + lane];

@@ -62,6 +62,14 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also waits for
+// every outstanding global load (vmcnt(0)), which would drain the direct-to-LDS
+// prefetch ring; tile data is instead waited for explicitly with s_waitcnt
+// vmcnt(n) before the barrier that publishes a tile.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Butterfly over lane groups: combine lanes l, l^16, l^32 (the four 16-lane
 // groups that hold the same MFMA column).
 __device__ __forceinline__ float group4_max(float x) {

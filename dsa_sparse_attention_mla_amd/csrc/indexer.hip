@@ -33,8 +33,8 @@ namespace dsa {
 namespace {
 constexpr int ID = 128;                 // indexer head dim
 constexpr int IH = 32;                  // indexer heads
-constexpr int TK = 64;                  // keys per tile
-constexpr int IDX_STAGE = TK * ID * 2;  // one ring stage: 64 keys x 256 B (swizzled, unpadded)
+constexpr int TK = 128;                 // keys per tile of the score kernel
+constexpr int IDX_STAGE = TK * ID * 2;  // one LDS key stage: 128 keys x 256 B (swizzled, unpadded)
 constexpr int QPB = 4;                  // queries per workgroup
 constexpr int IDX_NW = 8;               // waves per score workgroup: 2 per query
 constexpr int RANK_WORDS = 4096;        // bitmap words for ordering the output (131072 keys per window)
@@ -167,36 +167,41 @@ __device__ __forceinline__ float block512_max(float x, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   x = wave_max(x);
   if (lane == 0) red[wave] = x;
-  __syncthreads();
+  lds_barrier();
   float r = red[0];
 #pragma unroll
   for (int v = 1; v < IDX_NW; ++v) r = fmaxf(r, red[v]);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 __device__ __forceinline__ float block512_min(float x, float* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   x = wave_min(x);
   if (lane == 0) red[wave] = x;
-  __syncthreads();
+  lds_barrier();
   float r = red[0];
 #pragma unroll
   for (int v = 1; v < IDX_NW; ++v) r = fminf(r, red[v]);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
 // Cooperative (all 512 threads) threshold update and in-place compaction of one
-// query's candidate list: tau = a lower bound of the list's k-th largest score
-// (smallest value of the linear-histogram bin holding it), then keep the entries
-// with score >= max(old threshold, tau - band(tau)). Returns the new count.
-template <typename Off>
-__device__ int block_compact(float* cs, Off* co, int cnt, int k, float eps, float& thr, int* hist, int* misc,
+// query's candidate list. The list is two segments of the query's region: lo
+// entries at [0, lo) and hi entries at [CAPS-hi, CAPS) (its two waves fill it from
+// opposite ends); entry e of the logical list is at seg_pos(e). tau = a lower
+// bound of the list's k-th largest score (smallest value of the linear-histogram
+// bin holding it); entries with score >= max(old threshold, tau - band(tau)) are
+// moved to [0, newc), in order. Returns newc.
+template <typename Off, int CAPS>
+__device__ int block_compact(float* cs, Off* co, int lo, int hi, int k, float eps, float& thr, int* hist, int* misc,
                              float* red) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cnt = lo + hi;
+  auto pos_of = [&](int e) { return e < lo ? e : CAPS - hi + (e - lo); };
   float mx = -INFINITY, mn = INFINITY;
   for (int e = tid; e < cnt; e += 64 * IDX_NW) {
-    const float v = cs[e];
+    const float v = cs[pos_of(e)];
     mx = fmaxf(mx, v);
     mn = fminf(mn, v);
   }
@@ -206,34 +211,37 @@ __device__ int block_compact(float* cs, Off* co, int cnt, int k, float eps, floa
   if (mx > mn) {
     const float inv_w = 256.0f / (mx - mn);
     if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int e = tid; e < cnt; e += 64 * IDX_NW) atomicAdd(&hist[lin_bucket(cs[e], mn, inv_w)], 1);
-    __syncthreads();
+    lds_barrier();
+    for (int e = tid; e < cnt; e += 64 * IDX_NW) atomicAdd(&hist[lin_bucket(cs[pos_of(e)], mn, inv_w)], 1);
+    lds_barrier();
     if (wave == 0) {
       int bin, above;
       wave_find_bin(hist, k, lane, bin, above);
       if (lane == 0) misc[0] = bin;
     }
-    __syncthreads();
+    lds_barrier();
     const int bin = misc[0];
     float tb = INFINITY;
     for (int e = tid; e < cnt; e += 64 * IDX_NW) {
-      const float v = cs[e];
+      const float v = cs[pos_of(e)];
       if (lin_bucket(v, mn, inv_w) == bin) tb = fminf(tb, v);
     }
     tau = block512_min(tb, red);
   }
   thr = fmaxf(thr, tau - band_halfwidth(eps, tau));
+  // A survivor's destination never exceeds the position of the entry being read
+  // (the hi segment starts at or after lo), so chunk-by-chunk in-place moves are safe.
   int newc = 0;
   for (int c0 = 0; c0 < cnt; c0 += 64 * IDX_NW) {
     const int e = c0 + tid;
     const bool in = e < cnt;
-    const float v = in ? cs[e] : 0.f;
-    const Off id = in ? co[e] : (Off)0;
+    const int ps = in ? pos_of(e) : 0;
+    const float v = in ? cs[ps] : 0.f;
+    const Off id = in ? co[ps] : (Off)0;
     const bool keep = in && v >= thr;
     const unsigned long long bm = __ballot(keep);
     if (lane == 0) misc[8 + wave] = __popcll(bm);
-    __syncthreads();                      // every entry of this chunk has been read
+    lds_barrier();                        // every entry of this chunk has been read
     int off = newc;
     for (int x = 0; x < wave; ++x) off += misc[8 + x];
     if (keep) {
@@ -243,37 +251,49 @@ __device__ int block_compact(float* cs, Off* co, int cnt, int k, float eps, floa
     }
 #pragma unroll
     for (int x = 0; x < IDX_NW; ++x) newc += misc[8 + x];
-    __syncthreads();
+    lds_barrier();
   }
   return newc;
 }
 
-// Keys stream through a ring of LDS stages filled by direct global->LDS loads,
-// NSTAGE-1 tiles ahead of use. Within a stage, key r's 16-byte chunk c sits at
-// chunk slot r*16 + (c ^ (r & 15)), so the 32 keys one MFMA operand read touches
-// fall in distinct banks. Eight waves: wave w scores query w%4 against key half
-// w/4 (32 keys) of every 64-key tile, so two waves share each SIMD. A query's
-// two waves append survivors (score, key offset within the split) to one LDS
-// list through wave-aggregated atomic slots. When a list nears capacity at a
-// tile boundary, the whole workgroup recomputes that query's threshold from the
-// list and compacts it.
-template <typename Off, int NSTAGE>
+// Largest candidate capacity per query that fits the LDS next to the two key stages.
+template <typename Off>
+struct FilterCap {
+  static constexpr int value =
+      (int)(((163840 - 2 * IDX_STAGE - 256 * 4 - 8 * QPB * 4 - 16 * 4 - IDX_NW * 4) / (QPB * (4 + sizeof(Off)))) / 64 * 64);
+};
+
+// Key tiles (128 keys x 256 B) are fetched into registers PF tiles ahead of use
+// (four 16-byte loads per thread per tile) and written to one of two LDS stages
+// just before they are needed; the loop is unrolled PF times so every register
+// slot is static and the compiler waits only for the loads it must. Within a
+// stage, key r's 16-byte chunk c sits at chunk slot r*16 + (c ^ (r & 15)), so
+// the 32 keys one MFMA operand read touches fall in distinct banks.
+// Eight waves: wave w scores query w%4 against keys [64h, 64h+64) of every tile,
+// h = w/4, as two independent 32-key MFMA chains, so two waves share each SIMD.
+// A query's two waves append survivors (score, key offset within the split) to
+// the query's LDS list from opposite ends, each tracking its own count. When a
+// list nears capacity at a tile boundary, the whole workgroup recomputes that
+// query's threshold from the list and compacts it.
+template <typename Off>
 __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int span, int nsplit, int cap,
     float* __restrict__ cand_s, int* __restrict__ cand_i, int* __restrict__ cand_n) {
-  constexpr int AHEAD = NSTAGE - 1;
-  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-  unsigned char* ring = dyn;                                          // [NSTAGE][TK*256]
-  float* cs_all = (float*)(dyn + NSTAGE * IDX_STAGE);                 // [QPB][cap]
-  Off* co_all = (Off*)(cs_all + QPB * cap);                           // [QPB][cap]
-  int* hist = (int*)(co_all + QPB * cap);                             // [256]
-  int* qcnt = hist + 256;                                             // [QPB]
-  float* qthr = (float*)(qcnt + QPB);                                 // [QPB]
-  int* qovf = (int*)(qthr + QPB);                                     // [QPB]
-  float* qeps = (float*)(qovf + QPB);                                 // [QPB]
-  int* misc = (int*)(qeps + QPB);                                     // [16]
-  float* red = (float*)(misc + 16);                                   // [IDX_NW]
+  constexpr int PF = 3;                 // tiles in flight in registers
+  constexpr int CAPS = FilterCap<Off>::value;
+  constexpr int MARGIN = 2 * 64 + 64;   // room for one tile's appends (128) plus slack
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * IDX_STAGE];
+  __shared__ float cs_all[QPB * CAPS];
+  __shared__ Off co_all[QPB * CAPS];
+  __shared__ int hist[256];
+  __shared__ __attribute__((aligned(16))) int qlo[QPB];   // entries at the low end, written by wave h=0
+  __shared__ __attribute__((aligned(16))) int qhi[QPB];   // entries at the high end, written by wave h=1
+  __shared__ __attribute__((aligned(16))) int qovf[QPB];
+  __shared__ float qthr[QPB];
+  __shared__ float qeps[QPB];
+  __shared__ int misc[16];
+  __shared__ float red[IDX_NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qi = wave & (QPB - 1), kh = wave / QPB;
@@ -285,8 +305,8 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
   const int p = N - L + ii;
   const int ilast = min(L - 1, (int)blockIdx.x * QPB + QPB - 1);
   const int n_hi = min(min(N, n_lo + span), N - L + ilast + 1);
-  float* cs = cs_all + qi * cap;
-  Off* co = co_all + qi * cap;
+  float* cs = cs_all + qi * CAPS;      // cap (<= CAPS) is the list capacity the refine step sizes for
+  Off* co = co_all + qi * CAPS;
 
   bf16x8 qa[ID / 16];
   {
@@ -298,109 +318,135 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
 #pragma unroll
   for (int j = 0; j < 16; ++j) wr[j] = w[(size_t)ii * IH + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)];
   if (tid < QPB) {
-    qcnt[tid] = 0;
-    qthr[tid] = -INFINITY;
+    qlo[tid] = 0;
+    qhi[tid] = 0;
     qovf[tid] = 0;
+    qthr[tid] = -INFINITY;
     qeps[tid] = eps_in[min((int)blockIdx.x * QPB + tid, L - 1)];
   }
+  int mycnt = 0;                        // this wave's entries in its segment (uniform)
 
-  // 16 wave instructions of 64 x 16 B fill one stage; wave w issues blocks w and w+8
-  auto issue_tile = [&](int n0, int s) {
-    unsigned char* st = ring + s * IDX_STAGE;
+  // thread tid fetches chunk slots tid + 512u (u < 4) of a tile: key r = slot / 16,
+  // chunk c = (slot % 16) ^ (r % 16), stored at the slot
+  auto fetch = [&](int t, u32x4 (&dst)[4]) {
+    const int n0 = n_lo + t * TK;
 #pragma unroll
-    for (int u = 0; u < 16 / IDX_NW; ++u) {
-      const int blk = wave + IDX_NW * u;
-      const int slot = blk * 64 + lane;
+    for (int u = 0; u < 4; ++u) {
+      const int slot = tid + 512 * u;
       const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
-      const int n = min(n0 + r, n_hi - 1);          // keys past the range fetch a harmless row
-      __builtin_amdgcn_global_load_lds((const void*)(k + (size_t)n * ID + c * 8),
-                                       (DSA_LDS void*)(st + blk * 1024), 16, 0, 0);
+      const int n = min(n0 + r, n_hi - 1);  // past the range: a harmless row
+      dst[u] = *(const u32x4*)(k + (size_t)n * ID + c * 8);
     }
   };
-
-  const int ntiles = n_hi > n_lo ? (n_hi - n_lo + TK - 1) / TK : 0;
-  for (int t = 0; t < AHEAD && t < ntiles; ++t) issue_tile(n_lo + t * TK, t % NSTAGE);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int s = t % NSTAGE;
-    const int n0 = n_lo + t * TK;
-    // tiles issued after tile t: min(AHEAD-1, ntiles-1-t), two instructions each per wave
-    const int after = min(t + AHEAD - 1, ntiles - 1) - t;
-    if (after >= 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if (after == 1) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + AHEAD < ntiles) issue_tile(n0 + AHEAD * TK, (t + AHEAD) % NSTAGE);
-    // Compaction at the tile boundary. The shared counts are stable from the barrier
-    // above until the barrier before this tile's appends, so every wave takes the same
-    // decisions, and the cooperative compaction below only writes them after barriers
-    // that every wave has reached.
-    int need = 0;
+  auto stage_in = [&](int sidx, const u32x4 (&src)[4]) {
 #pragma unroll
-    for (int x = 0; x < QPB; ++x) need |= ((qcnt[x] > cap - 2 * 64) && !qovf[x]) << x;
+    for (int u = 0; u < 4; ++u) *(u32x4*)(ring + sidx * IDX_STAGE + (tid + 512 * u) * 16) = src[u];
+  };
+  u32x4 pf[PF][4];
+
+  // One tile. Barrier 1 publishes tile t (staged by the previous body) and the
+  // previous tile's appends and counts; between barrier 1 and barrier 2 no count
+  // changes except inside the cooperative compaction, which publishes them only
+  // after barriers every wave reaches, so all waves take the same decisions. After
+  // barrier 2 (stage t%2 fully read) the tile's survivors are appended and tile
+  // t+1 moves from its register slot into the other stage; the slot then refetches
+  // tile t+1+PF.
+  auto body = [&](int t, u32x4 (&slot)[4], int ntiles) {
+    const int n0 = n_lo + t * TK;
+    lds_barrier();
+    const int4 vlo = *(const int4*)qlo, vhi = *(const int4*)qhi, vov = *(const int4*)qovf;
+    const int need = ((vlo.x + vhi.x > cap - MARGIN) && !vov.x) | (((vlo.y + vhi.y > cap - MARGIN) && !vov.y) << 1) |
+                     (((vlo.z + vhi.z > cap - MARGIN) && !vov.z) << 2) | (((vlo.w + vhi.w > cap - MARGIN) && !vov.w) << 3);
     if (need) {
-      __syncthreads();
+      lds_barrier();
 #pragma unroll 1
       for (int x = 0; x < QPB; ++x) {
         if (!((need >> x) & 1)) continue;
         float thr = qthr[x];
-        const int newc = block_compact<Off>(cs_all + x * cap, co_all + x * cap, qcnt[x], topk, qeps[x], thr,
-                                            hist, misc, red);
+        const int newc = block_compact<Off, CAPS>(cs_all + x * CAPS, co_all + x * CAPS, qlo[x], qhi[x], topk,
+                                                  qeps[x], thr, hist, misc, red);
+        lds_barrier();                  // every wave has read the old counts
         if (tid == 0) {
-          qcnt[x] = newc;
+          qlo[x] = newc;
+          qhi[x] = 0;
           qthr[x] = thr;
-          qovf[x] = newc > cap - 2 * 64;
+          qovf[x] = newc > cap - MARGIN;
         }
-        __syncthreads();
+        lds_barrier();
       }
+      mycnt = kh == 0 ? qlo[qi] : qhi[qi];
     }
     const float thr = qthr[qi];
     const bool ovf = qovf[qi] != 0;
 
-    const unsigned char* st = ring + s * IDX_STAGE;
-    const int r = 32 * kh + (lane & 31);
-    const unsigned char* kp = st + r * 256;
-    bf16x8 kf[ID / 16];                  // all operand reads in flight before the MFMA chain
+    const unsigned char* st = ring + (t & 1) * IDX_STAGE;
+    const int ra = 64 * kh + (lane & 31), rb = ra + 32;
+    bf16x8 ka[ID / 16], kb[ID / 16];     // all operand reads in flight before the MFMA chains
 #pragma unroll
-    for (int kc = 0; kc < ID / 16; ++kc) kf[kc] = *(const bf16x8*)(kp + (((2 * kc + (lane >> 5)) ^ (r & 15)) * 16));
-    f32x16 acc = {};
+    for (int kc = 0; kc < ID / 16; ++kc) {
+      const int c = 2 * kc + (lane >> 5);
+      ka[kc] = *(const bf16x8*)(st + ra * 256 + ((c ^ (ra & 15)) * 16));
+      kb[kc] = *(const bf16x8*)(st + rb * 256 + ((c ^ (rb & 15)) * 16));
+    }
+    f32x16 acca = {}, accb = {};
 #pragma unroll
-    for (int kc = 0; kc < ID / 16; ++kc) acc = mfma32x32x16(qa[kc], kf[kc], acc);
+    for (int kc = 0; kc < ID / 16; ++kc) {
+      acca = mfma32x32x16(qa[kc], ka[kc], acca);
+      accb = mfma32x32x16(qa[kc], kb[kc], accb);
+    }
     // ReLU as an integer max on the bit pattern (exact for every non-NaN float, -0 -> +0),
-    // then the weighted head sum in two interleaved chains
+    // then the weighted head sums
     float pa = 0.f, pb = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      pa = fmaf(wr[j], __int_as_float(max(__float_as_int(acc[j]), 0)), pa);
-      pb = fmaf(wr[j + 1], __int_as_float(max(__float_as_int(acc[j + 1]), 0)), pb);
+    for (int j = 0; j < 16; ++j) {
+      pa = fmaf(wr[j], __int_as_float(max(__float_as_int(acca[j]), 0)), pa);
+      pb = fmaf(wr[j], __int_as_float(max(__float_as_int(accb[j]), 0)), pb);
     }
-    const float part = pa + pb;
-    // lanes l and l^32 hold the two halves of the heads of the same key
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    // lanes l and l^32 hold the two head halves of one key: lanes < 32 get key l of the
+    // first chain (pa), lanes >= 32 key l-32 of the second (pb)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
     const float sv = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int key = n0 + r;
-    const bool keep = active && !ovf && lane < 32 && key < n_hi && key <= p && sv >= thr;
-    // every wave has taken this tile's compaction decisions before any count changes
-    __syncthreads();
+    const int key = n0 + 64 * kh + lane;
+    const bool keep = active && !ovf && key < n_hi && key <= p && sv >= thr;
+    lds_barrier();
     const unsigned long long bm = __ballot(keep);
     if (bm) {
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&qcnt[qi], (int)__popcll(bm));
-      base = __shfl(base, 0);
+      const int before = __popcll(bm & ((1ull << lane) - 1ull));
       if (keep) {
-        const int pos = base + __popcll(bm & ((1ull << lane) - 1ull));
+        const int pos = kh == 0 ? mycnt + before : CAPS - 1 - (mycnt + before);
         cs[pos] = sv;
         co[pos] = (Off)(key - n_lo);
       }
+      mycnt += __popcll(bm);
+      if (lane == 0) {
+        if (kh == 0) qlo[qi] = mycnt;
+        else qhi[qi] = mycnt;
+      }
     }
+    if (t + 1 < ntiles) stage_in((t + 1) & 1, slot);
+    if (t + 1 + PF < ntiles) fetch(t + 1 + PF, slot);
+  };
+
+  const int ntiles = n_hi > n_lo ? (n_hi - n_lo + TK - 1) / TK : 0;
+#pragma unroll
+  for (int t = 0; t < PF; ++t)
+    if (t < ntiles) fetch(t, pf[t]);
+  if (ntiles > 0) stage_in(0, pf[0]);
+  if (PF < ntiles) fetch(PF, pf[0]);
+  // tile t+1 sits in register slot (t+1) % PF
+  for (int t0 = 0; t0 < ntiles; t0 += PF) {
+    body(t0, pf[1], ntiles);
+    if (t0 + 1 < ntiles) body(t0 + 1, pf[2], ntiles);
+    if (t0 + 2 < ntiles) body(t0 + 2, pf[0], ntiles);
   }
-  __syncthreads();
+  lds_barrier();
   if (active) {
     const size_t slot = (size_t)i * nsplit + split;
-    const int cnt = qcnt[qi];
+    const int lo = qlo[qi], hi = qhi[qi], cnt = lo + hi;
     for (int e = lane + 64 * kh; e < cnt; e += 64 * (IDX_NW / QPB)) {
-      cand_s[slot * cap + e] = cs[e];
-      cand_i[slot * cap + e] = n_lo + (int)co[e];
+      const int ps = e < lo ? e : CAPS - hi + (e - lo);
+      cand_s[slot * cap + e] = cs[ps];
+      cand_i[slot * cap + e] = n_lo + (int)co[ps];
     }
     if (kh == 0 && lane == 0) cand_n[slot] = qovf[qi] ? -1 : cnt;
   }
@@ -788,11 +834,9 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   pl.nsplit = ns;
   pl.span = span;
   pl.small_off = span <= 65536;
-  pl.nstage = pl.small_off ? 4 : 3;
+  pl.nstage = 2;
   // candidate capacity: what the LDS holds after the ring, per query, in multiples of 64
-  const size_t fixed = (size_t)pl.nstage * IDX_STAGE + 256 * 4 + 4 * QPB * 4 + 16 * 4 + IDX_NW * 4;
-  const size_t per = QPB * (4 + (pl.small_off ? 2 : 4));
-  pl.cap = (int)(((163840 - fixed) / per) / 64 * 64);
+  pl.cap = pl.small_off ? FilterCap<uint16_t>::value : FilterCap<int>::value;
   // the refine kernel holds nsplit * cap candidates (11 bytes each) next to SELECT_FIXED bytes
   const int cap_sel = (int)(((163840 - SELECT_FIXED) / 11 / ns) / 64 * 64);
   if (pl.cap > cap_sel) pl.cap = cap_sel;
@@ -808,7 +852,7 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   pl.off_cand_i = take(sizeof(int) * (size_t)L * ns * pl.cap);
   pl.off_scratch = take(sizeof(double) * (size_t)pl.fb_blocks * N);
   pl.ws_bytes = off;
-  pl.filter_lds = fixed + per * pl.cap;
+  pl.filter_lds = 0;                    // all LDS of the score kernel is static
   const size_t M = (size_t)ns * pl.cap;
   pl.select_lds = M * 4 + M * 4 + ((M + 15) & ~(size_t)15) + ((M + 7) & ~(size_t)7) * 2 + SELECT_FIXED;
   return pl;
@@ -827,12 +871,7 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
   hipError_t e;
   static bool attr_set = false;
   if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)score_filter_kernel<uint16_t, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)score_filter_kernel<int, 3>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-    if (e != hipSuccess) return e;
+
     e = hipFuncSetAttribute((const void*)select_refine_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -849,10 +888,10 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
     KernelTrace kt("indexer_score_filter", stream);
     const dim3 grid((L + QPB - 1) / QPB, pl.nsplit), block(64 * IDX_NW);
     if (pl.small_off)
-      hipLaunchKernelGGL((score_filter_kernel<uint16_t, 4>), grid, block, pl.filter_lds, stream, q, k, w, eps, L, N,
+      hipLaunchKernelGGL((score_filter_kernel<uint16_t>), grid, block, 0, stream, q, k, w, eps, L, N,
                          topk, pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n);
     else
-      hipLaunchKernelGGL((score_filter_kernel<int, 3>), grid, block, pl.filter_lds, stream, q, k, w, eps, L, N, topk,
+      hipLaunchKernelGGL((score_filter_kernel<int>), grid, block, 0, stream, q, k, w, eps, L, N, topk,
                          pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n);
   }
   {
