@@ -38,13 +38,14 @@ constexpr int IDX_STAGE = TK * ID * 2;  // one LDS key stage: 128 keys x 256 B (
 constexpr int QPB = 4;                  // queries per workgroup
 constexpr int IDX_NW = 8;               // waves per score workgroup: 2 per query
 constexpr int RANK_WORDS = 4096;        // bitmap words for ordering the output (131072 keys per window)
+static_assert(RANK_WORDS * 4 >= 64 * IH * 8, "band dots alias the word-prefix table");
 constexpr int RANK_CAP = 1024;          // band entries ranked in select_refine
 constexpr int NORM_BLOCKS = 256;
 constexpr int FB_ROWS = 256;            // block size of the fallback kernel
 // LDS of the refine kernel besides the candidate arrays: band scores/keys/bin values/flags,
 // the staged query, the rank bitmap, rank bases, histogram, scratch
 constexpr size_t SELECT_FIXED = RANK_CAP * 8 + RANK_CAP * 4 + RANK_CAP * 4 + RANK_CAP + IH * ID * 2 + RANK_WORDS * 4 +
-                                256 * 4 + 256 * 4 + 8 * 4 + 8 * 4;
+                                RANK_WORDS * 4 + 256 * 4 + 256 * 4 + 16 * 4;
 }  // namespace
 
 __device__ __forceinline__ void wave_sync() {
@@ -518,28 +519,45 @@ __device__ bool block_kth_exact(const float* vals, int n, int k, int* hist, int*
   return true;
 }
 
-// Canonical fp64 score of key n for query i, computed by 32 lanes (one head
-// each): d_h summed over dims in ascending order, then the head terms added in
-// ascending head order. Every product and sum is a separate IEEE operation.
-__device__ double canonical_score_32lanes(const uint16_t* qrow_lds, const uint16_t* __restrict__ k,
-                                          const float* __restrict__ wrow, int n, int l32, int src_base) {
-  const uint16_t* kr = k + (size_t)n * ID;
+// Canonical fp64 scores of up to 64 band keys whose rows are staged in LDS
+// (krows, 256 B each): lane l32 of 32-lane group g owns head l32 and keys
+// g, g+8, ..., g+56 (eight independent chains). d_h is summed over dims in
+// ascending order; the head terms are then added in ascending head order by one
+// lane per key. Every product and sum is a separate IEEE operation.
+__device__ void canonical_scores_batch(const uint16_t* qrow_lds, const uint16_t* krows, int nkeys,
+                                       const float* __restrict__ wrow, double* dh, double* out) {
+  const int tid = threadIdx.x, g = tid >> 5, l32 = tid & 31;
   const uint16_t* qh = qrow_lds + l32 * ID;
-  double d = 0.0;
-  for (int c = 0; c < ID; c += 8) {
-    const u32x4 kv = *(const u32x4*)(kr + c);
+  double d[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) d[j] = 0.0;
+  for (int c = 0; c < ID / 8; ++c) {
+    const u32x4 qv = *(const u32x4*)(qh + 8 * c);
+    u32x4 kv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kv[j] = *(const u32x4*)(krows + (size_t)(g + 8 * j) * ID + 8 * c);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint16_t kb = (uint16_t)((kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-      d = __dadd_rn(d, __dmul_rn((double)bf_bits2f(qh[c + e]), (double)bf_bits2f(kb)));
+      const double qd = (double)bf_bits2f((uint16_t)((qv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double kd = (double)bf_bits2f((uint16_t)((kv[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+        d[j] = __dadd_rn(d[j], __dmul_rn(qd, kd));
+      }
     }
   }
-  double s = 0.0;
-  for (int h = 0; h < IH; ++h) {
-    const double dh = __shfl(d, src_base + h);
-    s = __dadd_rn(s, __dmul_rn((double)wrow[h], dh > 0.0 ? dh : 0.0));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dh[(g + 8 * j) * IH + l32] = d[j];
+  __syncthreads();
+  if (tid < nkeys) {
+    double sc = 0.0;
+    for (int h = 0; h < IH; ++h) {
+      const double v = dh[tid * IH + h];
+      sc = __dadd_rn(sc, __dmul_rn((double)wrow[h], v > 0.0 ? v : 0.0));
+    }
+    out[tid] = sc;
   }
-  return s;
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(256) void select_refine_kernel(
@@ -558,11 +576,14 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
   float* binv = (float*)(bkey + RANK_CAP);              // [RANK_CAP] values of the threshold bin
   unsigned char* bsel = (unsigned char*)(binv + RANK_CAP);  // [RANK_CAP]
   uint16_t* qrow = (uint16_t*)(bsel + RANK_CAP);        // [IH*ID]
-  uint32_t* bitmap = (uint32_t*)(qrow + IH * ID);       // [RANK_WORDS]
-  int* tbase = (int*)(bitmap + RANK_WORDS);             // [256] per-thread rank bases
+  uint32_t* bitmap = (uint32_t*)(qrow + IH * ID);       // [RANK_WORDS]; band key rows while re-scoring
+  int* wpre = (int*)(bitmap + RANK_WORDS);              // [RANK_WORDS] kept keys before each word
+  double* dh = (double*)wpre;                           // [64][IH] per-head dots of a band batch (same bytes;
+                                                        // the band re-score ends before the emit starts)
+  int* tbase = wpre + RANK_WORDS;                       // [256] per-thread rank bases
   int* hist = tbase + 256;                              // [256]
-  int* misc = hist + 256;                               // [8]
-  float* red = (float*)(misc + 8);                      // [8]
+  int* misc = hist + 256;                               // [16]
+  float* red = (float*)(misc + 8);                      // [8] (aliases misc[8..15])
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = blockIdx.x;
@@ -576,9 +597,31 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
   for (int sp = 0; sp < nsplit; ++sp) {
     const int c = cand_n[(size_t)i * nsplit + sp];
     if (c < 0) { overflow = true; break; }
-    const float* src_s = cand_s + ((size_t)i * nsplit + sp) * cap;
-    const int* src_i = cand_i + ((size_t)i * nsplit + sp) * cap;
-    for (int e = tid; e < c; e += 256) { vs[M + e] = src_s[e]; vi[M + e] = src_i[e]; }
+    // 16-byte loads, four in flight per thread; a list region holds cap entries
+    // (a multiple of 64), so the last partial vector stays inside it
+    const float4* src_s = (const float4*)(cand_s + ((size_t)i * nsplit + sp) * cap);
+    const int4* src_i = (const int4*)(cand_i + ((size_t)i * nsplit + sp) * cap);
+    const int nv4 = (c + 3) / 4;
+    for (int e0 = tid; e0 < nv4; e0 += 256 * 4) {
+      float4 a[4];
+      int4 b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + 256 * u;
+        if (e < nv4) { a[u] = src_s[e]; b[u] = src_i[e]; }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + 256 * u;
+        if (e < nv4) {
+          const float av[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
+          const int bv[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if (4 * e + x < c) { vs[M + 4 * e + x] = av[x]; vi[M + 4 * e + x] = bv[x]; }
+        }
+      }
+    }
     M += c;
   }
   if (overflow) {
@@ -601,16 +644,23 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     const float hi = tk + hw, lo = tk - hw;
     if (tid == 0) { misc[2] = 0; misc[3] = 0; }
     __syncthreads();
-    for (int e = tid; e < M; e += 256) {
-      const float v = vs[e];
-      unsigned char c = 0;
-      if (v > hi) { c = 1; atomicAdd(&misc[2], 1); }
-      else if (v >= lo) {
-        c = 2;
-        const int b = atomicAdd(&misc[3], 1);
+    for (int e0 = 0; e0 < M; e0 += 256) {
+      const int e = e0 + tid;
+      const float v = e < M ? vs[e] : -INFINITY;
+      const bool isin = e < M && v > hi, isband = e < M && !isin && v >= lo;
+      const unsigned long long bin_ = __ballot(isin), bband = __ballot(isband);
+      int base_in = 0, base_b = 0;
+      if (lane == 0) {
+        if (bin_) atomicAdd(&misc[2], (int)__popcll(bin_));
+        if (bband) base_b = atomicAdd(&misc[3], (int)__popcll(bband));
+      }
+      base_b = __builtin_amdgcn_readfirstlane(base_b);
+      (void)base_in;
+      if (e < M) cls[e] = isin ? 1 : (isband ? 2 : 0);
+      if (isband) {
+        const int b = base_b + __popcll(bband & ((1ull << lane) - 1ull));
         if (b < RANK_CAP) { bid[e] = (short)b; bkey[b] = vi[e]; }
       }
-      cls[e] = c;
     }
     __syncthreads();
     const int n_in = misc[2], nb = misc[3];
@@ -621,16 +671,18 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     }
     for (int e = tid; e < IH * ID / 8; e += 256)
       *(u32x4*)(qrow + 8 * e) = *(const u32x4*)(q + (size_t)i * IH * ID + 8 * e);
-    __syncthreads();
     const float* wrow = w + (size_t)i * IH;
-    const int half = lane >> 5, l32 = lane & 31;
-    for (int b0 = wave * 2; b0 < nb; b0 += 8) {
-      const int b = b0 + half;
-      const int n = b < nb ? bkey[b] : bkey[0];
-      const double sc = canonical_score_32lanes(qrow, k, wrow, n, l32, half * 32);
-      if (b < nb && l32 == 0) bscore[b] = sc;
+    uint16_t* krows = (uint16_t*)bitmap;                // 64 rows x 256 B = the bitmap's 16 KB
+    for (int b0 = 0; b0 < nb; b0 += 64) {
+      const int nk = min(64, nb - b0);
+      for (int x = tid; x < 64 * (ID / 8); x += 256) {   // row r, chunk c; missing rows repeat row 0
+        const int r = x >> 4, c = x & 15;
+        const int n = bkey[b0 + (r < nk ? r : 0)];
+        *(u32x4*)(krows + r * ID + 8 * c) = *(const u32x4*)(k + (size_t)n * ID + 8 * c);
+      }
+      __syncthreads();
+      canonical_scores_batch(qrow, krows, nk, wrow, dh, bscore + b0);
     }
-    __syncthreads();
     for (int b = tid; b < nb; b += 256) {
       const double sc = bscore[b];
       const int key = bkey[b];
@@ -671,9 +723,13 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     }
     if (lane == 63) misc[4 + wave] = incl;
     __syncthreads();
-    int wbase = 0;
-    for (int x = 0; x < wave; ++x) wbase += misc[4 + x];
-    tbase[tid] = wbase + incl - own;
+    int run = incl - own;
+    for (int x = 0; x < wave; ++x) run += misc[4 + x];
+#pragma unroll
+    for (int x = 0; x < WPT; ++x) {
+      wpre[tid * WPT + x] = run;
+      run += __popc(bitmap[tid * WPT + x]);
+    }
     const int total = misc[4] + misc[5] + misc[6] + misc[7];
     __syncthreads();
     for (int e = tid; e < M; e += 256) {
@@ -681,11 +737,7 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
       const bool kept = cls[e] == 1 || (cls[e] == 2 && bsel[bid[e]]);
       if (kept && key >= w0 && key < w0 + RANK_WORDS * 32) {
         const int word = (key - w0) >> 5, bit = (key - w0) & 31;
-        const int owner = word / WPT;
-        int rank = tbase[owner];
-        for (int x = owner * WPT; x < word; ++x) rank += __popc(bitmap[x]);
-        rank += __popc(bitmap[word] & ((1u << bit) - 1u));
-        const int pos = done + rank;
+        const int pos = done + wpre[word] + __popc(bitmap[word] & ((1u << bit) - 1u));
         if (pos < topk) {
           orow[pos] = key;
           if (srow) srow[pos] = vs[e];
