@@ -25,10 +25,12 @@
 //                        reads)
 // Splitting the row between two waves halves the per-wave registers (Q 36, O 64
 // VGPRs), which lets two waves share a SIMD and keep LDS reads in flight.
-// Row fetch: a ring of 3 LDS stages filled by direct global->LDS 16-byte loads
-// (no register staging), issued 2 tiles ahead of use; the index list of a
-// segment of up to 2048 keys is staged in LDS first, so a row address never
-// waits on an index load.
+// Row fetch: each tile's rows are loaded into registers PF tiles ahead of use
+// (five 16-byte loads per thread at most) and written to one of two LDS stages
+// just before they are needed; the tile loop is unrolled PF times so every
+// register slot is static and the compiler waits only for the loads it must.
+// The index list of a segment of up to 4096 keys is staged in LDS first, so a
+// row address never waits on an index load.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,43 +43,31 @@ constexpr int T = 32;                   // keys per tile
 constexpr int CH = D * 2 / 16;          // 16-byte chunks per row (72)
 constexpr int ROWCH = CH + 1;           // padded LDS row, in chunks (bank spread)
 constexpr int ROWB = ROWCH * 16;        // 1168 bytes
-constexpr int BLK = 64;                 // chunks per direct-to-LDS wave instruction
-constexpr int NBLK = (T * ROWCH + BLK - 1) / BLK;   // 37 instructions per tile
-constexpr int STAGE = NBLK * BLK * 16;  // 37888 bytes per ring stage
-constexpr int NSTAGE = 3;               // ring depth
-constexpr int AHEAD = NSTAGE - 1;       // tiles in flight beyond the current one
-constexpr int SEG = 2048;               // index entries staged per segment
+constexpr int STAGE = T * ROWB;         // 37376 bytes per LDS stage (two stages)
+constexpr int PF = 2;                   // tiles in flight in registers
+constexpr int CPT = (T * CH + 511) / 512;   // 16-byte chunks per thread per tile (5)
+constexpr int SEG = 4096;               // index entries staged per segment
 constexpr int KCH = D / 32 / 2;         // MFMA k-steps per half row (9)
 constexpr int NDBH = DV / 16 / 2;       // 16-wide value blocks per half (16)
 constexpr int NW = 8;                   // waves per workgroup: 4 head groups x 2 row halves
 constexpr int XCH_BYTES = NW * 64 * 32; // partial-score exchange: 8 floats per lane
-constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE + SEG * 4 + NSTAGE * T * 4 + XCH_BYTES;
+constexpr size_t LDS_BYTES = 2 * (size_t)STAGE + SEG * 4 + 2 * T * 4 + XCH_BYTES;
 }  // namespace
-
-// Wait until at most n of this wave's vector-memory operations are outstanding.
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-}
 
 template <bool SPARSE>
 __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, int L, int N, int H, int topk, int q0, int causal, float scale_log2) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-  unsigned char* ring = dyn;
-  int* sidx = (int*)(dyn + (size_t)NSTAGE * STAGE);
-  int* sflag = sidx + SEG;                                  // [NSTAGE][T]
-  f32x4* xch = (f32x4*)(sflag + NSTAGE * T);                // [NW][2][64] partial scores
+  unsigned char* ring = dyn;                                // [2][STAGE]
+  int* sidx = (int*)(dyn + 2 * (size_t)STAGE);              // [SEG]
+  int* sflag = sidx + SEG;                                  // [2][T]
+  f32x4* xch = (f32x4*)(sflag + 2 * T);                     // [NW][2][64] partial scores
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int b = blockIdx.y;
   const int i = q0 + blockIdx.x;
-  // a wave whose 16 heads lie beyond H computes on a clamped copy and stores nothing
   const int hg = wave & 3, half = wave >> 2;
   const bool wave_active = (blockIdx.z * 4 + hg) * 16 < H;
   const int head = wave_active ? (blockIdx.z * 4 + hg) * 16 + c16 : c16;
@@ -85,36 +75,124 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   const int count = SPARSE ? topk : (causal ? p + 1 : N);
   const uint16_t* kvb = kv + (size_t)b * N * D;
   const int32_t* irow = SPARSE ? idx + ((size_t)b * L + i) * topk : nullptr;
-  const int nblk_w = wave < NBLK % NW ? NBLK / NW + 1 : NBLK / NW;   // 5 or 4 instructions per tile
 
   bf16x8 qf[KCH];
   {
     const uint16_t* qrow = q + (((size_t)b * L + i) * H + head) * D + 288 * half + 8 * g;
 #pragma unroll
     for (int kc = 0; kc < KCH; ++kc) qf[kc] = *(const bf16x8*)(qrow + 32 * kc);
+    // Consume the fragments here, so their loads are known complete before the tile loop;
+    // otherwise the loop's merged wait state would drain the row prefetch every tile.
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc) asm volatile("" ::"v"(qf[kc]));
   }
   f32x4 o[NDBH];
 #pragma unroll
   for (int db = 0; db < NDBH; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
 
-  // Issue the direct-to-LDS loads of tile t (keys seg_base + 32t ...) into ring stage s.
-  auto issue_tile = [&](int t, int s, int seg_base, int seg_cnt) {
-    unsigned char* st = ring + (size_t)s * STAGE;
-    for (int u = 0; u < nblk_w; ++u) {
-      const int blk = wave + NW * u;
-      const int pch = blk * BLK + lane;             // chunk slot within the stage
-      const int r = pch / ROWCH, cpos = pch - r * ROWCH;
-      int key = -1;
-      if (r < T) {
-        const int slot = t * T + r;
-        if (slot < seg_cnt) key = SPARSE ? sidx[slot] : seg_base + slot;
-        if (cpos == 0) sflag[s * T + r] = key >= 0;
-      }
-      const int c = (r < T && cpos < CH) ? cpos : 0;   // padding slots fetch a harmless chunk
-      const uint16_t* src = kvb + (size_t)(key >= 0 ? key : 0) * D + c * 8;
-      __builtin_amdgcn_global_load_lds((const void*)src, (DSA_LDS void*)(st + blk * BLK * 16), 16, 0, 0);
+  // chunk u of this thread in a tile: c = tid + 512u (c < 32*72): row c/72, 16-byte column c%72
+  auto key_of = [&](int t, int r, int seg_base, int seg_cnt) -> int {
+    const int slot = t * T + r;
+    if (slot >= seg_cnt) return -1;
+    return SPARSE ? sidx[slot] : seg_base + slot;
+  };
+  // Every thread issues CPT loads for every fetch, also past the tile's chunks and past
+  // the last tile (those read row 0 and are never staged), so the number of outstanding
+  // loads is the same on every path and the compiler's waits stay exact.
+  auto fetch = [&](int t, u32x4 (&dst)[CPT], int seg_base, int seg_cnt) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = min(tid + 512 * u, T * CH - 1);
+      const int r = c / CH, col = c - r * CH;
+      const int key = key_of(t, r, seg_base, seg_cnt);
+      dst[u] = *(const u32x4*)(kvb + (size_t)(key >= 0 ? key : 0) * D + col * 8);   // invalid: row 0, masked
     }
+  };
+  auto stage_in = [&](int t, int st_i, const u32x4 (&src)[CPT], int seg_base, int seg_cnt) {
+    unsigned char* st = ring + (size_t)st_i * STAGE;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + 512 * u;
+      if (c < T * CH) {
+        const int r = c / CH, col = c - r * CH;
+        *(u32x4*)(st + r * ROWB + col * 16) = src[u];
+      }
+    }
+    if (tid < T) sflag[st_i * T + tid] = key_of(t, tid, seg_base, seg_cnt) >= 0;
+  };
+  u32x4 pf[PF][CPT];
+
+  // One tile. Barrier 1 publishes tile t; the partial-score exchange needs barrier 2.
+  // After the value product (stage t%2 and the exchange buffer fully read by this
+  // wave; every wave has passed barrier 2, so the other stage is free) tile t+1
+  // moves from its register slot into the other stage and the slot refetches t+1+PF.
+  auto body = [&](int t, u32x4 (&slot)[CPT], int ntiles, int seg_base, int seg_cnt) {
+    lds_barrier();
+    const int s = t & 1;
+    const unsigned char* st = ring + (size_t)s * STAGE;
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const unsigned char* rowp = st + (16 * kb + c16) * ROWB + 576 * half + 16 * g;
+#pragma unroll
+      for (int kc = 0; kc < KCH; ++kc) sacc[kb] = mfma16x16x32(*(const bf16x8*)(rowp + 64 * kc), qf[kc], sacc[kb]);
+    }
+    // swap partial scores with the other half of this head group; both sum in the same order
+    xch[(wave * 2 + 0) * 64 + lane] = sacc[0];
+    xch[(wave * 2 + 1) * 64 + lane] = sacc[1];
+    lds_barrier();
+    {
+      const int pw = wave ^ 4;
+      const f32x4 o0 = xch[(pw * 2 + 0) * 64 + lane], o1 = xch[(pw * 2 + 1) * 64 + lane];
+      sacc[0] = half == 0 ? sacc[0] + o0 : o0 + sacc[0];
+      sacc[1] = half == 0 ? sacc[1] + o1 : o1 + sacc[1];
+    }
+    float x[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool v = sflag[s * T + 16 * kb + 4 * g + j] != 0;
+        const float xv = v ? sacc[kb][j] * scale_log2 : -INFINITY;
+        x[kb * 4 + j] = xv;
+        tmax = fmaxf(tmax, xv);
+      }
+    tmax = group4_max(tmax);
+    const float mnew = fmaxf(m, tmax);
+    float pv[8];
+    float alpha = 1.f, psum = 0.f;
+    if (mnew == -INFINITY) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = 0.f;
+    } else {
+      alpha = exp2f(m - mnew);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = exp2f(x[e] - mnew);
+        psum += pv[e];
+      }
+    }
+    psum = group4_sum(psum);
+    lsum = lsum * alpha + psum;
+    m = mnew;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < NDBH; ++db) o[db] *= alpha;
+    }
+    const bf16x8 pk = pack_bf16x8(pv);
+    // V^T operand: lane (g, c16) points at row 4g + c16/4 (and 16 + that), columns 4*(c16%4)
+    const unsigned char* vb = st + (4 * g + (c16 >> 2)) * ROWB + 512 * half + 8 * (c16 & 3);
+#pragma unroll
+    for (int db = 0; db < NDBH; ++db) {
+      const short4v lo = lds_read_tr16(vb + 32 * db);
+      const short4v hi = lds_read_tr16(vb + 16 * ROWB + 32 * db);
+      o[db] = mfma16x16x32(join_bf16x8(lo, hi), pk, o[db]);
+    }
+    if (t + 1 < ntiles) stage_in(t + 1, (t + 1) & 1, slot, seg_base, seg_cnt);
+    fetch(t + 1 + PF, slot, seg_base, seg_cnt);
   };
 
   const int nseg = count > 0 ? (SPARSE ? (count + SEG - 1) / SEG : 1) : 0;
@@ -123,83 +201,31 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const int seg_cnt = SPARSE ? min(SEG, count - seg_base) : count;
     if (SPARSE) {
       lds_barrier();                               // the previous segment's indices are no longer read
-      for (int e = tid; e < seg_cnt; e += 64 * NW) {
-        const int x = irow[seg_base + e];
-        sidx[e] = (x >= 0 && x < N) ? x : -1;
+      // all of this thread's index loads in flight before any is used
+      constexpr int PER = SEG / (64 * NW);
+      int xs[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int e = tid + 64 * NW * u;
+        xs[u] = e < seg_cnt ? irow[seg_base + e] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int e = tid + 64 * NW * u;
+        if (e < seg_cnt) sidx[e] = (xs[u] >= 0 && xs[u] < N) ? xs[u] : -1;
       }
       lds_barrier();
     }
     const int ntiles = (seg_cnt + T - 1) / T;
-    for (int t = 0; t < AHEAD && t < ntiles; ++t) issue_tile(t, t % NSTAGE, seg_base, seg_cnt);
-
-    for (int t = 0; t < ntiles; ++t) {
-      const int s = t % NSTAGE;
-      const int after = min(t + AHEAD - 1, ntiles - 1) - t;   // tiles issued after tile t
-      wait_vm(after * nblk_w);
-      lds_barrier();                               // tile t is in LDS; stage of tile t-1 is free
-      if (t + AHEAD < ntiles) issue_tile(t + AHEAD, (t + AHEAD) % NSTAGE, seg_base, seg_cnt);
-
-      const unsigned char* st = ring + (size_t)s * STAGE;
-      f32x4 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const unsigned char* rowp = st + (16 * kb + c16) * ROWB + 576 * half + 16 * g;
-#pragma unroll
-        for (int kc = 0; kc < KCH; ++kc) sacc[kb] = mfma16x16x32(*(const bf16x8*)(rowp + 64 * kc), qf[kc], sacc[kb]);
-      }
-      // swap partial scores with the other half of this head group; both sum in the same order
-      xch[(wave * 2 + 0) * 64 + lane] = sacc[0];
-      xch[(wave * 2 + 1) * 64 + lane] = sacc[1];
-      lds_barrier();
-      {
-        const int pw = wave ^ 4;
-        const f32x4 o0 = xch[(pw * 2 + 0) * 64 + lane], o1 = xch[(pw * 2 + 1) * 64 + lane];
-        sacc[0] = half == 0 ? sacc[0] + o0 : o0 + sacc[0];
-        sacc[1] = half == 0 ? sacc[1] + o1 : o1 + sacc[1];
-      }
-      float x[8];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool v = sflag[s * T + 16 * kb + 4 * g + j] != 0;
-          const float xv = v ? sacc[kb][j] * scale_log2 : -INFINITY;
-          x[kb * 4 + j] = xv;
-          tmax = fmaxf(tmax, xv);
-        }
-      tmax = group4_max(tmax);
-      const float mnew = fmaxf(m, tmax);
-      float pv[8];
-      float alpha = 1.f, psum = 0.f;
-      if (mnew == -INFINITY) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-      } else {
-        alpha = exp2f(m - mnew);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = exp2f(x[e] - mnew);
-          psum += pv[e];
-        }
-      }
-      psum = group4_sum(psum);
-      lsum = lsum * alpha + psum;
-      m = mnew;
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < NDBH; ++db) o[db] *= alpha;
-      }
-      const bf16x8 pk = pack_bf16x8(pv);
-      // V^T operand: lane (g, c16) points at row 4g + c16/4 (and 16 + that), columns 4*(c16%4)
-      const unsigned char* vb = st + (4 * g + (c16 >> 2)) * ROWB + 512 * half + 8 * (c16 & 3);
-#pragma unroll
-      for (int db = 0; db < NDBH; ++db) {
-        const short4v lo = lds_read_tr16(vb + 32 * db);
-        const short4v hi = lds_read_tr16(vb + 16 * ROWB + 32 * db);
-        o[db] = mfma16x16x32(join_bf16x8(lo, hi), pk, o[db]);
-      }
+    for (int t = 0; t < PF; ++t) fetch(t, pf[t], seg_base, seg_cnt);
+    if (ntiles > 0) stage_in(0, 0, pf[0], seg_base, seg_cnt);
+    fetch(PF, pf[0], seg_base, seg_cnt);
+    // tile t+1 sits in register slot (t+1) % PF
+    static_assert(PF == 2, "the unrolled tile loop below assumes two register slots");
+    for (int t0 = 0; t0 < ntiles; t0 += PF) {
+      body(t0, pf[1], ntiles, seg_base, seg_cnt);
+      if (t0 + 1 < ntiles) body(t0 + 1, pf[0], ntiles, seg_base, seg_cnt);
     }
   }
 

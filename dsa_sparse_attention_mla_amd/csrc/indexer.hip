@@ -318,6 +318,12 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
   float wr[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) wr[j] = w[(size_t)ii * IH + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)];
+  // Consume the fragments and weights here, so their loads are known complete before the
+  // tile loop; otherwise the loop's merged wait state would drain the key prefetch.
+#pragma unroll
+  for (int kc = 0; kc < ID / 16; ++kc) asm volatile("" ::"v"(qa[kc]));
+#pragma unroll
+  for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(wr[j]));
   if (tid < QPB) {
     qlo[tid] = 0;
     qhi[tid] = 0;
@@ -329,6 +335,9 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
 
   // thread tid fetches chunk slots tid + 512u (u < 4) of a tile: key r = slot / 16,
   // chunk c = (slot % 16) ^ (r % 16), stored at the slot
+  // Every fetch issues its four loads, also past the last tile (clamped rows, never
+  // staged), so the number of outstanding loads is the same on every path and the
+  // compiler's waits stay exact.
   auto fetch = [&](int t, u32x4 (&dst)[4]) {
     const int n0 = n_lo + t * TK;
 #pragma unroll
@@ -425,15 +434,16 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
       }
     }
     if (t + 1 < ntiles) stage_in((t + 1) & 1, slot);
-    if (t + 1 + PF < ntiles) fetch(t + 1 + PF, slot);
+    fetch(t + 1 + PF, slot);
   };
 
   const int ntiles = n_hi > n_lo ? (n_hi - n_lo + TK - 1) / TK : 0;
+  if (ntiles > 0) {
 #pragma unroll
-  for (int t = 0; t < PF; ++t)
-    if (t < ntiles) fetch(t, pf[t]);
-  if (ntiles > 0) stage_in(0, pf[0]);
-  if (PF < ntiles) fetch(PF, pf[0]);
+    for (int t = 0; t < PF; ++t) fetch(t, pf[t]);
+    stage_in(0, pf[0]);
+    fetch(PF, pf[0]);
+  }
   // tile t+1 sits in register slot (t+1) % PF
   for (int t0 = 0; t0 < ntiles; t0 += PF) {
     body(t0, pf[1], ntiles);
