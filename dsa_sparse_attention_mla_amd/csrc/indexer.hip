@@ -33,8 +33,8 @@ namespace dsa {
 namespace {
 constexpr int ID = 128;                 // indexer head dim
 constexpr int IH = 32;                  // indexer heads
-constexpr int TK = 128;                 // keys per tile of the score kernel
-constexpr int IDX_STAGE = TK * ID * 2;  // one LDS key stage: 128 keys x 256 B (swizzled, unpadded)
+constexpr int TK = 256;                 // keys per tile of the score kernel
+constexpr int IDX_STAGE = TK * ID * 2;  // the LDS key stage: 256 keys x 256 B (swizzled, unpadded)
 constexpr int QPB = 4;                  // queries per workgroup
 constexpr int IDX_NW = 8;               // waves per score workgroup: 2 per query
 constexpr int RANK_WORDS = 4096;        // bitmap words for ordering the output (131072 keys per window)
@@ -257,21 +257,21 @@ __device__ int block_compact(float* cs, Off* co, int lo, int hi, int k, float ep
   return newc;
 }
 
-// Largest candidate capacity per query that fits the LDS next to the two key stages.
+// Largest candidate capacity per query that fits the LDS next to the key stage.
 template <typename Off>
 struct FilterCap {
   static constexpr int value =
-      (int)(((163840 - 2 * IDX_STAGE - 256 * 4 - 8 * QPB * 4 - 16 * 4 - IDX_NW * 4) / (QPB * (4 + sizeof(Off)))) / 64 * 64);
+      (int)(((163840 - IDX_STAGE - 256 * 4 - 8 * QPB * 4 - 16 * 4 - IDX_NW * 4) / (QPB * (4 + sizeof(Off)))) / 64 * 64);
 };
 
-// Key tiles (128 keys x 256 B) are fetched into registers PF tiles ahead of use
-// (four 16-byte loads per thread per tile) and written to one of two LDS stages
-// just before they are needed; the loop is unrolled PF times so every register
-// slot is static and the compiler waits only for the loads it must. Within a
-// stage, key r's 16-byte chunk c sits at chunk slot r*16 + (c ^ (r & 15)), so
-// the 32 keys one MFMA operand read touches fall in distinct banks.
-// Eight waves: wave w scores query w%4 against keys [64h, 64h+64) of every tile,
-// h = w/4, as two independent 32-key MFMA chains, so two waves share each SIMD.
+// Key tiles (256 keys x 256 B) are fetched into registers one tile ahead of use
+// (eight 16-byte loads per thread) and written into the single LDS stage once
+// every wave has finished reading the previous tile. Within the stage, key r's
+// 16-byte chunk c sits at chunk slot r*16 + (c ^ (r & 15)), so the 32 keys one
+// MFMA operand read touches fall in distinct banks.
+// Eight waves: wave w scores query w%4 against keys [128h, 128h+128) of every
+// tile, h = w/4, as four independent 32-key MFMA chains (two pairs), so two
+// waves share each SIMD with plenty of independent work between barriers.
 // A query's two waves append survivors (score, key offset within the split) to
 // the query's LDS list from opposite ends, each tracking its own count. When a
 // list nears capacity at a tile boundary, the whole workgroup recomputes that
@@ -281,10 +281,11 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int span, int nsplit, int cap,
     float* __restrict__ cand_s, int* __restrict__ cand_i, int* __restrict__ cand_n) {
-  constexpr int PF = 3;                 // tiles in flight in registers
   constexpr int CAPS = FilterCap<Off>::value;
-  constexpr int MARGIN = 2 * 64 + 64;   // room for one tile's appends (128) plus slack
-  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * IDX_STAGE];
+  constexpr int PER_WAVE = TK / 2;      // keys per wave per tile (128)
+  constexpr int MARGIN = 2 * PER_WAVE + 64;   // room for one tile's appends plus slack
+  constexpr int CPT = TK * 16 / 512;    // 16-byte chunks per thread per tile (8)
+  __shared__ __attribute__((aligned(16))) unsigned char stage[IDX_STAGE];
   __shared__ float cs_all[QPB * CAPS];
   __shared__ Off co_all[QPB * CAPS];
   __shared__ int hist[256];
@@ -333,36 +334,69 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
   }
   int mycnt = 0;                        // this wave's entries in its segment (uniform)
 
-  // thread tid fetches chunk slots tid + 512u (u < 4) of a tile: key r = slot / 16,
-  // chunk c = (slot % 16) ^ (r % 16), stored at the slot
-  // Every fetch issues its four loads, also past the last tile (clamped rows, never
-  // staged), so the number of outstanding loads is the same on every path and the
-  // compiler's waits stay exact.
-  auto fetch = [&](int t, u32x4 (&dst)[4]) {
+  // thread tid fetches chunk slots tid + 512u (u < CPT) of a tile: key r = slot / 16,
+  // chunk c = (slot % 16) ^ (r % 16), stored at the slot. Every fetch issues all its
+  // loads, also past the last tile (clamped rows, never staged), so the number of
+  // outstanding loads is the same on every path and the compiler's waits stay exact.
+  u32x4 pf[CPT];
+  auto fetch = [&](int t) {
     const int n0 = n_lo + t * TK;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < CPT; ++u) {
       const int slot = tid + 512 * u;
       const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
-      const int n = min(n0 + r, n_hi - 1);  // past the range: a harmless row
-      dst[u] = *(const u32x4*)(k + (size_t)n * ID + c * 8);
+      const int n = min(n0 + r, n_hi - 1);
+      pf[u] = *(const u32x4*)(k + (size_t)n * ID + c * 8);
     }
   };
-  auto stage_in = [&](int sidx, const u32x4 (&src)[4]) {
+  auto stage_in = [&]() {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *(u32x4*)(ring + sidx * IDX_STAGE + (tid + 512 * u) * 16) = src[u];
+    for (int u = 0; u < CPT; ++u) *(u32x4*)(stage + (tid + 512 * u) * 16) = pf[u];
   };
-  u32x4 pf[PF][4];
 
-  // One tile. Barrier 1 publishes tile t (staged by the previous body) and the
-  // previous tile's appends and counts; between barrier 1 and barrier 2 no count
-  // changes except inside the cooperative compaction, which publishes them only
-  // after barriers every wave reaches, so all waves take the same decisions. After
-  // barrier 2 (stage t%2 fully read) the tile's survivors are appended and tile
-  // t+1 moves from its register slot into the other stage; the slot then refetches
-  // tile t+1+PF.
-  auto body = [&](int t, u32x4 (&slot)[4], int ntiles) {
+  // two 32-key MFMA chains: scores of keys r0 + lane (lanes < 32) and r0 + 32 + (lane - 32)
+  auto score_pair = [&](int r0) -> float {
+    const int ra = r0 + (lane & 31), rb = ra + 32;
+    bf16x8 ka[ID / 16], kb[ID / 16];
+#pragma unroll
+    for (int kc = 0; kc < ID / 16; ++kc) {
+      const int c = 2 * kc + (lane >> 5);
+      ka[kc] = *(const bf16x8*)(stage + ra * 256 + ((c ^ (ra & 15)) * 16));
+      kb[kc] = *(const bf16x8*)(stage + rb * 256 + ((c ^ (rb & 15)) * 16));
+    }
+    f32x16 acca = {}, accb = {};
+#pragma unroll
+    for (int kc = 0; kc < ID / 16; ++kc) {
+      acca = mfma32x32x16(qa[kc], ka[kc], acca);
+      accb = mfma32x32x16(qa[kc], kb[kc], accb);
+    }
+    // ReLU as an integer max on the bit pattern (exact for every non-NaN float, -0 -> +0),
+    // then the weighted head sums
+    float pa = 0.f, pb = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      pa = fmaf(wr[j], __int_as_float(max(__float_as_int(acca[j]), 0)), pa);
+      pb = fmaf(wr[j], __int_as_float(max(__float_as_int(accb[j]), 0)), pb);
+    }
+    // lanes l and l^32 hold the two head halves of one key: lanes < 32 get key l of the
+    // first chain (pa), lanes >= 32 key l-32 of the second (pb)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  };
+
+  const int ntiles = n_hi > n_lo ? (n_hi - n_lo + TK - 1) / TK : 0;
+  if (ntiles > 0) {
+    fetch(0);
+    stage_in();
+    fetch(1);
+  }
+  for (int t = 0; t < ntiles; ++t) {
     const int n0 = n_lo + t * TK;
+    // Barrier 1 publishes tile t and the previous tile's appends and counts; until
+    // barrier 2 no count changes except inside the cooperative compaction, which
+    // publishes them only after barriers every wave reaches, so all waves take the
+    // same decisions. After barrier 2 the stage is free: survivors are appended,
+    // tile t+1 moves in from registers and the registers fetch tile t+2.
     lds_barrier();
     const int4 vlo = *(const int4*)qlo, vhi = *(const int4*)qhi, vov = *(const int4*)qovf;
     const int need = ((vlo.x + vhi.x > cap - MARGIN) && !vov.x) | (((vlo.y + vhi.y > cap - MARGIN) && !vov.y) << 1) |
@@ -389,66 +423,36 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
     const float thr = qthr[qi];
     const bool ovf = qovf[qi] != 0;
 
-    const unsigned char* st = ring + (t & 1) * IDX_STAGE;
-    const int ra = 64 * kh + (lane & 31), rb = ra + 32;
-    bf16x8 ka[ID / 16], kb[ID / 16];     // all operand reads in flight before the MFMA chains
-#pragma unroll
-    for (int kc = 0; kc < ID / 16; ++kc) {
-      const int c = 2 * kc + (lane >> 5);
-      ka[kc] = *(const bf16x8*)(st + ra * 256 + ((c ^ (ra & 15)) * 16));
-      kb[kc] = *(const bf16x8*)(st + rb * 256 + ((c ^ (rb & 15)) * 16));
-    }
-    f32x16 acca = {}, accb = {};
-#pragma unroll
-    for (int kc = 0; kc < ID / 16; ++kc) {
-      acca = mfma32x32x16(qa[kc], ka[kc], acca);
-      accb = mfma32x32x16(qa[kc], kb[kc], accb);
-    }
-    // ReLU as an integer max on the bit pattern (exact for every non-NaN float, -0 -> +0),
-    // then the weighted head sums
-    float pa = 0.f, pb = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      pa = fmaf(wr[j], __int_as_float(max(__float_as_int(acca[j]), 0)), pa);
-      pb = fmaf(wr[j], __int_as_float(max(__float_as_int(accb[j]), 0)), pb);
-    }
-    // lanes l and l^32 hold the two head halves of one key: lanes < 32 get key l of the
-    // first chain (pa), lanes >= 32 key l-32 of the second (pb)
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
-    const float sv = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int key = n0 + 64 * kh + lane;
-    const bool keep = active && !ovf && key < n_hi && key <= p && sv >= thr;
+    const int r0 = PER_WAVE * kh;
+    const float sv0 = score_pair(r0);
+    const float sv1 = score_pair(r0 + 64);
+    const int key0 = n0 + r0 + lane, key1 = key0 + 64;
+    const bool keep0 = active && !ovf && key0 < n_hi && key0 <= p && sv0 >= thr;
+    const bool keep1 = active && !ovf && key1 < n_hi && key1 <= p && sv1 >= thr;
     lds_barrier();
-    const unsigned long long bm = __ballot(keep);
-    if (bm) {
-      const int before = __popcll(bm & ((1ull << lane) - 1ull));
-      if (keep) {
-        const int pos = kh == 0 ? mycnt + before : CAPS - 1 - (mycnt + before);
-        cs[pos] = sv;
-        co[pos] = (Off)(key - n_lo);
+    const unsigned long long bm0 = __ballot(keep0), bm1 = __ballot(keep1);
+    if (bm0 | bm1) {
+      const int b0 = __popcll(bm0);
+      const int before0 = __popcll(bm0 & ((1ull << lane) - 1ull));
+      const int before1 = b0 + __popcll(bm1 & ((1ull << lane) - 1ull));
+      if (keep0) {
+        const int pos = kh == 0 ? mycnt + before0 : CAPS - 1 - (mycnt + before0);
+        cs[pos] = sv0;
+        co[pos] = (Off)(key0 - n_lo);
       }
-      mycnt += __popcll(bm);
+      if (keep1) {
+        const int pos = kh == 0 ? mycnt + before1 : CAPS - 1 - (mycnt + before1);
+        cs[pos] = sv1;
+        co[pos] = (Off)(key1 - n_lo);
+      }
+      mycnt += b0 + __popcll(bm1);
       if (lane == 0) {
         if (kh == 0) qlo[qi] = mycnt;
         else qhi[qi] = mycnt;
       }
     }
-    if (t + 1 < ntiles) stage_in((t + 1) & 1, slot);
-    fetch(t + 1 + PF, slot);
-  };
-
-  const int ntiles = n_hi > n_lo ? (n_hi - n_lo + TK - 1) / TK : 0;
-  if (ntiles > 0) {
-#pragma unroll
-    for (int t = 0; t < PF; ++t) fetch(t, pf[t]);
-    stage_in(0, pf[0]);
-    fetch(PF, pf[0]);
-  }
-  // tile t+1 sits in register slot (t+1) % PF
-  for (int t0 = 0; t0 < ntiles; t0 += PF) {
-    body(t0, pf[1], ntiles);
-    if (t0 + 1 < ntiles) body(t0 + 1, pf[2], ntiles);
-    if (t0 + 2 < ntiles) body(t0 + 2, pf[0], ntiles);
+    if (t + 1 < ntiles) stage_in();
+    fetch(t + 2);
   }
   lds_barrier();
   if (active) {
@@ -896,7 +900,7 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   pl.nsplit = ns;
   pl.span = span;
   pl.small_off = span <= 65536;
-  pl.nstage = 2;
+  pl.nstage = 1;
   // candidate capacity: what the LDS holds after the ring, per query, in multiples of 64
   pl.cap = pl.small_off ? FilterCap<uint16_t>::value : FilterCap<int>::value;
   // the refine kernel holds nsplit * cap candidates (11 bytes each) next to SELECT_FIXED bytes
