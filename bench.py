@@ -18,7 +18,13 @@ The line also carries:
                 L = N = 4096, absorbed at L = 512 / N = 16384) with their MFMA
                 fractions.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+  traffic       HBM bytes per launch of the dominant kernel from rocprofv3's
+                FETCH_SIZE / WRITE_SIZE counters, scaled by what the same
+                counters read for a plain copy of known size
+                (python bench.py --copy-calibration 1024); null once the
+                kernel's source differs from the one the counters were taken on.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -36,6 +42,19 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
 L, N, TOPK, BLOCK, H = 1024, 131072, 2048, 4096, 64
 SEED = 1004
+
+# rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) on a 1 GiB device copy read
+# 524302 KiB fetched and 1048576 KiB written per dispatch: fetch counts half the
+# bytes a copy moves on this chip, write counts all of them.
+FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
+# Counter readings (KiB per dispatch, mean of 5 launches of this workload) and a
+# digest of the kernel sources they were taken on.
+COUNTERS = {
+    "indexer_score_filter": {"fetch_kib": 139549.2, "write_kib": 54382.0,
+                             "sources": ("indexer.hip", "common.h"), "sha256_16": "6ebcf3ef3a9b40e0"},
+    "sparse_attn": {"fetch_kib": 892832.5, "write_kib": 69635.0,
+                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "3523ea51723a53c2"},
+}
 METRIC = "prefill tok/s at 128K ctx (sparse MLA); MFMA util %, HBM GB/s % of peak"
 
 
@@ -56,6 +75,33 @@ def sparse_attn_bytes(L, topk, H):
 
 def sparse_attn_flops(L, topk, H):
     return L * topk * H * 2 * (576 + 512)
+
+
+def traffic_bytes(kernel):
+    """HBM bytes per launch from the calibrated counters, or None if the kernel changed since."""
+    import hashlib
+    c = COUNTERS.get(kernel)
+    if c is None:
+        return None
+    m = hashlib.sha256()
+    for f in c["sources"]:
+        with open(os.path.join(HERE, "dsa_sparse_attention_mla_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    if m.hexdigest()[:16] != c["sha256_16"]:
+        return None
+    return (c["fetch_kib"] * FETCH_FACTOR + c["write_kib"] * WRITE_FACTOR) * 1024.0
+
+
+def copy_calibration(mib):
+    """A plain device copy of `mib` MiB, three times, for calibrating the byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {mib} MiB three times")
 
 
 def cpu_baseline(g, sample):
@@ -124,15 +170,21 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=96)
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(query sharding needs no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     import dsa_sparse_attention_mla_amd as dm
@@ -176,13 +228,13 @@ def main():
         fl = indexer_flops(L, N)
         ach = fl / (t_idx * 1e-3) / 1e12
         roof = {"kernel": "indexer_score_filter", "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic_bytes("indexer_score_filter"),
                 "per_launch": f"{fl:.4e} FLOP (8192 per visible query-key pair)", "ms": t_idx}
     else:
         by = sparse_attn_bytes(L, TOPK, H)
         ach = by / (t_att * 1e-3) / 1e9
         roof = {"kernel": "sparse_attn", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                "frac": ach / PEAK_HBM_GBS, "traffic": traffic_bytes("sparse_attn"),
                 "per_launch": f"{by:.4e} B (gathered rows, q, out, idx)", "ms": t_att}
 
     other = None
