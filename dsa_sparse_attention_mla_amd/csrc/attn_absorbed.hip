@@ -168,10 +168,10 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) pv[e] = 0.f;
     } else {
-      alpha = exp2f(m - mnew);
+      alpha = exp2_fast(m - mnew);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pv[e] = exp2f(x[e] - mnew);
+        pv[e] = exp2_fast(x[e] - mnew);
         psum += pv[e];
       }
     }

@@ -22,6 +22,7 @@ namespace dsa {
 
 namespace {
 constexpr int DN = 128, DR = 64, DQK = DN + DR, DVN = 128;
+static_assert(DVN == DN, "K_nope and V rows share one address formula");
 constexpr int T = 32;
 }  // namespace
 
@@ -171,10 +172,10 @@ __global__ __launch_bounds__(256) void nonabsorbed_attn_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) pv[e] = 0.f;
     } else {
-      alpha = exp2f(m - mnew);
+      alpha = exp2_fast(m - mnew);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pv[e] = exp2f(x[e] - mnew);
+        pv[e] = exp2_fast(x[e] - mnew);
         psum += pv[e];
       }
     }
@@ -225,16 +226,268 @@ __global__ __launch_bounds__(256) void nonabsorbed_attn_kernel(
   }
 }
 
+// bf16 path.
+//
+// Work: a query tile is 128 queries of one head. Causal tiles grow linearly
+// with their index, so each workgroup runs the pair (tile p, tile nq-1-p) back
+// to back: every workgroup carries the same work, and with one workgroup per
+// compute unit none of them idles at the end.
+//
+// Workgroup: 8 waves. Wave w owns queries 32*(w%4) .. +31 of the tile (the 32
+// columns of 32x32x16 MFMAs) and key half w/4 of every 64-key step, so the two
+// waves of a query group split the keys and merge their (max, sum, output)
+// through LDS at the end of the tile.
+//
+// Keys stream through two LDS stages; the next step is loaded into registers
+// while the current one is consumed, then stored to the other stage: one
+// barrier per step.
+//
+// Per step and wave: S^T (32 keys x 32 queries) = K_row . Q^T in 12 MFMAs over
+// the 192-deep [K_nope | K_rope] row; lanes l and l+32 hold the 32 scores of one
+// query; P^T rounded to bf16 is the B operand of O^T += V^T . P^T (8 MFMAs, V^T
+// read with LDS transpose reads in the key order of the S^T accumulator layout).
+namespace {
+constexpr int NB_T = 32;                               // keys per wave per step
+constexpr int NB_KT = 2 * NB_T;                        // keys per step
+constexpr int NB_KROW = DQK * 2 + 16;                  // LDS K row: [K_nope(h) | K_rope] + pad
+constexpr int NB_VROW = DVN * 2 + 32;                  // LDS V row + pad (transpose reads conflict-free)
+constexpr int NB_KREG = NB_KT * NB_KROW;
+constexpr int NB_STAGE = NB_KREG + NB_KT * NB_VROW;
+constexpr int NB_NW = 8;
+constexpr int NB_RCH = (DQK + DVN) * 2 / 16;           // 16-byte chunks per key: 16 K_nope, 8 K_rope, 16 V
+constexpr int NB_PER = NB_KT * NB_RCH / (NB_NW * 64);  // chunks per thread per step
+constexpr int NB_QT = 128;
+constexpr int NB_XCH = 2 + 2 * 16;                     // merge record per lane: m, l, two output blocks
+static_assert(NB_KT * NB_RCH % (NB_NW * 64) == 0, "step chunks must divide the workgroup");
+static_assert(NB_NW * NB_XCH * 64 * 4 <= 2 * NB_STAGE, "merge area fits the stages");
+}  // namespace
+
+// Combine lanes l and l^32 (the two row halves of a 32x32 accumulator column).
+// Both lanes see the operands in the same order, so they agree bit for bit.
+__device__ __forceinline__ float half_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+__global__ __launch_bounds__(512) void nonabsorbed_bf16_kernel(
+    const uint16_t* __restrict__ qn, const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kn,
+    const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vv, uint16_t* __restrict__ out, int L, int N,
+    int H, int nq, int causal, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * NB_STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, g = lane >> 5;
+  const int qg = wave & 3, half = wave >> 2;
+  const int pair = blockIdx.x / H, h = blockIdx.x - pair * H, b = blockIdx.y;
+  const size_t kb0 = (size_t)b * N;
+  const float sl = scale_log2;
+
+  // Loads of one step (64 keys): loads 0-1 take K_nope (16 lanes per 256-byte
+  // row, keys tid/16 and 32 + tid/16), load 2 K_rope (8 lanes per 128-byte row,
+  // key tid/8), loads 3-4 V like K_nope. Keys past the context repeat the last
+  // key (their scores are masked).
+  static_assert(NB_PER == 5 && NB_KT == 64 && NB_NW * 64 == 512, "load map assumes 64 keys x 512 threads");
+  const int r16 = tid >> 4, c16b = (tid & 15) * 16, r8 = tid >> 3, c8b = (tid & 7) * 16;
+  const unsigned char* kn_b = (const unsigned char*)kn + (size_t)h * DN * 2 + c16b;
+  const unsigned char* kr_b = (const unsigned char*)kr + c8b;
+  const unsigned char* v_b = (const unsigned char*)vv + (size_t)h * DVN * 2 + c16b;
+  const size_t kstride = (size_t)H * DN * 2;
+  auto fetch = [&](u32x4 (&pf)[NB_PER], int t) {
+    const int kt = t * NB_KT;
+    const size_t ka = kb0 + min(kt + r16, N - 1), kb = kb0 + min(kt + 32 + r16, N - 1);
+    const size_t kc = kb0 + min(kt + r8, N - 1);
+    pf[0] = *(const u32x4*)(kn_b + ka * kstride);
+    pf[1] = *(const u32x4*)(kn_b + kb * kstride);
+    pf[2] = *(const u32x4*)(kr_b + kc * (DR * 2));
+    pf[3] = *(const u32x4*)(v_b + ka * kstride);
+    pf[4] = *(const u32x4*)(v_b + kb * kstride);
+  };
+  const int ldk0 = r16 * NB_KROW + c16b, ldk1 = (32 + r16) * NB_KROW + c16b;
+  const int ldr = r8 * NB_KROW + DN * 2 + c8b;
+  const int ldv0 = NB_KREG + r16 * NB_VROW + c16b, ldv1 = NB_KREG + (32 + r16) * NB_VROW + c16b;
+  auto stage_in = [&](const u32x4 (&pf)[NB_PER], int st) {
+    unsigned char* sb = smem + st * NB_STAGE;
+    *(u32x4*)(sb + ldk0) = pf[0];
+    *(u32x4*)(sb + ldk1) = pf[1];
+    *(u32x4*)(sb + ldr) = pf[2];
+    *(u32x4*)(sb + ldv0) = pf[3];
+    *(u32x4*)(sb + ldv1) = pf[4];
+  };
+
+  const int npass = (nq - 1 - pair == pair) ? 1 : 2;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int qt = pass == 0 ? pair : nq - 1 - pair;
+    const int i0 = qt * NB_QT, iw = i0 + 32 * qg, i = iw + col;
+    const bool qvalid = i < L;
+    const int p = causal ? N - L + i : N - 1;             // last visible key of this lane's query
+    const int count = causal ? N - L + min(L - 1, i0 + NB_QT - 1) + 1 : N;
+    const int wcount = iw >= L ? 0 : (causal ? N - L + min(L - 1, iw + 31) + 1 : N);
+    const int wsafe = causal ? N - L + iw : N;            // keys below this are visible to all queries of the wave
+    const int ntiles = (count + NB_KT - 1) / NB_KT;
+
+    // Query fragments (B operand): column = query, k = dims 16kk + 8g + e of [Q_nope | Q_rope].
+    bf16x8 qb[DQK / 16];
+    {
+      const size_t qrow = ((size_t)b * L + (qvalid ? i : 0)) * H + h;
+#pragma unroll
+      for (int kk = 0; kk < DQK / 16; ++kk)
+        qb[kk] = kk < DN / 16 ? *(const bf16x8*)(qn + qrow * DN + 16 * kk + 8 * g)
+                              : *(const bf16x8*)(qr + qrow * DR + 16 * (kk - DN / 16) + 8 * g);
+#pragma unroll
+      for (int kk = 0; kk < DQK / 16; ++kk) asm volatile("" ::"v"(qb[kk]));
+    }
+    f32x16 o[DVN / 32];
+#pragma unroll
+    for (int db = 0; db < DVN / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
+    float m = -INFINITY, lsum = 0.f;
+
+    // Steps alternate between LDS stages 0 and 1; the next step's rows are
+    // loaded into registers while this one is consumed.
+    auto step = [&](int t, int st) {
+      const int k0 = t * NB_KT + NB_T * half;
+      if (k0 >= wcount) return;
+      const unsigned char* ks = smem + st * NB_STAGE + NB_T * half * NB_KROW;
+      const unsigned char* vs = smem + st * NB_STAGE + NB_KREG + NB_T * half * NB_VROW;
+      f32x16 sacc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+      const unsigned char* kp = ks + col * NB_KROW + 16 * g;
+      // K fragments rotate through four registers so that four LDS reads are in
+      // flight ahead of the MFMA chain
+      bf16x8 kf[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kf[kk] = *(const bf16x8*)(kp + 32 * kk);
+#pragma unroll
+      for (int kk = 0; kk < DQK / 16; ++kk) {
+        sacc = mfma32x32x16(kf[kk & 3], qb[kk], sacc);
+        if (kk + 4 < DQK / 16) kf[kk & 3] = *(const bf16x8*)(kp + 32 * (kk + 4));
+      }
+      // schedule: 4 LDS reads, then (MFMA, LDS read) x 8, then the last 4 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int kk = 0; kk < DQK / 16 - 4; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      // this lane holds keys k0 + 8*(j/4) + 4g + j%4 of query i
+      if (k0 + NB_T - 1 >= wsafe) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (k0 + 8 * (j >> 2) + 4 * g + (j & 3) > p) sacc[j] = -INFINITY;
+      }
+      float tmax = sacc[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, sacc[j]);
+      tmax = half_max(tmax);
+      const float mnew = fmaxf(m, tmax);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2_fast((m - mref) * sl);
+      const float nb = -mref * sl;
+      float pv[16], psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        pv[j] = exp2_fast(fmaf(sacc[j], sl, nb));
+        psum += pv[j];
+      }
+      psum = half_sum(psum);
+      lsum = lsum * alpha + psum;
+      m = mnew;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < DVN / 32; ++db) o[db] *= alpha;
+      }
+      bf16x8 pk[2];
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        typedef float f32x8 __attribute__((ext_vector_type(8)));
+        f32x8 v8 = {pv[8 * ks2], pv[8 * ks2 + 1], pv[8 * ks2 + 2], pv[8 * ks2 + 3],
+                    pv[8 * ks2 + 4], pv[8 * ks2 + 5], pv[8 * ks2 + 6], pv[8 * ks2 + 7]};
+        pk[ks2] = __builtin_convertvector(v8, bf16x8);
+      }
+      // V^T fragment: lane points at key 16ks + 4g + (lane%16)/4 (+8 for the upper
+      // four k entries), dims 32db + 16*((lane/16)%2) + 4*(lane%4).
+      const unsigned char* vb = vs + (4 * g + ((lane & 15) >> 2)) * NB_VROW + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int db = 0; db < DVN / 32; ++db) {
+          const short4v lo = lds_read_tr16(vb + 16 * ks2 * NB_VROW + 64 * db);
+          const short4v hi = lds_read_tr16(vb + (16 * ks2 + 8) * NB_VROW + 64 * db);
+          o[db] = mfma32x32x16(join_bf16x8(lo, hi), pk[ks2], o[db]);
+        }
+    };
+
+    u32x4 pf[NB_PER];
+    fetch(pf, 0);
+    stage_in(pf, 0);
+    lds_barrier();
+    for (int t = 0; t < ntiles; ++t) {
+      fetch(pf, min(t + 1, ntiles - 1));
+      step(t, t & 1);
+      stage_in(pf, (t + 1) & 1);
+      lds_barrier();
+    }
+
+    // Merge the two key halves: each wave hands over the output blocks it does
+    // not write (half 0 writes dims 0-63, half 1 dims 64-127) with its m and l.
+    float* xw = (float*)smem + wave * NB_XCH * 64 + lane;
+    xw[0] = m;
+    xw[64] = lsum;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      xw[(2 + j) * 64] = o[half == 0 ? 2 : 0][j];
+      xw[(18 + j) * 64] = o[half == 0 ? 3 : 1][j];
+    }
+    lds_barrier();
+    const float* xp = (const float*)smem + (wave ^ 4) * NB_XCH * 64 + lane;
+    const float m2 = xp[0], l2 = xp[64];
+    const float mx = fmaxf(m, m2);
+    const float a1 = mx == -INFINITY ? 0.f : exp2_fast((m - mx) * sl);
+    const float a2 = mx == -INFINITY ? 0.f : exp2_fast((m2 - mx) * sl);
+    const float lt = lsum * a1 + l2 * a2;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (qvalid) {
+      uint16_t* op = out + (((size_t)b * L + i) * H + h) * DVN + 4 * g;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int db = 2 * half + e;
+        const f32x16 mine = half == 0 ? o[e] : o[2 + e];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          f32x4 v4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v4[q] = (mine[4 * jj + q] * a1 + xp[(2 + 16 * e + 4 * jj + q) * 64] * a2) * inv;
+          *(bf16x4*)(op + 32 * db + 8 * jj) = __builtin_convertvector(v4, bf16x4);
+        }
+      }
+    }
+    lds_barrier();
+  }
+}
+
 hipError_t launch_nonabsorbed_attn(bool bf16, const void* qn, const void* qr, const void* kn, const void* kr,
                                    const void* v, void* out, int B, int L, int N, int H, int causal, float scale,
                                    hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
+  if (bf16) {
+    const int nq = (L + NB_QT - 1) / NB_QT;
+    dim3 grid((nq + 1) / 2 * H, B), block(512);
+    KernelTrace kt("nonabsorbed_attn_bf16", stream);
+    hipLaunchKernelGGL(nonabsorbed_bf16_kernel, grid, block, 0, stream, (const uint16_t*)qn, (const uint16_t*)qr,
+                       (const uint16_t*)kn, (const uint16_t*)kr, (const uint16_t*)v, (uint16_t*)out, L, N, H, nq,
+                       causal, scale_log2);
+    return hipGetLastError();
+  }
   dim3 grid((L + 63) / 64, H, B), block(256);
-  KernelTrace kt(bf16 ? "nonabsorbed_attn_bf16" : "nonabsorbed_attn_f32", stream);
-  if (bf16)
-    hipLaunchKernelGGL((nonabsorbed_attn_kernel<true>), grid, block, 0, stream, qn, qr, kn, kr, v, out, L, N, H, causal, scale_log2);
-  else
-    hipLaunchKernelGGL((nonabsorbed_attn_kernel<false>), grid, block, 0, stream, qn, qr, kn, kr, v, out, L, N, H, causal, scale_log2);
+  KernelTrace kt("nonabsorbed_attn_f32", stream);
+  hipLaunchKernelGGL((nonabsorbed_attn_kernel<false>), grid, block, 0, stream, qn, qr, kn, kr, v, out, L, N, H, causal, scale_log2);
   return hipGetLastError();
 }
 

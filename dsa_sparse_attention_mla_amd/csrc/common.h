@@ -70,6 +70,11 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// 2^x with the hardware instruction alone (about 1 ulp; results below 2^-126
+// flush to zero, which softmax weights never need). exp2f adds a range check and
+// rescale for denormal results that costs several instructions per call.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Butterfly over lane groups: combine lanes l, l^16, l^32 (the four 16-lane
 // groups that hold the same MFMA column).
 __device__ __forceinline__ float group4_max(float x) {

@@ -75,6 +75,43 @@ def test_nonabsorbed_bf16_small(L, N):
     assert_close(got, ref, TOL_BF16, f"nonabs bf16 L={L} N={N}")
 
 
+@pytest.mark.parametrize("L,N,H", [(1, 1, 16), (37, 200, 4), (129, 129, 3), (256, 1000, 16)])
+def test_nonabsorbed_bf16_shapes(L, N, H):
+    """Ragged query tiles (not multiples of 128 or 32), odd head counts, L < N, a single key."""
+    t, f = _nonabs(40 + L + H, L, N, H, "bf16", scale=0.5)
+    got = _run_nonabs(t)
+    ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], 1 / math.sqrt(192))
+    assert_close(got, ref, TOL_BF16, f"nonabs bf16 L={L} N={N} H={H}")
+
+
+def test_nonabsorbed_bf16_sharpened_and_first_row():
+    """Scale x8 (peaked softmax: a causal off-by-one moves the output far past the tolerance);
+    the first query sees only key 0, so its output is V[0] exactly."""
+    L = N = 300
+    t, f = _nonabs(48, L, N, 16, "bf16", scale=0.5)
+    scale = 8 / math.sqrt(192)
+    got = _run_nonabs(t, scale=scale)
+    ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], scale)
+    assert_close(got, ref, TOL_BF16, "nonabs bf16 sharpened")
+    assert np.array_equal(got[0], f["v"][0])
+
+
+def test_nonabsorbed_bf16_noncausal_batch():
+    """Non-causal, B = 2: each entry matches the oracle and its own single-sequence call."""
+    L, N, H = 70, 333, 16
+    gs = [gen_nonabsorbed(60 + e, L, N, H=H, dtype="bf16", scale=0.5) for e in range(2)]
+    t = {k: torch.stack([dev(g[k]) for g in gs]) for k in gs[0]}
+    out = dm.mla_prefill_dense(t["qn"], t["kn"], q_rope=t["qr"], k_rope=t["kr"], v=t["v"], causal=False)
+    one = dm.mla_prefill_dense(t["qn"][1:].contiguous(), t["kn"][1:].contiguous(), q_rope=t["qr"][1:].contiguous(),
+                               k_rope=t["kr"][1:].contiguous(), v=t["v"][1:].contiguous(), causal=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out[1], one[0])
+    for e, g in enumerate(gs):
+        f = {k: to_f64(v) for k, v in g.items()}
+        ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], 1 / math.sqrt(192), causal=False)
+        assert_close(host_f64(out[e]), ref, TOL_BF16, f"nonabs bf16 non-causal batch {e}")
+
+
 def test_nonabsorbed_bf16_full_size_sampled():
     """L = N = 4096, 16 heads, bf16 (0.5 N(0,1)): sampled query rows against the oracle."""
     L = N = 4096
