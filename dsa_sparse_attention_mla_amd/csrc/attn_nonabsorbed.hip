@@ -250,13 +250,14 @@ namespace {
 constexpr int NB_T = 32;                               // keys per wave per step
 constexpr int NB_KT = 2 * NB_T;                        // keys per step
 constexpr int NB_KROW = DQK * 2 + 16;                  // LDS K row: [K_nope(h) | K_rope] + pad
-constexpr int NB_VROW = DVN * 2 + 32;                  // LDS V row + pad (transpose reads conflict-free)
+constexpr int NB_VROW = DVN * 2 + 64;                  // LDS V row + pad: rows 16 banks apart, transpose reads conflict-free
 constexpr int NB_KREG = NB_KT * NB_KROW;
 constexpr int NB_STAGE = NB_KREG + NB_KT * NB_VROW;
 constexpr int NB_NW = 8;
 constexpr int NB_RCH = (DQK + DVN) * 2 / 16;           // 16-byte chunks per key: 16 K_nope, 8 K_rope, 16 V
 constexpr int NB_PER = NB_KT * NB_RCH / (NB_NW * 64);  // chunks per thread per step
 constexpr int NB_QT = 128;
+constexpr float NB_SLACK = 8.f;                        // log2 of the largest unnormalised weight
 constexpr int NB_XCH = 2 + 2 * 16;                     // merge record per lane: m, l, two output blocks
 static_assert(NB_KT * NB_RCH % (NB_NW * 64) == 0, "step chunks must divide the workgroup");
 static_assert(NB_NW * NB_XCH * 64 * 4 <= 2 * NB_STAGE, "merge area fits the stages");
@@ -385,9 +386,13 @@ __global__ __launch_bounds__(512) void nonabsorbed_bf16_kernel(
 #pragma unroll
       for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, sacc[j]);
       tmax = half_max(tmax);
-      const float mnew = fmaxf(m, tmax);
+      // The reference max m moves only when the new scores exceed it by more than
+      // 2^NB_SLACK (or on the first visible key): softmax does not depend on the
+      // reference, and weights up to 2^NB_SLACK are exact enough in bf16 / fp32.
+      // The output rescale then happens a few times per query instead of most steps.
+      const bool bump = (tmax - m) * sl > NB_SLACK;
+      const float mnew = bump ? tmax : m;
       const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2_fast((m - mref) * sl);
       const float nb = -mref * sl;
       float pv[16], psum = 0.f;
 #pragma unroll
@@ -396,12 +401,14 @@ __global__ __launch_bounds__(512) void nonabsorbed_bf16_kernel(
         psum += pv[j];
       }
       psum = half_sum(psum);
-      lsum = lsum * alpha + psum;
-      m = mnew;
-      if (__ballot(alpha != 1.f)) {
+      if (__ballot(bump)) {
+        const float alpha = bump ? exp2_fast((m - mref) * sl) : 1.f;
+        lsum *= alpha;
 #pragma unroll
         for (int db = 0; db < DVN / 32; ++db) o[db] *= alpha;
       }
+      lsum += psum;
+      m = mnew;
       bf16x8 pk[2];
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
