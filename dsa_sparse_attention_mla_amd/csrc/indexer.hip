@@ -37,6 +37,7 @@ constexpr int TK = 256;                 // keys per tile of the score kernel
 constexpr int IDX_STAGE = TK * ID * 2;  // the LDS key stage: 256 keys x 256 B (swizzled, unpadded)
 constexpr int QPB = 4;                  // queries per workgroup
 constexpr int IDX_NW = 8;               // waves per score workgroup: 2 per query
+constexpr int SAMPLE = 2048;            // keys scored up front to start the filter threshold
 constexpr int RANK_WORDS = 4096;        // bitmap words for ordering the output (131072 keys per window)
 static_assert(RANK_WORDS * 4 >= 64 * IH * 8, "band dots alias the word-prefix table");
 constexpr int RANK_CAP = 1024;          // band entries ranked in select_refine
@@ -187,81 +188,89 @@ __device__ __forceinline__ float block512_min(float x, float* red) {
   return r;
 }
 
-// Cooperative (all 512 threads) threshold update and in-place compaction of one
-// query's candidate list. The list is two segments of the query's region: lo
-// entries at [0, lo) and hi entries at [CAPS-hi, CAPS) (its two waves fill it from
-// opposite ends); entry e of the logical list is at seg_pos(e). tau = a lower
-// bound of the list's k-th largest score (smallest value of the linear-histogram
-// bin holding it); entries with score >= max(old threshold, tau - band(tau)) are
-// moved to [0, newc), in order. Returns newc.
+// Threshold update and in-place compaction of the candidate lists of the queries
+// flagged in `mine`, all queries at once. A query's list has two segments, owned by
+// its two waves: the front wave (kh = 0) keeps its entries at [0, n0), the back wave
+// (kh = 1) at [CAPS - n1, CAPS). Each wave scans only its own segment; partial
+// results (min / max, the shared 256-bin linear histogram, the minimum inside the
+// bin of the k-th largest) meet in LDS at three workgroup barriers that every wave
+// takes. tau = that minimum is a lower bound of the list's k-th largest score; each
+// wave then keeps its entries with score >= max(old threshold, tau - band(tau)),
+// compacting them toward its own end (a destination never passes the entry being
+// read, so the in-place moves are safe). Returns this wave's new segment count.
+// The caller guarantees that a flagged list holds at least k entries.
 template <typename Off, int CAPS>
-__device__ int block_compact(float* cs, Off* co, int lo, int hi, int k, float eps, float& thr, int* hist, int* misc,
-                             float* red) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cnt = lo + hi;
-  auto pos_of = [&](int e) { return e < lo ? e : CAPS - hi + (e - lo); };
-  float mx = -INFINITY, mn = INFINITY;
-  for (int e = tid; e < cnt; e += 64 * IDX_NW) {
-    const float v = cs[pos_of(e)];
-    mx = fmaxf(mx, v);
-    mn = fminf(mn, v);
-  }
-  mx = block512_max(mx, red);
-  mn = block512_min(mn, red);
-  float tau = mn;
-  if (mx > mn) {
-    const float inv_w = 256.0f / (mx - mn);
-    if (tid < 256) hist[tid] = 0;
-    lds_barrier();
-    for (int e = tid; e < cnt; e += 64 * IDX_NW) atomicAdd(&hist[lin_bucket(cs[pos_of(e)], mn, inv_w)], 1);
-    lds_barrier();
-    if (wave == 0) {
-      int bin, above;
-      wave_find_bin(hist, k, lane, bin, above);
-      if (lane == 0) misc[0] = bin;
+__device__ int pair_compact(float* cs, Off* co, int mycnt, int kh, bool mine, int k, float eps, float& thr,
+                            int* hq, float* red, bool compact = true) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, partner = wave ^ QPB;
+  auto seg = [&](int e) { return kh == 0 ? e : CAPS - 1 - e; };
+  if (mine) {
+    float mx = -INFINITY, mn = INFINITY;
+    for (int e = lane; e < mycnt; e += 64) {
+      const float v = cs[seg(e)];
+      mx = fmaxf(mx, v);
+      mn = fminf(mn, v);
     }
-    lds_barrier();
-    const int bin = misc[0];
+    mx = wave_max(mx);
+    mn = wave_min(mn);
+    if (lane == 0) {
+      red[2 * wave] = mx;
+      red[2 * wave + 1] = mn;
+    }
+    if (kh == 0)
+      for (int b = lane; b < 256; b += 64) hq[b] = 0;
+  }
+  lds_barrier();
+  float qmx = -INFINITY, qmn = INFINITY;
+  if (mine) {
+    qmx = fmaxf(red[2 * wave], red[2 * partner]);
+    qmn = fminf(red[2 * wave + 1], red[2 * partner + 1]);
+  }
+  const bool spread = qmx > qmn;
+  const float inv_w = spread ? 256.0f / (qmx - qmn) : 0.f;
+  if (mine && spread)
+    for (int e = lane; e < mycnt; e += 64) atomicAdd(&hq[lin_bucket(cs[seg(e)], qmn, inv_w)], 1);
+  lds_barrier();
+  if (mine && spread) {
+    int bin, above;
+    wave_find_bin(hq, k, lane, bin, above);   // both waves of the query find the same bin
     float tb = INFINITY;
-    for (int e = tid; e < cnt; e += 64 * IDX_NW) {
-      const float v = cs[pos_of(e)];
-      if (lin_bucket(v, mn, inv_w) == bin) tb = fminf(tb, v);
+    for (int e = lane; e < mycnt; e += 64) {
+      const float v = cs[seg(e)];
+      if (lin_bucket(v, qmn, inv_w) == bin) tb = fminf(tb, v);
     }
-    tau = block512_min(tb, red);
+    tb = wave_min(tb);
+    if (lane == 0) red[2 * wave] = tb;
   }
+  lds_barrier();
+  if (!mine) return mycnt;
+  const float tau = spread ? fminf(red[2 * wave], red[2 * partner]) : qmn;
   thr = fmaxf(thr, tau - band_halfwidth(eps, tau));
-  // A survivor's destination never exceeds the position of the entry being read
-  // (the hi segment starts at or after lo), so chunk-by-chunk in-place moves are safe.
-  int newc = 0;
-  for (int c0 = 0; c0 < cnt; c0 += 64 * IDX_NW) {
-    const int e = c0 + tid;
-    const bool in = e < cnt;
-    const int ps = in ? pos_of(e) : 0;
-    const float v = in ? cs[ps] : 0.f;
-    const Off id = in ? co[ps] : (Off)0;
+  if (!compact) return mycnt;
+  int outc = 0;
+  for (int c0 = 0; c0 < mycnt; c0 += 64) {
+    const int e = c0 + lane;
+    const bool in = e < mycnt;
+    const int ps = seg(in ? e : c0);
+    const float v = cs[ps];
+    const Off id = co[ps];
     const bool keep = in && v >= thr;
     const unsigned long long bm = __ballot(keep);
-    if (lane == 0) misc[8 + wave] = __popcll(bm);
-    lds_barrier();                        // every entry of this chunk has been read
-    int off = newc;
-    for (int x = 0; x < wave; ++x) off += misc[8 + x];
     if (keep) {
-      const int pos = off + __popcll(bm & ((1ull << lane) - 1ull));
-      cs[pos] = v;
-      co[pos] = id;
+      const int dst = seg(outc + __popcll(bm & ((1ull << lane) - 1ull)));
+      cs[dst] = v;
+      co[dst] = id;
     }
-#pragma unroll
-    for (int x = 0; x < IDX_NW; ++x) newc += misc[8 + x];
-    lds_barrier();
+    outc += __popcll(bm);
   }
-  return newc;
+  return outc;
 }
 
 // Largest candidate capacity per query that fits the LDS next to the key stage.
 template <typename Off>
 struct FilterCap {
   static constexpr int value =
-      (int)(((163840 - IDX_STAGE - 256 * 4 - 8 * QPB * 4 - 16 * 4 - IDX_NW * 4) / (QPB * (4 + sizeof(Off)))) / 64 * 64);
+      (int)(((163840 - IDX_STAGE - QPB * 256 * 4 - 8 * QPB * 4 - 2 * IDX_NW * 4) / (QPB * (4 + sizeof(Off)))) / 64 * 64);
 };
 
 // Key tiles (256 keys x 256 B) are fetched into registers one tile ahead of use
@@ -280,7 +289,7 @@ template <typename Off>
 __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int span, int nsplit, int cap,
-    float* __restrict__ cand_s, int* __restrict__ cand_i, int* __restrict__ cand_n) {
+    float* __restrict__ cand_s, int* __restrict__ cand_i, int* __restrict__ cand_n, float* __restrict__ cand_t) {
   constexpr int CAPS = FilterCap<Off>::value;
   constexpr int PER_WAVE = TK / 2;      // keys per wave per tile (128)
   constexpr int MARGIN = 2 * PER_WAVE + 64;   // room for one tile's appends plus slack
@@ -288,14 +297,13 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char stage[IDX_STAGE];
   __shared__ float cs_all[QPB * CAPS];
   __shared__ Off co_all[QPB * CAPS];
-  __shared__ int hist[256];
+  __shared__ int hist[QPB * 256];
   __shared__ __attribute__((aligned(16))) int qlo[QPB];   // entries at the low end, written by wave h=0
   __shared__ __attribute__((aligned(16))) int qhi[QPB];   // entries at the high end, written by wave h=1
   __shared__ __attribute__((aligned(16))) int qovf[QPB];
   __shared__ float qthr[QPB];
   __shared__ float qeps[QPB];
-  __shared__ int misc[16];
-  __shared__ float red[IDX_NW];
+  __shared__ float red[2 * IDX_NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qi = wave & (QPB - 1), kh = wave / QPB;
@@ -384,6 +392,46 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   };
 
+  // Sampling prologue. SAMPLE keys spread evenly over the keys that every query of
+  // the group sees are scored first; each query's threshold starts just below the
+  // r-th largest sample score, r six standard deviations above the expected number
+  // of sample keys in the top-k. That start is an estimate, not a bound: the refine
+  // step checks that every list covers the band around the final k-th score and
+  // sends the query to the exact fallback otherwise. With few visible keys the
+  // threshold starts at -inf, a bound by construction.
+  {
+    const int nv_min = min(N, N - L + (int)blockIdx.x * QPB + 1);
+    const float mean = (float)topk * SAMPLE / (float)max(nv_min, 1);
+    if (nv_min >= 8 * SAMPLE && mean <= SAMPLE / 8 && SAMPLE <= cap) {
+      const int rk = min(SAMPLE / 2, (int)ceilf(mean + 6.f * sqrtf(mean) + 8.f));
+      for (int t = 0; t < SAMPLE / TK; ++t) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+          const int slot = tid + 512 * u;
+          const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
+          const int n = (int)((long long)(t * TK + r) * nv_min / SAMPLE);
+          pf[u] = *(const u32x4*)(k + (size_t)n * ID + c * 8);
+        }
+        lds_barrier();                  // previous sample tile fully read
+        stage_in();
+        lds_barrier();
+        const int r0 = PER_WAVE * kh;
+        const float sv0 = score_pair(r0), sv1 = score_pair(r0 + 64);
+        if (active) {                   // every score goes to the list; key ids are not needed
+          cs[kh == 0 ? mycnt + lane : CAPS - 1 - (mycnt + lane)] = sv0;
+          cs[kh == 0 ? mycnt + 64 + lane : CAPS - 65 - (mycnt + lane)] = sv1;
+          mycnt += 128;
+        }
+      }
+      lds_barrier();
+      float thr_q = -INFINITY;
+      pair_compact<Off, CAPS>(cs, co, mycnt, kh, active, rk, qeps[qi], thr_q, hist + qi * 256, red, false);
+      mycnt = 0;
+      if (active && kh == 0 && lane == 0) qthr[qi] = thr_q;
+      lds_barrier();
+    }
+  }
+
   const int ntiles = n_hi > n_lo ? (n_hi - n_lo + TK - 1) / TK : 0;
   if (ntiles > 0) {
     fetch(0);
@@ -401,27 +449,30 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
     const int4 vlo = *(const int4*)qlo, vhi = *(const int4*)qhi, vov = *(const int4*)qovf;
     const int need = ((vlo.x + vhi.x > cap - MARGIN) && !vov.x) | (((vlo.y + vhi.y > cap - MARGIN) && !vov.y) << 1) |
                      (((vlo.z + vhi.z > cap - MARGIN) && !vov.z) << 2) | (((vlo.w + vhi.w > cap - MARGIN) && !vov.w) << 3);
+    bool ovf_now = false;
     if (need) {
-      lds_barrier();
-#pragma unroll 1
-      for (int x = 0; x < QPB; ++x) {
-        if (!((need >> x) & 1)) continue;
-        float thr = qthr[x];
-        const int newc = block_compact<Off, CAPS>(cs_all + x * CAPS, co_all + x * CAPS, qlo[x], qhi[x], topk,
-                                                  qeps[x], thr, hist, misc, red);
-        lds_barrier();                  // every wave has read the old counts
-        if (tid == 0) {
-          qlo[x] = newc;
-          qhi[x] = 0;
-          qthr[x] = thr;
-          qovf[x] = newc > cap - MARGIN;
+      const bool mine = (need >> qi) & 1;
+      float thr_q = qthr[qi];
+      const int newc = pair_compact<Off, CAPS>(cs, co, mycnt, kh, mine, topk, qeps[qi], thr_q, hist + qi * 256, red);
+      if (mine) {
+        mycnt = newc;
+        if (lane == 0) {
+          if (kh == 0) {
+            qlo[qi] = newc;
+            qthr[qi] = thr_q;
+          } else {
+            qhi[qi] = newc;
+          }
         }
-        lds_barrier();
       }
-      mycnt = kh == 0 ? qlo[qi] : qhi[qi];
+      lds_barrier();
+      if (mine) {
+        ovf_now = qlo[qi] + qhi[qi] > cap - MARGIN;
+        if (kh == 0 && lane == 0) qovf[qi] = ovf_now;
+      }
     }
     const float thr = qthr[qi];
-    const bool ovf = qovf[qi] != 0;
+    const bool ovf = ovf_now || qovf[qi] != 0;
 
     const int r0 = PER_WAVE * kh;
     const float sv0 = score_pair(r0);
@@ -463,7 +514,10 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
       cand_s[slot * cap + e] = cs[ps];
       cand_i[slot * cap + e] = n_lo + (int)co[ps];
     }
-    if (kh == 0 && lane == 0) cand_n[slot] = qovf[qi] ? -1 : cnt;
+    if (kh == 0 && lane == 0) {
+      cand_n[slot] = qovf[qi] ? -1 : cnt;
+      cand_t[slot] = qthr[qi];
+    }
   }
 }
 
@@ -578,7 +632,8 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int nsplit, int cap,
     const float* __restrict__ cand_s, const int* __restrict__ cand_i, const int* __restrict__ cand_n,
-    int* __restrict__ fb_flag, int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+    const float* __restrict__ cand_t, int* __restrict__ fb_flag, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   const int M_cap = nsplit * cap;
   float* vs = (float*)dyn;                              // [M_cap] candidate scores
@@ -645,8 +700,18 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
   __syncthreads();
 
   const float eps = eps_in[i];
+  // Each split's list holds every key scoring at least that split's final filter
+  // threshold; the selection below is exact only if every threshold lies at or
+  // below the band around the k-th score (always true for thresholds derived from
+  // the lists themselves, to be checked for the sampled start).
+  float thr_max = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) thr_max = fmaxf(thr_max, cand_t[(size_t)i * nsplit + sp]);
   if (nv <= topk) {
-    // every visible key is in the list (the filter threshold never rose)
+    // every visible key must be in the lists: only an untouched threshold guarantees it
+    if (thr_max > -INFINITY) {
+      if (tid == 0) fb_flag[i] = 1;
+      return;
+    }
     for (int e = tid; e < M; e += 256) cls[e] = 1;
   } else {
     float tk;
@@ -656,6 +721,10 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     }
     const float hw = band_halfwidth(eps, tk);
     const float hi = tk + hw, lo = tk - hw;
+    if (thr_max > lo) {
+      if (tid == 0) fb_flag[i] = 1;
+      return;
+    }
     if (tid == 0) { misc[2] = 0; misc[3] = 0; }
     __syncthreads();
     for (int e0 = 0; e0 < M; e0 += 256) {
@@ -913,6 +982,7 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   pl.off_partial = take(sizeof(float) * NORM_BLOCKS);
   pl.off_eps = take(sizeof(float) * (size_t)L);
   pl.off_cand_n = take(sizeof(int) * (size_t)L * ns);
+  pl.off_cand_t = take(sizeof(float) * (size_t)L * ns);
   pl.off_fb = take(sizeof(int) * (size_t)L);
   pl.off_cand_s = take(sizeof(float) * (size_t)L * ns * pl.cap);
   pl.off_cand_i = take(sizeof(int) * (size_t)L * ns * pl.cap);
@@ -930,6 +1000,7 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
   float* partial = (float*)(base + pl.off_partial);
   float* eps = (float*)(base + pl.off_eps);
   int* cand_n = (int*)(base + pl.off_cand_n);
+  float* cand_t = (float*)(base + pl.off_cand_t);
   int* fb = (int*)(base + pl.off_fb);
   float* cand_s = (float*)(base + pl.off_cand_s);
   int* cand_i = (int*)(base + pl.off_cand_i);
@@ -955,15 +1026,15 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
     const dim3 grid((L + QPB - 1) / QPB, pl.nsplit), block(64 * IDX_NW);
     if (pl.small_off)
       hipLaunchKernelGGL((score_filter_kernel<uint16_t>), grid, block, 0, stream, q, k, w, eps, L, N,
-                         topk, pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n);
+                         topk, pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n, cand_t);
     else
       hipLaunchKernelGGL((score_filter_kernel<int>), grid, block, 0, stream, q, k, w, eps, L, N, topk,
-                         pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n);
+                         pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n, cand_t);
   }
   {
     KernelTrace kt("indexer_select_refine", stream);
     hipLaunchKernelGGL(select_refine_kernel, dim3(L), dim3(256), pl.select_lds, stream, q, k, w, eps, L, N, topk,
-                       pl.nsplit, pl.cap, cand_s, cand_i, cand_n, fb, idx_out, score_out);
+                       pl.nsplit, pl.cap, cand_s, cand_i, cand_n, cand_t, fb, idx_out, score_out);
   }
   {
     KernelTrace kt("indexer_exact_fallback", stream);

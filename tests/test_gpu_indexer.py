@@ -59,6 +59,38 @@ def test_indexer_zero_query_all_ties():
     _check_rows(idx, ref, np.arange(6), "zero query")
 
 
+def test_indexer_sampled_start_moderate_context():
+    """Contexts of at least 16384 visible keys start the filter threshold from a scored
+    sample of 2048 keys: every row must still equal the oracle."""
+    g = gen_indexer(98, 8, 40000)
+    idx, sc, ref, s = _run(g, 512)
+    _check_rows(idx, ref, np.arange(8), "sampled start L=8 N=40000 k=512")
+    # the filter path returns fp32 MFMA estimates, a good share of which differ from
+    # the fp32-rounded canonical scores (the exact fallback returns those exactly)
+    canon = np.take_along_axis(s, idx.astype(np.int64), axis=1).astype(np.float32)
+    assert np.mean(sc != canon) > 0.05
+
+
+def test_indexer_sampled_start_adversarial():
+    """Keys at the sampled positions are scaled by 4, so the sampled start lands far
+    above the true k-th score and the lists miss most of the top-k: the refine step
+    must detect it and the exact fallback must still return the oracle's sets."""
+    L, N, topk, sample = 4, 20000, 2048, 2048
+    g = gen_indexer(99, L, N)
+    nv_min = N - L + 1                       # keys visible to every query of the group
+    pos = (np.arange(sample, dtype=np.int64) * nv_min) // sample
+    kb = g["k_idx"].data
+    rows = kb[pos]
+    nz = (rows & 0x7F80) != 0
+    rows[nz] += 0x0100                        # bf16 exponent + 2: exact multiplication by 4
+    kb[pos] = rows
+    idx, sc, ref, s = _run(g, topk)
+    _check_rows(idx, ref, np.arange(L), "sampled start adversarial")
+    # every row went through the exact fallback: its scores are the canonical ones in fp32
+    canon = np.take_along_axis(s, idx.astype(np.int64), axis=1).astype(np.float32)
+    assert np.array_equal(sc, canon)
+
+
 def test_indexer_full_size_small_config():
     """L = 512, N = 65536, top-k 2048 (blocks of 4096): every row against the oracle."""
     g = gen_indexer(1003, 512, 65536)
