@@ -521,6 +521,183 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
   }
 }
 
+// ---------------------------------------------------------------- 3b. score + filter, global lists
+// Variant of the score kernel for contexts long enough for the sampled start
+// (every query of the launch sees at least 8 * SAMPLE keys). The threshold is
+// fixed after the sampling prologue, so survivors go straight to the query's list
+// in global memory (one LDS atomic per wave and query for the positions) and no
+// list is kept on chip. That frees the LDS for two 32 KB key stages filled by
+// direct global-to-LDS loads one 128-key tile ahead, and with at most 128 VGPRs two
+// workgroups share a compute unit (four waves per SIMD). A list that would exceed
+// its capacity marks the query for the exact fallback.
+namespace {
+constexpr int GT = 128;                                  // keys per tile
+constexpr int G_STAGE = GT * ID * 2;                     // 32 KB
+constexpr int G_DMA = G_STAGE / (IDX_NW * 64 * 16);      // 16-byte direct loads per lane per tile
+static_assert(G_DMA * IDX_NW * 64 * 16 == G_STAGE, "tile loads cover the stage");
+static_assert(SAMPLE * QPB * 4 <= G_STAGE, "sample scores fit one stage");
+}  // namespace
+
+// 16-byte direct global->LDS load: lane l writes LDS bytes [m0 + 16 l, m0 + 16 l + 16).
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
+}
+
+__global__ __launch_bounds__(64 * IDX_NW, 2) void score_list_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
+    const float* __restrict__ eps_in, int L, int N, int topk, int span, int nsplit, int cap,
+    float* __restrict__ cand_s, int* __restrict__ cand_i, int* __restrict__ cand_n, float* __restrict__ cand_t) {
+  __shared__ __attribute__((aligned(1024))) unsigned char stage[2][G_STAGE];
+  __shared__ int hist[QPB * 256];
+  __shared__ int qcnt[QPB];
+  __shared__ int qovf[QPB];
+  __shared__ float red[2 * IDX_NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qi = wave & (QPB - 1), kh = wave / QPB;
+  const int split = blockIdx.y;
+  const int n_lo = split * span;
+  const int i = blockIdx.x * QPB + qi;
+  const bool active = i < L;
+  const int ii = active ? i : L - 1;
+  const int p = N - L + ii;
+  const int ilast = min(L - 1, (int)blockIdx.x * QPB + QPB - 1);
+  const int n_hi = min(min(N, n_lo + span), N - L + ilast + 1);
+  const uint32_t lds_stage = (uint32_t)(uintptr_t)(DSA_LDS void*)&stage[0][0];
+
+  bf16x8 qa[ID / 16];
+  {
+    const uint16_t* qrow = q + ((size_t)ii * IH + (lane & 31)) * ID + 8 * (lane >> 5);
+#pragma unroll
+    for (int kc = 0; kc < ID / 16; ++kc) qa[kc] = *(const bf16x8*)(qrow + 16 * kc);
+  }
+  float wr[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) wr[j] = w[(size_t)ii * IH + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3)];
+#pragma unroll
+  for (int kc = 0; kc < ID / 16; ++kc) asm volatile("" ::"v"(qa[kc]));
+#pragma unroll
+  for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(wr[j]));
+  if (tid < QPB) {
+    qcnt[tid] = 0;
+    qovf[tid] = 0;
+  }
+
+  // Tile loads: wave w's load u covers LDS chunk slots (w*G_DMA + u)*64 + lane, i.e.
+  // key r = slot / 16 of the tile and stored chunk c' = slot % 16, which holds global
+  // chunk c' ^ (r % 16) of that key (the swizzle that keeps MFMA operand reads
+  // conflict-free). key_of maps a tile row to a key index.
+  auto dma_tile = [&](auto key_of, int st) {
+#pragma unroll
+    for (int u = 0; u < G_DMA; ++u) {
+      const int slot = (wave * G_DMA + u) * 64 + lane;
+      const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
+      dma16(k + (size_t)key_of(r) * ID + c * 8,
+            __builtin_amdgcn_readfirstlane(lds_stage + st * G_STAGE + (wave * G_DMA + u) * 1024));
+    }
+  };
+
+  // Scores of keys r0 + lane (this query) from stage st: two 32-key chains
+  // (lanes < 32 get keys r0 .. r0+31, lanes >= 32 keys r0+32 .. r0+63), with the
+  // key fragments read two k-steps ahead of the MFMAs.
+  auto score64 = [&](int st, int r0) -> float {
+    const unsigned char* sb = stage[st];
+    const int ra = r0 + (lane & 31), rb = ra + 32;
+    auto frag = [&](int r, int kc) {
+      const int c = 2 * kc + (lane >> 5);
+      return *(const bf16x8*)(sb + r * 256 + ((c ^ (r & 15)) * 16));
+    };
+    f32x16 acca = {}, accb = {};
+    bf16x8 fa0 = frag(ra, 0), fb0 = frag(rb, 0), fa1 = frag(ra, 1), fb1 = frag(rb, 1);
+#pragma unroll
+    for (int kc = 0; kc < ID / 16; ++kc) {
+      const bf16x8 xa = (kc & 1) ? fa1 : fa0, xb = (kc & 1) ? fb1 : fb0;
+      if (kc + 2 < ID / 16) {
+        if (kc & 1) { fa1 = frag(ra, kc + 2); fb1 = frag(rb, kc + 2); }
+        else { fa0 = frag(ra, kc + 2); fb0 = frag(rb, kc + 2); }
+      }
+      acca = mfma32x32x16(qa[kc], xa, acca);
+      accb = mfma32x32x16(qa[kc], xb, accb);
+    }
+    float pa = 0.f, pb = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      pa = fmaf(wr[j], __int_as_float(max(__float_as_int(acca[j]), 0)), pa);
+      pb = fmaf(wr[j], __int_as_float(max(__float_as_int(accb[j]), 0)), pb);
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  };
+
+  // Sampling prologue: SAMPLE keys spread evenly over the keys every query of the
+  // group sees; the start threshold sits just below the rk-th largest sample score
+  // (see score_filter_kernel). Sample scores go to stage 1 as two segments per
+  // query (front wave from the start, back wave from the end), the layout the
+  // threshold search shares with the list compaction.
+  float thr = -INFINITY;
+  {
+    const int nv_min = min(N, N - L + (int)blockIdx.x * QPB + 1);
+    const float mean = (float)topk * SAMPLE / (float)max(nv_min, 1);
+    if (nv_min >= 8 * SAMPLE && mean <= SAMPLE / 8) {
+      const int rk = min(SAMPLE / 2, (int)ceilf(mean + 6.f * sqrtf(mean) + 8.f));
+      float* ss = (float*)stage[1] + qi * SAMPLE;
+      for (int t = 0; t < SAMPLE / GT; ++t) {
+        dma_tile([&](int r) { return (int)((long long)(t * GT + r) * nv_min / SAMPLE); }, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        const float sv = score64(0, 64 * kh);
+        const int e = t * 64 + lane;
+        if (active) ss[kh == 0 ? e : SAMPLE - 1 - e] = sv;
+        lds_barrier();                  // stage 0 fully read before the next tile lands
+      }
+      float thr_q = -INFINITY;
+      pair_compact<float, SAMPLE>(ss, (float*)nullptr, SAMPLE / 2, kh, active, rk, eps_in[ii], thr_q,
+                                  hist + qi * 256, red, false);
+      thr = thr_q;
+      lds_barrier();                    // sample scores fully read before stage 1 is reused
+    }
+  }
+
+  const size_t slot = (size_t)ii * nsplit + split;
+  float* ls = cand_s + slot * cap;
+  int* li = cand_i + slot * cap;
+  const int ntiles = n_hi > n_lo ? (n_hi - n_lo + GT - 1) / GT : 0;
+  auto main_key = [&](int t) { return [=](int r) { return min(n_lo + t * GT + r, n_hi - 1); }; };
+  if (ntiles > 0) {
+    dma_tile(main_key(0), 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  lds_barrier();
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    dma_tile(main_key(min(t + 1, ntiles - 1)), st ^ 1);
+    const float sv = score64(st, 64 * kh);
+    const int key = n_lo + t * GT + 64 * kh + lane;
+    const bool keep = active && key < n_hi && key <= p && sv >= thr;
+    const unsigned long long bm = __ballot(keep);
+    if (bm) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&qcnt[qi], (int)__popcll(bm));
+      base = __shfl(base, 0);
+      if (keep) {
+        const int pos = base + (int)__popcll(bm & ((1ull << lane) - 1ull));
+        if (pos < cap) {
+          ls[pos] = sv;
+          li[pos] = key;
+        } else {
+          qovf[qi] = 1;
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+  }
+  if (active && kh == 0 && lane == 0) {
+    cand_n[slot] = qovf[qi] ? -1 : qcnt[qi];
+    cand_t[slot] = thr;
+  }
+}
+
 // ---------------------------------------------------------------- 4. select + band refine
 // Block-level (256 threads) exact k-th largest of vals[0..n) (finite, n >= k):
 // linear histogram to find the bin, then an exact rank count inside the bin.
@@ -975,6 +1152,10 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   // the refine kernel holds nsplit * cap candidates (11 bytes each) next to SELECT_FIXED bytes
   const int cap_sel = (int)(((163840 - SELECT_FIXED) / 11 / ns) / 64 * 64);
   if (pl.cap > cap_sel) pl.cap = cap_sel;
+  {
+    const int nv0 = L > 0 ? std::min(N, N - L + 1) : N;
+    pl.global_lists = L > 0 && nv0 >= 8 * SAMPLE && (double)topk * SAMPLE / nv0 <= SAMPLE / 8 && SAMPLE <= pl.cap;
+  }
   pl.fb_blocks = L < 32 ? L : 32;
   if (pl.fb_blocks < 1) pl.fb_blocks = 1;
   size_t off = 0;
@@ -1024,7 +1205,10 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
   {
     KernelTrace kt("indexer_score_filter", stream);
     const dim3 grid((L + QPB - 1) / QPB, pl.nsplit), block(64 * IDX_NW);
-    if (pl.small_off)
+    if (pl.global_lists)
+      hipLaunchKernelGGL(score_list_kernel, grid, block, 0, stream, q, k, w, eps, L, N, topk, pl.span, pl.nsplit,
+                         pl.cap, cand_s, cand_i, cand_n, cand_t);
+    else if (pl.small_off)
       hipLaunchKernelGGL((score_filter_kernel<uint16_t>), grid, block, 0, stream, q, k, w, eps, L, N,
                          topk, pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n, cand_t);
     else
