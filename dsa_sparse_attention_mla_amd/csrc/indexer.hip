@@ -542,8 +542,12 @@ static_assert(SAMPLE * QPB * 4 <= G_STAGE, "sample scores fit one stage");
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
 }
+// Same with a wave-uniform base address (SGPRs) plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
+}
 
-__global__ __launch_bounds__(64 * IDX_NW, 2) void score_list_kernel(
+__global__ __launch_bounds__(64 * IDX_NW) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_list_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int span, int nsplit, int cap,
     float* __restrict__ cand_s, int* __restrict__ cand_i, int* __restrict__ cand_n, float* __restrict__ cand_t) {
@@ -587,34 +591,47 @@ __global__ __launch_bounds__(64 * IDX_NW, 2) void score_list_kernel(
   // key r = slot / 16 of the tile and stored chunk c' = slot % 16, which holds global
   // chunk c' ^ (r % 16) of that key (the swizzle that keeps MFMA operand reads
   // conflict-free). key_of maps a tile row to a key index.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto dma_tile = [&](auto key_of, int st) {
 #pragma unroll
     for (int u = 0; u < G_DMA; ++u) {
-      const int slot = (wave * G_DMA + u) * 64 + lane;
+      const int slot = (wave_u * G_DMA + u) * 64 + lane;
       const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
-      dma16(k + (size_t)key_of(r) * ID + c * 8,
-            __builtin_amdgcn_readfirstlane(lds_stage + st * G_STAGE + (wave * G_DMA + u) * 1024));
+      dma16(k + (size_t)key_of(r) * ID + c * 8, lds_stage + st * G_STAGE + (wave_u * G_DMA + u) * 1024);
     }
+  };
+  // A tile of consecutive keys n0 .. n0+127: load u of wave w covers rows
+  // 4(4w + u) + lane/16, and with r % 16 = 4u + lane/16 the stored chunk lane%16 holds
+  // global chunk (lane%16) ^ (lane/16) ^ 4u, so the byte offset within the tile is
+  // 4096 w + 1024 u (uniform) plus lane_dma ^ 64u (per lane).
+  static_assert(G_DMA == 4, "row and chunk algebra of the tile loads");
+  const uint32_t lane_dma = ((lane >> 4) * 256) | ((((lane & 15) ^ (lane >> 4)) & 15) * 16);
+  auto dma_run = [&](int n0, int st) {
+    const unsigned char* base = (const unsigned char*)k + (size_t)n0 * (ID * 2) + wave_u * (G_DMA * 1024);
+#pragma unroll
+    for (int u = 0; u < G_DMA; ++u)
+      dma16s(base + u * 1024, lane_dma ^ (64u * u), lds_stage + st * G_STAGE + (wave_u * G_DMA + u) * 1024);
   };
 
   // Scores of keys r0 + lane (this query) from stage st: two 32-key chains
   // (lanes < 32 get keys r0 .. r0+31, lanes >= 32 keys r0+32 .. r0+63), with the
   // key fragments read two k-steps ahead of the MFMAs.
+  // Fragment addresses: both chains' rows have r % 16 = lane % 16, so stored chunk
+  // (2kc + lane/32) ^ (lane % 16) splits into a per-lane part and (32 kc) ^ (16 (lane & 14)).
+  const int xsw = 16 * (lane & 14);
+  const int lane_off = (lane & 31) * 256 + 16 * (((lane >> 5) ^ lane) & 1);
   auto score64 = [&](int st, int r0) -> float {
-    const unsigned char* sb = stage[st];
-    const int ra = r0 + (lane & 31), rb = ra + 32;
-    auto frag = [&](int r, int kc) {
-      const int c = 2 * kc + (lane >> 5);
-      return *(const bf16x8*)(sb + r * 256 + ((c ^ (r & 15)) * 16));
-    };
+    const unsigned char* ba = stage[st] + r0 * 256 + lane_off;
+    auto fa = [&](int kc) { return *(const bf16x8*)(ba + ((32 * kc) ^ xsw)); };
+    auto fb = [&](int kc) { return *(const bf16x8*)(ba + 32 * 256 + ((32 * kc) ^ xsw)); };
     f32x16 acca = {}, accb = {};
-    bf16x8 fa0 = frag(ra, 0), fb0 = frag(rb, 0), fa1 = frag(ra, 1), fb1 = frag(rb, 1);
+    bf16x8 fa0 = fa(0), fb0 = fb(0), fa1 = fa(1), fb1 = fb(1);
 #pragma unroll
     for (int kc = 0; kc < ID / 16; ++kc) {
       const bf16x8 xa = (kc & 1) ? fa1 : fa0, xb = (kc & 1) ? fb1 : fb0;
       if (kc + 2 < ID / 16) {
-        if (kc & 1) { fa1 = frag(ra, kc + 2); fb1 = frag(rb, kc + 2); }
-        else { fa0 = frag(ra, kc + 2); fb0 = frag(rb, kc + 2); }
+        if (kc & 1) { fa1 = fa(kc + 2); fb1 = fb(kc + 2); }
+        else { fa0 = fa(kc + 2); fb0 = fb(kc + 2); }
       }
       acca = mfma32x32x16(qa[kc], xa, acca);
       accb = mfma32x32x16(qa[kc], xb, accb);
@@ -662,15 +679,21 @@ __global__ __launch_bounds__(64 * IDX_NW, 2) void score_list_kernel(
   float* ls = cand_s + slot * cap;
   int* li = cand_i + slot * cap;
   const int ntiles = n_hi > n_lo ? (n_hi - n_lo + GT - 1) / GT : 0;
-  auto main_key = [&](int t) { return [=](int r) { return min(n_lo + t * GT + r, n_hi - 1); }; };
+  // rows past n_hi are loaded but masked; only a tile running past the end of the key
+  // array clamps its rows
+  auto dma_main = [&](int t, int st) {
+    const int n0 = n_lo + t * GT;
+    if (n0 + GT <= N) dma_run(n0, st);
+    else dma_tile([=](int r) { return min(n0 + r, N - 1); }, st);
+  };
   if (ntiles > 0) {
-    dma_tile(main_key(0), 0);
+    dma_main(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   lds_barrier();
   for (int t = 0; t < ntiles; ++t) {
     const int st = t & 1;
-    dma_tile(main_key(min(t + 1, ntiles - 1)), st ^ 1);
+    dma_main(min(t + 1, ntiles - 1), st ^ 1);
     const float sv = score64(st, 64 * kh);
     const int key = n_lo + t * GT + 64 * kh + lane;
     const bool keep = active && key < n_hi && key <= p && sv >= thr;
