@@ -50,6 +50,7 @@ constexpr int SEG = 4096;               // index entries staged per segment
 constexpr int KCH = D / 32 / 2;         // MFMA k-steps per half row (9)
 constexpr int NDBH = DV / 16 / 2;       // 16-wide value blocks per half (16)
 constexpr int NW = 8;                   // waves per workgroup: 4 head groups x 2 row halves
+constexpr float SLACK = 8.f;            // log2 of the largest unnormalised softmax weight
 constexpr int XCH_BYTES = NW * 64 * 32; // partial-score exchange: 8 floats per lane
 constexpr size_t LDS_BYTES = 2 * (size_t)STAGE + SEG * 4 + 2 * T * 4 + XCH_BYTES;
 }  // namespace
@@ -161,28 +162,28 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
         tmax = fmaxf(tmax, xv);
       }
     tmax = group4_max(tmax);
-    const float mnew = fmaxf(m, tmax);
+    // The reference max moves only when a score exceeds it by more than 2^SLACK (or
+    // on the first valid key): softmax does not depend on the reference, and weights
+    // up to 2^SLACK lose nothing in bf16 / fp32, so the output rescale is rare.
+    const bool bump = tmax - m > SLACK;
+    const float mnew = bump ? tmax : m;
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
     float pv[8];
-    float alpha = 1.f, psum = 0.f;
-    if (mnew == -INFINITY) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-    } else {
-      alpha = exp2_fast(m - mnew);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = exp2_fast(x[e] - mnew);
-        psum += pv[e];
-      }
-    }
-    psum = group4_sum(psum);
-    lsum = lsum * alpha + psum;
-    m = mnew;
-    if (__ballot(alpha != 1.f)) {
+    for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(x[e] - mref);
+    // The normaliser sums the bf16-rounded weights the value product uses, so the
+    // output is an exact convex combination of those weights (a dominant key gives
+    // back its value row, whatever the rounding of its weight).
+    const bf16x8 pk = pack_bf16x8(pv);
+    const float psum = group4_sum(sum_bf16x8(pk));
+    if (__ballot(bump)) {
+      const float alpha = bump ? exp2_fast(m - mref) : 1.f;
+      lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < NDBH; ++db) o[db] *= alpha;
     }
-    const bf16x8 pk = pack_bf16x8(pv);
+    lsum += psum;
+    m = mnew;
     // V^T operand: lane (g, c16) points at row 4g + c16/4 (and 16 + that), columns 4*(c16%4)
     const unsigned char* vb = st + (4 * g + (c16 >> 2)) * ROWB + 512 * half + 8 * (c16 & 3);
 #pragma unroll
@@ -234,10 +235,8 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   uint16_t* orow = out + (((size_t)b * L + i) * H + head) * DV + 256 * half + 4 * g;
 #pragma unroll
   for (int db = 0; db < NDBH; ++db) {
-    uint2 w;
-    w.x = (uint32_t)f2bf_bits(o[db][0] * inv) | ((uint32_t)f2bf_bits(o[db][1] * inv) << 16);
-    w.y = (uint32_t)f2bf_bits(o[db][2] * inv) | ((uint32_t)f2bf_bits(o[db][3] * inv) << 16);
-    *(uint2*)(orow + 16 * db) = w;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    *(bf16x4*)(orow + 16 * db) = __builtin_convertvector(o[db] * inv, bf16x4);
   }
 }
 

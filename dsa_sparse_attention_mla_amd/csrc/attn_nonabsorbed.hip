@@ -394,13 +394,14 @@ __global__ __launch_bounds__(512) void nonabsorbed_bf16_kernel(
       const float mnew = bump ? tmax : m;
       const float mref = mnew == -INFINITY ? 0.f : mnew;
       const float nb = -mref * sl;
-      float pv[16], psum = 0.f;
+      float pv[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        pv[j] = exp2_fast(fmaf(sacc[j], sl, nb));
-        psum += pv[j];
-      }
-      psum = half_sum(psum);
+      for (int j = 0; j < 16; ++j) pv[j] = exp2_fast(fmaf(sacc[j], sl, nb));
+      // the normaliser sums the bf16-rounded weights the value product uses
+      bf16x8 pk[2];
+      pk[0] = pack_bf16x8(pv);
+      pk[1] = pack_bf16x8(pv + 8);
+      const float psum = half_sum(sum_bf16x8(pk[0]) + sum_bf16x8(pk[1]));
       if (__ballot(bump)) {
         const float alpha = bump ? exp2_fast((m - mref) * sl) : 1.f;
         lsum *= alpha;
@@ -409,14 +410,6 @@ __global__ __launch_bounds__(512) void nonabsorbed_bf16_kernel(
       }
       lsum += psum;
       m = mnew;
-      bf16x8 pk[2];
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        typedef float f32x8 __attribute__((ext_vector_type(8)));
-        f32x8 v8 = {pv[8 * ks2], pv[8 * ks2 + 1], pv[8 * ks2 + 2], pv[8 * ks2 + 3],
-                    pv[8 * ks2 + 4], pv[8 * ks2 + 5], pv[8 * ks2 + 6], pv[8 * ks2 + 7]};
-        pk[ks2] = __builtin_convertvector(v8, bf16x8);
-      }
       // V^T fragment: lane points at key 16ks + 4g + (lane%16)/4 (+8 for the upper
       // four k entries), dims 32db + 16*((lane/16)%2) + 4*(lane%4).
       const unsigned char* vb = vs + (4 * g + ((lane & 15) >> 2)) * NB_VROW + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));

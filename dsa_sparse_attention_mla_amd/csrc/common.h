@@ -54,12 +54,12 @@ __device__ __forceinline__ float bf_bits2f(uint16_t b) {
   return __builtin_bit_cast(float, ((uint32_t)b) << 16);
 }
 
+// Eight floats to bf16 with the hardware convert (round to nearest even, the same
+// as f2bf_bits for finite values), two per instruction.
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
-  typedef short short8v __attribute__((ext_vector_type(8)));
-  short8v v;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (short)f2bf_bits(x[e]);
-  return __builtin_bit_cast(bf16x8, v);
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, bf16x8);
 }
 
 // Workgroup barrier that orders LDS accesses only. __syncthreads() also waits for
@@ -75,17 +75,30 @@ __device__ __forceinline__ void lds_barrier() {
 // rescale for denormal results that costs several instructions per call.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Butterfly over lane groups: combine lanes l, l^16, l^32 (the four 16-lane
-// groups that hold the same MFMA column).
+// Sum of the eight bf16 values of v, in fp32 (exact conversions), pairwise.
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v) {
+  const u32x4 w = __builtin_bit_cast(u32x4, v);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    s += __uint_as_float(w[e] << 16) + __uint_as_float(w[e] & 0xFFFF0000u);
+  return s;
+}
+
+// Combine lanes l, l^16, l^32, l^48 (the four 16-lane groups that hold the same
+// 16x16 MFMA column) with the lane-swap instructions: each swap hands both lanes of
+// a pair the two values in the same order, so all four lanes end bit-identical.
 __device__ __forceinline__ float group4_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group4_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 }  // namespace dsa
