@@ -50,10 +50,10 @@ FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 # Counter readings (KiB per dispatch, mean of 5 launches of this workload) and a
 # digest of the kernel sources they were taken on.
 COUNTERS = {
-    "indexer_score_filter": {"fetch_kib": 139549.2, "write_kib": 54382.0,
-                             "sources": ("indexer.hip", "common.h"), "sha256_16": "6ebcf3ef3a9b40e0"},
-    "sparse_attn": {"fetch_kib": 892832.5, "write_kib": 69635.0,
-                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "3523ea51723a53c2"},
+    "indexer_score_filter": {"fetch_kib": 202503.6, "write_kib": 39248.1,
+                             "sources": ("indexer.hip", "common.h"), "sha256_16": "aaf48d8f488a25d7"},
+    "sparse_attn": {"fetch_kib": 890765.9, "write_kib": 65536.0,
+                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "0d2630e32c2f7446"},
 }
 METRIC = "prefill tok/s at 128K ctx (sparse MLA); MFMA util %, HBM GB/s % of peak"
 
