@@ -24,7 +24,12 @@ The line also carries:
                 (python bench.py --copy-calibration 1024); null once the
                 kernel's source differs from the one the counters were taken on.
 
+  dense_baseline the path the sparse call replaces (masked dense attention) on
+                the same chunk, with the speed-ups of the sparse path.
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
+       python bench.py --sweep        context sweep, sparse vs masked dense
+       python bench.py --copy-calibration MIB
 """
 from __future__ import annotations
 
@@ -153,6 +158,55 @@ def dense_configs(dm, torch, reps=10):
     return res
 
 
+def masked_baseline(dm, torch, q, kv, idx, t_sparse_ms, step_ms, reps=3):
+    """The path the sparse call replaces, on the same chunk: dense absorbed attention over
+    every visible key under the same top-k selection ("Sparse prefill for GLM", "The dense
+    mask"). Not part of the step; reported with the sparse speed-ups it implies."""
+    ws = torch.empty(dm.masked_workspace_bytes(1, L, N), dtype=torch.uint8, device=q.device)
+    out = torch.empty((L, H, 512), dtype=torch.bfloat16, device=q.device)
+    ms = _time(lambda: dm.mla_prefill_masked(q, kv, idx, out=out, workspace=ws), torch, reps)
+    visible = sum(min(N, N - L + i + 1) for i in range(L))
+    fl = 2176 * H * visible
+    return {"workload": f"masked dense absorbed attention, L={L}, N={N}, {H} heads, top-{TOPK} mask",
+            "ms": ms, "tflops": fl / ms / 1e9, "mfma_frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS,
+            "attention_speedup_sparse": ms / t_sparse_ms if t_sparse_ms else None,
+            "step_speedup_sparse": (step_ms - t_sparse_ms + ms) / step_ms if t_sparse_ms else None}
+
+
+def sweep(dm, torch, dev):
+    """Chunked-prefill context sweep ("Sparse prefill for GLM", "When it runs" and the
+    prompt-length benchmark): for each context N and chunk length L, one prefill step of
+    the chunk with the sparse path (indexer + gathered attention) and with the path it
+    replaces (indexer + masked dense attention); the crossover places the gate's minimum
+    context on this GPU. Inputs: one synthetic draw at the largest sizes, sliced."""
+    from synth import gen_dsa_prefill
+    Nmax, Lmax = 131072, 1024
+    g = gen_dsa_prefill(SEED, Lmax, Nmax, H=H)
+    full = {k: dev(g[k]) for k in ("q_idx", "k_idx", "w", "q", "kv")}
+    rows = []
+    for n in (4096, 8192, 16384, 32768, 65536, 131072):
+        for l in (512, 1024):
+            q_idx, w, q = full["q_idx"][:l], full["w"][:l], full["q"][:l]
+            k_idx, kv = full["k_idx"][:n], full["kv"][:n]
+            ws = torch.empty(dm.indexer_workspace_bytes(l, n, TOPK, BLOCK), dtype=torch.uint8, device=q.device)
+            mws = torch.empty(dm.masked_workspace_bytes(1, l, n), dtype=torch.uint8, device=q.device)
+            idx = torch.empty((l, TOPK), dtype=torch.int32, device=q.device)
+            out = torch.empty((l, H, 512), dtype=torch.bfloat16, device=q.device)
+            t_idx = _time(lambda: dm.dsa_indexer_topk(q_idx, k_idx, w, TOPK, block=BLOCK, out=idx, workspace=ws),
+                          torch, 5)
+            t_sp = _time(lambda: dm.mla_prefill_sparse(q, kv, idx, out=out), torch, 5)
+            t_md = _time(lambda: dm.mla_prefill_masked(q, kv, idx, out=out, workspace=mws), torch, 3)
+            row = {"N": n, "L": l, "indexer_ms": t_idx, "sparse_attn_ms": t_sp, "masked_dense_attn_ms": t_md,
+                   "sparse_tok_s": l / ((t_idx + t_sp) * 1e-3), "dense_tok_s": l / ((t_idx + t_md) * 1e-3),
+                   "speedup": (t_idx + t_md) / (t_idx + t_sp), "gate_says_sparse": bool(dm.use_sparse(True, 1, l, n))}
+            log(f"sweep N={n} L={l}: sparse {row['sparse_tok_s']:.0f} tok/s, dense {row['dense_tok_s']:.0f} tok/s, "
+                f"x{row['speedup']:.2f}")
+            rows.append(row)
+    wins = [r["N"] for r in rows if r["speedup"] > 1.0]
+    return {"sweep": rows, "smallest_context_where_sparse_wins": min(wins) if wins else None,
+            "gate_min_context": 16384}
+
+
 def _time(fn, torch, reps):
     for _ in range(2):
         fn()
@@ -174,6 +228,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=96)
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the context sweep (sparse vs masked dense, N = 4K..128K, L = 512/1024)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -191,6 +247,10 @@ def main():
     from synth import gen_dsa_prefill
     sys.path.insert(0, os.path.join(HERE, "tests"))
     from gpu_util import dev
+
+    if args.sweep:
+        print(json.dumps(sweep(dm, torch, dev)), flush=True)
+        return
 
     log("bench: generating inputs")
     g = gen_dsa_prefill(SEED, L, N, H=H)
@@ -238,9 +298,12 @@ def main():
                 "per_launch": f"{by:.4e} B (gathered rows, q, out, idx)", "ms": t_att}
 
     other = None
+    baseline = None
     if not args.no_other_configs:
         log("bench: dense configurations")
         other = dense_configs(dm, torch)
+        log("bench: masked dense baseline")
+        baseline = masked_baseline(dm, torch, q, kv, idx, t_att, ms_per_step)
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
@@ -262,6 +325,7 @@ def main():
                                  "frac_hbm": sparse_attn_bytes(L, TOPK, H) / (t_att * 1e-3) / 1e9 / PEAK_HBM_GBS if t_att else None,
                                  "tflops": sparse_attn_flops(L, TOPK, H) / (t_att * 1e-3) / 1e12 if t_att else None},
         "other_configs": other,
+        "dense_baseline": baseline,
     }
     print(json.dumps(line), flush=True)
 

@@ -150,6 +150,49 @@ def mla_prefill_sparse(q, kv, idx, *, scale=None, query_block=1024, out=None):
     return out
 
 
+def masked_workspace_bytes(B: int, L: int, N: int) -> int:
+    """Workspace of mla_prefill_masked (the selection bitmaps)."""
+    n = ctypes.c_size_t(0)
+    p = ctypes.c_void_p(256)                # placeholder pointers: a size query reads nothing
+    check(lib().mla_prefill_masked(B, L, N, 16, p, p, p, 1, 1.0, p, None, ctypes.byref(n), None),
+          "mla_prefill_masked (workspace query)")
+    return n.value
+
+
+def mla_prefill_masked(q, kv, idx, *, scale=None, out=None, workspace=None):
+    """Dense absorbed prefill under each query's top-k selection (the gated path).
+
+    q [L,H,576] or [B,L,H,576] bf16, kv [N,576] or [B,N,576] bf16, idx [L,topk] or
+    [B,L,topk] int32 -> out [L,H,512] or [B,L,H,512] bf16.
+    """
+    batched = q.dim() == 4
+    if not batched:
+        q, kv, idx = q[None], kv[None], idx[None]
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv, "kv", torch.bfloat16, 3)
+    _need(idx, "idx", torch.int32, 3)
+    B, L, H, D = q.shape
+    N = kv.shape[1]
+    if D != 576 or kv.shape[0] != B or kv.shape[2] != 576 or idx.shape[:2] != (B, L):
+        raise ValueError("shapes must be q [B,L,H,576], kv [B,N,576], idx [B,L,topk]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(576)
+    if out is None:
+        out = torch.empty((B, L, H, 512), dtype=torch.bfloat16, device=q.device)
+    else:
+        if not batched:
+            out = out[None]
+        _need(out, "out", torch.bfloat16, 4)
+    nbytes = masked_workspace_bytes(B, L, N)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    st = lib().mla_prefill_masked(B, L, N, H, _ptr(q), _ptr(kv), _ptr(idx), idx.shape[2], float(scale), _ptr(out),
+                                  _ptr(workspace), ctypes.byref(n), _stream(q.device))
+    check(st, "mla_prefill_masked")
+    return out if batched else out[0]
+
+
 def use_sparse(sparse_prefill: bool, B: int, L: int, N: int,
                min_context: int = SPARSE_PREFILL_MIN_CONTEXT_DEFAULT) -> bool:
     """The gate ("Sparse prefill for GLM", section "When it runs"): sparse only when switched
@@ -168,9 +211,8 @@ def dsa_prefill(q, kv, q_idx, k_idx, w, topk, *, scale=None, block=4096, query_b
     idx = dsa_indexer_topk(q_idx, k_idx, w, topk, block=block)
     if use_sparse(sparse_prefill, 1, L, N, min_context):
         return mla_prefill_sparse(q, kv, idx, scale=scale, query_block=query_block), idx
-    # below the gate: the dense path over all visible keys under the top-k selection,
-    # which equals gathering exactly the selected rows
-    return mla_prefill_sparse(q, kv, idx, scale=scale, query_block=query_block), idx
+    # below the gate: the dense path over every visible key under the top-k selection
+    return mla_prefill_masked(q, kv, idx, scale=scale), idx
 
 
 class kernel_trace:

@@ -105,7 +105,7 @@ int mla_prefill_dense(int mode, int dtype, int B, int L, int N, int H, const voi
   if (mode == DSA_MLA_MODE_NONABSORBED)
     return hip_status(dsa::launch_nonabsorbed_attn(dtype == DSA_MLA_BF16, q, q_rope, k, k_rope, v, out, B, L, N, H,
                                                    causal, scale, st));
-  return hip_status(dsa::launch_absorbed_attn(false, (const uint16_t*)q, (const uint16_t*)k, nullptr, (uint16_t*)out,
+  return hip_status(dsa::launch_absorbed_attn(0, (const uint16_t*)q, (const uint16_t*)k, nullptr, nullptr, (uint16_t*)out,
                                               B, L, N, H, 0, 0, L, causal, scale, st));
 }
 
@@ -144,11 +144,33 @@ int mla_prefill_sparse(int B, int L, int N, int H, const void* q, const void* kv
   if (a != DSA_MLA_OK) return a;
   for (int q0 = 0; q0 < L; q0 += query_block) {
     const int nq = L - q0 < query_block ? L - q0 : query_block;
-    const hipError_t e = dsa::launch_absorbed_attn(true, (const uint16_t*)q, (const uint16_t*)kv, idx, (uint16_t*)out,
+    const hipError_t e = dsa::launch_absorbed_attn(1, (const uint16_t*)q, (const uint16_t*)kv, idx, nullptr, (uint16_t*)out,
                                                    1, L, N, H, topk, q0, nq, 0, scale, (hipStream_t)stream);
     if (e != hipSuccess) return DSA_MLA_HIP;
   }
   return DSA_MLA_OK;
+}
+
+int mla_prefill_masked(int B, int L, int N, int H, const void* q, const void* kv, const int32_t* idx, int topk,
+                       float scale, void* out, void* ws, size_t* ws_bytes, void* stream) {
+  if (B < 0 || L < 0 || N < 1 || H < 1 || topk < 1) return DSA_MLA_INVALID_ARG;
+  if (L > N) return DSA_MLA_INVALID_ARG;
+  if (!std::isfinite(scale)) return DSA_MLA_INVALID_ARG;
+  if (q == nullptr || kv == nullptr || idx == nullptr || out == nullptr) return DSA_MLA_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv) || !aligned4(idx) || !aligned16(out)) return DSA_MLA_INVALID_ARG;
+  if (H % 16 != 0) return DSA_MLA_UNSUPPORTED;
+  const size_t words = (size_t)B * L * (size_t)((N + 31) / 32);
+  const int wsr = workspace_step(words * 4, ws, ws_bytes);
+  if (wsr >= 0) return wsr;
+  if (B == 0 || L == 0) return DSA_MLA_OK;
+  const int a = check_arch();
+  if (a != DSA_MLA_OK) return a;
+  uint32_t* mask = (uint32_t*)ws;
+  hipError_t e = dsa::launch_mask_rows(idx, B, L, N, topk, mask, (hipStream_t)stream);
+  if (e != hipSuccess) return DSA_MLA_HIP;
+  e = dsa::launch_absorbed_attn(2, (const uint16_t*)q, (const uint16_t*)kv, idx, mask, (uint16_t*)out, B, L, N, H,
+                                topk, 0, L, 1, scale, (hipStream_t)stream);
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -1,12 +1,15 @@
 // Absorbed (latent-space) MLA attention over joined 576-wide latent+rope rows.
 //
-// One kernel serves two calls:
+// One kernel serves three calls:
 //  * dense absorbed prefill (keys 0..p_i of a contiguous cache, bottom-right
-//    causal), and
+//    causal),
 //  * sparse prefill: each query attends only to the rows its index list names,
 //    gathered from the cache ("Sparse prefill for GLM", section "Sparse
 //    attention": joined latent+rope rows, all heads share the gathered block,
-//    absorbed attention whose value is the latent part of the row).
+//    absorbed attention whose value is the latent part of the row), and
+//  * masked dense prefill, the path the sparse one replaces (same page, section
+//    "The dense mask"): every visible key is visited and only the keys the
+//    query's top-k selection marks in a bitmap get weight.
 //
 // Work decomposition (gfx950): one workgroup per query and 64-head group, 8
 // waves. Wave w owns the 16 heads of head group w%4 and one half h = w/4 of the
@@ -55,10 +58,15 @@ constexpr int XCH_BYTES = NW * 64 * 32; // partial-score exchange: 8 floats per 
 constexpr size_t LDS_BYTES = 2 * (size_t)STAGE + SEG * 4 + 2 * T * 4 + XCH_BYTES;
 }  // namespace
 
-template <bool SPARSE>
+// MODE: 0 dense (every visible key), 1 sparse (gathered index lists), 2 masked
+// dense (every visible key, weighted only where the query's selection bitmap has
+// its bit set).
+template <int MODE>
 __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
-    uint16_t* __restrict__ out, int L, int N, int H, int topk, int q0, int causal, float scale_log2) {
+    const uint32_t* __restrict__ mask, uint16_t* __restrict__ out, int L, int N, int H, int topk, int q0, int causal,
+    float scale_log2) {
+  constexpr bool SPARSE = MODE == 1;
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   unsigned char* ring = dyn;                                // [2][STAGE]
   int* sidx = (int*)(dyn + 2 * (size_t)STAGE);              // [SEG]
@@ -76,6 +84,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   const int count = SPARSE ? topk : (causal ? p + 1 : N);
   const uint16_t* kvb = kv + (size_t)b * N * D;
   const int32_t* irow = SPARSE ? idx + ((size_t)b * L + i) * topk : nullptr;
+  const uint32_t* mrow = MODE == 2 ? mask + ((size_t)b * L + i) * ((N + 31) / 32) : nullptr;
 
   bf16x8 qf[KCH];
   {
@@ -120,7 +129,11 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
         *(u32x4*)(st + r * ROWB + col * 16) = src[u];
       }
     }
-    if (tid < T) sflag[st_i * T + tid] = key_of(t, tid, seg_base, seg_cnt) >= 0;
+    if (tid < T) {
+      bool v = key_of(t, tid, seg_base, seg_cnt) >= 0;
+      if constexpr (MODE == 2) v = v && ((mrow[(seg_base + t * T) / 32] >> tid) & 1u);
+      sflag[st_i * T + tid] = v;
+    }
   };
   u32x4 pf[PF][CPT];
 
@@ -240,30 +253,66 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   }
 }
 
+// One workgroup per (query, batch): the query's selection bitmap (bit n of word n/32
+// set when its index list names key n, entries outside [0, N) ignored), built in LDS
+// a chunk of words at a time and written out whole.
+__global__ __launch_bounds__(256) void mask_rows_kernel(const int32_t* __restrict__ idx, int L, int N, int topk,
+                                                        uint32_t* __restrict__ mask) {
+  constexpr int CW = 8192;                  // words per chunk (32 KB of LDS)
+  __shared__ uint32_t words[CW];
+  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int W = (N + 31) / 32;
+  const int32_t* irow = idx + ((size_t)b * L + i) * topk;
+  uint32_t* mrow = mask + ((size_t)b * L + i) * W;
+  for (int c0 = 0; c0 < W; c0 += CW) {
+    const int cw = min(CW, W - c0);
+    for (int e = tid; e < cw; e += 256) words[e] = 0u;
+    __syncthreads();
+    for (int t = tid; t < topk; t += 256) {
+      const int n = irow[t];
+      const int wd = n >> 5;
+      if (n >= 0 && n < N && wd >= c0 && wd < c0 + cw) atomicOr(&words[wd - c0], 1u << (n & 31));
+    }
+    __syncthreads();
+    for (int e = tid; e < cw; e += 256) mrow[c0 + e] = words[e];
+    __syncthreads();
+  }
+}
+
+hipError_t launch_mask_rows(const int32_t* idx, int B, int L, int N, int topk, uint32_t* mask, hipStream_t stream) {
+  KernelTrace kt("mask_rows", stream);
+  hipLaunchKernelGGL(mask_rows_kernel, dim3(L, B), dim3(256), 0, stream, idx, L, N, topk, mask);
+  return hipGetLastError();
+}
+
 // Launch over queries [q0, q0 + nq) of a chunk of L queries. H must be a multiple of 16;
 // a workgroup covers 64 heads (grid z walks head groups).
-hipError_t launch_absorbed_attn(bool sparse, const uint16_t* q, const uint16_t* kv, const int32_t* idx, uint16_t* out,
-                                int B, int L, int N, int H, int topk, int q0, int nq, int causal, float scale,
-                                hipStream_t stream) {
+hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                                const uint32_t* mask, uint16_t* out, int B, int L, int N, int H, int topk, int q0,
+                                int nq, int causal, float scale, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)absorbed_attn_kernel<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)absorbed_attn_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)LDS_BYTES);
-    if (e != hipSuccess) return e;
+    const void* fns[3] = {(const void*)absorbed_attn_kernel<0>, (const void*)absorbed_attn_kernel<1>,
+                          (const void*)absorbed_attn_kernel<2>};
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+      if (e != hipSuccess) return e;
+    }
     attr_set = true;
   }
   const float scale_log2 = scale * 1.4426950408889634f;
   dim3 grid(nq, B, (H + 63) / 64), block(64 * NW);
-  KernelTrace kt(sparse ? "sparse_attn" : "absorbed_dense_attn", stream);
-  if (sparse)
-    hipLaunchKernelGGL((absorbed_attn_kernel<true>), grid, block, LDS_BYTES, stream, q, kv, idx, out, L, N, H, topk,
-                       q0, causal, scale_log2);
+  static const char* names[3] = {"absorbed_dense_attn", "sparse_attn", "masked_dense_attn"};
+  KernelTrace kt(names[mode], stream);
+  if (mode == 1)
+    hipLaunchKernelGGL((absorbed_attn_kernel<1>), grid, block, LDS_BYTES, stream, q, kv, idx, mask, out, L, N, H,
+                       topk, q0, causal, scale_log2);
+  else if (mode == 2)
+    hipLaunchKernelGGL((absorbed_attn_kernel<2>), grid, block, LDS_BYTES, stream, q, kv, idx, mask, out, L, N, H,
+                       topk, q0, causal, scale_log2);
   else
-    hipLaunchKernelGGL((absorbed_attn_kernel<false>), grid, block, LDS_BYTES, stream, q, kv, idx, out, L, N, H, topk,
-                       q0, causal, scale_log2);
+    hipLaunchKernelGGL((absorbed_attn_kernel<0>), grid, block, LDS_BYTES, stream, q, kv, idx, mask, out, L, N, H,
+                       topk, q0, causal, scale_log2);
   return hipGetLastError();
 }
 

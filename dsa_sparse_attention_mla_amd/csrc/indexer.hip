@@ -25,6 +25,8 @@
 //  5. exact_fallback:     rows whose candidates overflowed (huge ties) are solved
 //                         from the canonical fp64 score of every visible key.
 // Output rows are in ascending key order, padded with -1.
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -1176,8 +1178,18 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   const int cap_sel = (int)(((163840 - SELECT_FIXED) / 11 / ns) / 64 * 64);
   if (pl.cap > cap_sel) pl.cap = cap_sel;
   {
+    // Long contexts use the global-list kernel, whose lists live in memory and are
+    // bounded only by what the refine kernel holds (cap_sel per split). It is chosen
+    // when every query group gets the sampled start and the expected candidate count,
+    // k + 6 sqrt(k nv / S) + 8 nv / S (the keys above the rk-th largest of S samples),
+    // stays under 60% of that capacity; a list that still overflows costs its query
+    // the exact fallback.
     const int nv0 = L > 0 ? std::min(N, N - L + 1) : N;
-    pl.global_lists = L > 0 && nv0 >= 8 * SAMPLE && (double)topk * SAMPLE / nv0 <= SAMPLE / 8 && SAMPLE <= pl.cap;
+    const double mean = (double)topk * SAMPLE / std::max(nv0, 1);
+    const double expect = topk + 6.0 * std::sqrt((double)topk * nv0 / SAMPLE) + 8.0 * nv0 / SAMPLE;
+    pl.global_lists = L > 0 && nv0 >= 8 * SAMPLE && mean <= SAMPLE / 8 && SAMPLE <= cap_sel &&
+                      expect <= 0.6 * (double)ns * cap_sel;
+    if (pl.global_lists) pl.cap = cap_sel;
   }
   pl.fb_blocks = L < 32 ? L : 32;
   if (pl.fb_blocks < 1) pl.fb_blocks = 1;

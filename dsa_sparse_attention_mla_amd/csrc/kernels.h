@@ -21,9 +21,10 @@ class KernelTrace {
   void* a_;
 };
 
-hipError_t launch_absorbed_attn(bool sparse, const uint16_t* q, const uint16_t* kv, const int32_t* idx, uint16_t* out,
-                                int B, int L, int N, int H, int topk, int q0, int nq, int causal, float scale,
-                                hipStream_t stream);
+hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                                const uint32_t* mask, uint16_t* out, int B, int L, int N, int H, int topk, int q0,
+                                int nq, int causal, float scale, hipStream_t stream);
+hipError_t launch_mask_rows(const int32_t* idx, int B, int L, int N, int topk, uint32_t* mask, hipStream_t stream);
 
 hipError_t launch_nonabsorbed_attn(bool bf16, const void* qn, const void* qr, const void* kn, const void* kr,
                                    const void* v, void* out, int B, int L, int N, int H, int causal, float scale,

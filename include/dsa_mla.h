@@ -2,10 +2,12 @@
  * dsa_mla.h -- C ABI of libdsa_mla.so: MLA prefill and DeepSeek-sparse-attention
  * (DSA) prefill on AMD Instinct MI355X (gfx950).
  *
- * Three calls:
+ * Four calls:
  *   mla_prefill_dense   dense causal MLA prefill, non-absorbed or absorbed
  *   dsa_indexer_topk    indexer scores fused with a running top-k selection
  *   mla_prefill_sparse  absorbed attention over each query's gathered top-k rows
+ *   mla_prefill_masked  dense absorbed attention under each query's top-k mask
+ *                       (the path the sparse call replaces; the gated case)
  *
  * Conventions shared by all calls
  * -------------------------------
@@ -127,6 +129,28 @@ int dsa_indexer_topk(int B, int L, int N, int Hi, int Di, const void* q_idx, con
  */
 int mla_prefill_sparse(int B, int L, int N, int H, const void* q, const void* kv, const int32_t* idx, int topk,
                        float scale, int query_block, void* out, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * mla_prefill_masked -- dense absorbed MLA prefill under each query's top-k
+ * selection ("Sparse prefill for GLM", section "The dense mask": before the
+ * sparse path, the indexer's choice became a boolean mask with one row per query
+ * and one column per key, and attention ran over every key with the unselected
+ * ones masked out; section "When it runs": calls the gate turns away still take
+ * this path).
+ *
+ *   score[b,i,h,n] = scale * q[b,i,h,:] . kv[b,n,:]   for n <= N-L+i named in idx[b,i,:]
+ *   out[b,i,h,:]   = softmax_n(score) . kv[b,n,0:512]
+ *   q [B,L,H,576] bf16   kv [B,N,576] bf16   idx [B,L,topk] int32   out [B,L,H,512] bf16
+ *
+ * Index entries outside [0, N) are ignored, a repeated index selects its key
+ * once, and a selected key past the causal limit stays masked. Every visible
+ * key is visited: this is the dense cost the sparse call removes. A row with no
+ * selected visible key gets zeros. Supported: B >= 1, 0 <= L <= N, H a multiple
+ * of 16. Needs workspace: B*L*ceil(N/32) 32-bit words for the selection bitmaps
+ * (query its size with ws == NULL); the bitmaps are rebuilt on every call.
+ */
+int mla_prefill_masked(int B, int L, int N, int H, const void* q, const void* kv, const int32_t* idx, int topk,
+                       float scale, void* out, void* ws, size_t* ws_bytes, void* stream);
 
 /*
  * Per-kernel timing (diagnostics). dsa_mla_trace_enable(1) makes every later

@@ -117,3 +117,29 @@ def test_gate_helper_matches_predicate():
     assert not dm.use_sparse(True, 2, 512, 131072)
     assert not dm.use_sparse(True, 1, 1, 131072)
     assert not dm.use_sparse(False, 1, 512, 131072)
+
+
+def _masked(**kw):
+    a = dict(B=1, L=4, N=64, H=64, q=P, kv=P, idx=P, topk=8, scale=0.1, out=P, ws=None, ws_bytes=None, stream=None)
+    a.update(kw)
+    return dm.lib().mla_prefill_masked(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=24), _lib.UNSUPPORTED), (dict(topk=0), _lib.INVALID_ARG), (dict(idx=None), _lib.INVALID_ARG),
+    (dict(L=65, N=64), _lib.INVALID_ARG), (dict(out=MIS), _lib.INVALID_ARG), (dict(kv=None), _lib.INVALID_ARG),
+    (dict(scale=float("nan")), _lib.INVALID_ARG), (dict(), _lib.WORKSPACE), (dict(L=0), _lib.OK),
+])
+def test_masked_validation(kw, code):
+    assert _masked(**kw) == code
+
+
+def test_masked_workspace_is_the_bitmaps():
+    sz = ctypes.c_size_t(0)
+    assert _masked(B=2, L=1024, N=131072, ws_bytes=ctypes.byref(sz)) == _lib.OK
+    assert sz.value == 2 * 1024 * (131072 // 32) * 4
+    assert dm.masked_workspace_bytes(1, 3, 33) == 3 * 2 * 4
+    ok = ctypes.c_size_t(sz.value)
+    assert _masked(B=2, L=1024, N=131072, ws=P, ws_bytes=ctypes.byref(ok)) == _lib.ARCH
+    small = ctypes.c_size_t(sz.value - 4)
+    assert _masked(B=2, L=1024, N=131072, ws=P, ws_bytes=ctypes.byref(small)) == _lib.WORKSPACE

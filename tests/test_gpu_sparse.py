@@ -107,3 +107,69 @@ def test_sparse_inputs_unchanged_outputs_overwritten_repeatable():
         assert torch.equal(a, b)
     assert not torch.isnan(out1).any()
     assert torch.equal(out1, out2)
+
+
+# ---- dense attention under the top-k mask (the path the sparse call replaces; the gated case)
+
+def _masked_case(seed, L, N, topk, H=64):
+    g = gen_absorbed(seed, L, N, H=H)
+    idx = gen_topk_indices(seed + 7, L, N, topk)
+    return g, idx
+
+
+@pytest.mark.parametrize("L,N,topk", [(20, 500, 64), (33, 1000, 100), (5, 40, 48), (1, 37, 4)])
+def test_masked_dense_matches_oracle_and_gather(L, N, topk):
+    g, idxn = _masked_case(110 + L, L, N, topk)
+    q, kv, qf, kvf = dev(g["q"]), dev(g["kv"]), to_f64(g["q"]), to_f64(g["kv"])
+    out = host_f64(dm.mla_prefill_masked(q, kv, dev(idxn)))
+    ref = oracle.mla_masked_dense(qf, kvf, idxn, SCALE)
+    assert_close(out, ref, TOL_BF16, f"masked dense L={L} N={N} topk={topk}")
+    gathered = host_f64(dm.mla_prefill_sparse(q, kv, dev(idxn)))
+    assert_close(out, gathered, TOL_BF16, "masked dense vs gather")
+
+
+def test_masked_dense_selection_rules():
+    """-1 and out-of-range entries ignored, a repeated index selects its key once, a
+    selected key past the causal limit stays masked, an empty selection gives zeros."""
+    L, N, topk = 6, 70, 8
+    g, _ = _masked_case(120, L, N, topk)
+    q, kv, qf, kvf = dev(g["q"]), dev(g["kv"]), to_f64(g["q"]), to_f64(g["kv"])
+    idxn = np.full((L, topk), -1, dtype=np.int32)
+    idxn[0, :3] = [0, 64, 69]            # 69 is past query 0's causal limit (64)
+    idxn[1, :4] = [5, 5, 5, 30]           # repeats select once
+    idxn[2, :4] = [5, 70, -9, 11]         # out of range: ignored
+    idxn[3] = np.arange(8) * 9
+    out = host_f64(dm.mla_prefill_masked(q, kv, dev(idxn)))
+    ref = oracle.mla_masked_dense(qf, kvf, idxn, SCALE)
+    assert np.all(out[4] == 0) and np.all(out[5] == 0)
+    assert_close(out, ref, TOL_BF16, "masked selection rules")
+
+
+def test_masked_dense_batch():
+    L, N, topk, H = 12, 200, 32, 64
+    cases = [_masked_case(130 + b, L, N, topk, H) for b in range(2)]
+    q = torch.stack([dev(c[0]["q"]) for c in cases])
+    kv = torch.stack([dev(c[0]["kv"]) for c in cases])
+    idx = torch.stack([dev(c[1]) for c in cases])
+    out = dm.mla_prefill_masked(q, kv, idx)
+    one = dm.mla_prefill_masked(q[1], kv[1], idx[1])
+    torch.cuda.synchronize()
+    assert torch.equal(out[1], one)
+    for b, (g, idxn) in enumerate(cases):
+        ref = oracle.mla_masked_dense(to_f64(g["q"]), to_f64(g["kv"]), idxn, SCALE)
+        assert_close(host_f64(out[b]), ref, TOL_BF16, f"masked batch {b}")
+
+
+def test_dsa_prefill_gated_uses_masked_dense():
+    """Below the minimum context the gate sends the chunk to the masked dense path;
+    the result matches the oracle's gated prefill."""
+    from synth import gen_dsa_prefill
+    L, N, topk = 24, 3000, 128
+    g = gen_dsa_prefill(140, L, N, H=64)
+    t = {k: dev(v) for k, v in g.items()}
+    out, idx = dm.dsa_prefill(t["q"], t["kv"], t["q_idx"], t["k_idx"], t["w"], topk)
+    torch.cuda.synchronize()
+    f = {k: to_f64(v) for k, v in g.items()}
+    ref, ref_idx = oracle.dsa_prefill(f["q"], f["kv"], f["q_idx"], f["k_idx"], f["w"], topk, SCALE)
+    assert np.array_equal(np.sort(idx.cpu().numpy(), axis=1), np.sort(ref_idx, axis=1))
+    assert_close(host_f64(out), ref, TOL_BF16, "gated dsa_prefill")
