@@ -99,25 +99,33 @@ def indexer_workspace_bytes(L, N, topk, block=4096, Hi=32, Di=128):
 
 
 def dsa_indexer_topk(q_idx, k_idx, w, topk, *, block=4096, return_scores=False, out=None, workspace=None):
-    """Exact indexer top-k. q_idx [L,32,128] bf16, k_idx [N,128] bf16, w [L,32] fp32.
+    """Exact indexer top-k. q_idx [L,32,128] bf16, k_idx [N,128] bf16, w [L,32] fp32
+    (or with a leading batch dimension B on all three).
 
-    Returns idx [L,topk] int32 (ascending key order, -1 padded), and the fp32
-    scores of the returned keys when return_scores is set. `workspace` (a uint8
-    device tensor of at least indexer_workspace_bytes) avoids a per-call allocation.
+    Returns idx [L,topk] (or [B,L,topk]) int32 (ascending key order, -1 padded), and
+    the fp32 scores of the returned keys when return_scores is set. `workspace` (a
+    uint8 device tensor of at least indexer_workspace_bytes, which does not depend on
+    B) avoids a per-call allocation.
     """
-    _need(q_idx, "q_idx", torch.bfloat16, 3)
-    _need(k_idx, "k_idx", torch.bfloat16, 2)
-    _need(w, "w", torch.float32, 2)
-    L, Hi, Di = q_idx.shape
-    N = k_idx.shape[0]
-    if k_idx.shape[1] != Di or w.shape != (L, Hi):
-        raise ValueError("shapes must be q_idx [L,Hi,Di], k_idx [N,Di], w [L,Hi]")
+    batched = q_idx.dim() == 4
+    if not batched:
+        q_idx, k_idx, w = q_idx[None], k_idx[None], w[None]
+    _need(q_idx, "q_idx", torch.bfloat16, 4)
+    _need(k_idx, "k_idx", torch.bfloat16, 3)
+    _need(w, "w", torch.float32, 3)
+    B, L, Hi, Di = q_idx.shape
+    N = k_idx.shape[1]
+    if k_idx.shape[0] != B or k_idx.shape[2] != Di or w.shape != (B, L, Hi):
+        raise ValueError("shapes must be q_idx [B,L,Hi,Di], k_idx [B,N,Di], w [B,L,Hi]")
     dev = q_idx.device
-    idx = out if out is not None else torch.empty((L, topk), dtype=torch.int32, device=dev)
-    scores = torch.empty((L, topk), dtype=torch.float32, device=dev) if return_scores else None
+    if out is not None:
+        idx = out if batched else out[None]
+    else:
+        idx = torch.empty((B, L, topk), dtype=torch.int32, device=dev)
+    scores = torch.empty((B, L, topk), dtype=torch.float32, device=dev) if return_scores else None
 
     def call(ws, ws_bytes):
-        return lib().dsa_indexer_topk(1, L, N, Hi, Di, _ptr(q_idx), _ptr(k_idx), _ptr(w), int(topk), int(block),
+        return lib().dsa_indexer_topk(B, L, N, Hi, Di, _ptr(q_idx), _ptr(k_idx), _ptr(w), int(topk), int(block),
                                       _ptr(idx), _ptr(scores), ws, ws_bytes, _stream(dev))
 
     if workspace is not None:
@@ -126,28 +134,36 @@ def dsa_indexer_topk(q_idx, k_idx, w, topk, *, block=4096, return_scores=False, 
     else:
         ws, size = _workspace(call, dev)
     check(call(_ptr(ws), None if size is None else ctypes.byref(size)), "dsa_indexer_topk")
+    if not batched:
+        idx = idx[0]
+        scores = scores[0] if scores is not None else None
     return (idx, scores) if return_scores else idx
 
 
 def mla_prefill_sparse(q, kv, idx, *, scale=None, query_block=1024, out=None):
-    """Sparse absorbed prefill. q [L,H,576] bf16, kv [N,576] bf16, idx [L,topk] int32 -> out [L,H,512] bf16."""
-    _need(q, "q", torch.bfloat16, 3)
-    _need(kv, "kv", torch.bfloat16, 2)
-    _need(idx, "idx", torch.int32, 2)
-    L, H, D = q.shape
-    N = kv.shape[0]
-    if D != 576 or kv.shape[1] != 576 or idx.shape[0] != L:
-        raise ValueError("shapes must be q [L,H,576], kv [N,576], idx [L,topk]")
+    """Sparse absorbed prefill. q [L,H,576] bf16, kv [N,576] bf16, idx [L,topk] int32
+    -> out [L,H,512] bf16 (or all with a leading batch dimension B)."""
+    batched = q.dim() == 4
+    if not batched:
+        q, kv, idx = q[None], kv[None], idx[None]
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv, "kv", torch.bfloat16, 3)
+    _need(idx, "idx", torch.int32, 3)
+    B, L, H, D = q.shape
+    N = kv.shape[1]
+    if D != 576 or kv.shape[0] != B or kv.shape[2] != 576 or idx.shape[:2] != (B, L):
+        raise ValueError("shapes must be q [B,L,H,576], kv [B,N,576], idx [B,L,topk]")
     if scale is None:
         scale = 1.0 / math.sqrt(576)
     if out is None:
-        out = torch.empty((L, H, 512), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((B, L, H, 512), dtype=torch.bfloat16, device=q.device)
     else:
-        _need(out, "out", torch.bfloat16, 3)
-    st = lib().mla_prefill_sparse(1, L, N, H, _ptr(q), _ptr(kv), _ptr(idx), idx.shape[1], float(scale),
+        out = out if batched else out[None]
+        _need(out, "out", torch.bfloat16, 4)
+    st = lib().mla_prefill_sparse(B, L, N, H, _ptr(q), _ptr(kv), _ptr(idx), idx.shape[2], float(scale),
                                   int(query_block), _ptr(out), None, None, _stream(q.device))
     check(st, "mla_prefill_sparse")
-    return out
+    return out if batched else out[0]
 
 
 def masked_workspace_bytes(B: int, L: int, N: int) -> int:
@@ -194,22 +210,26 @@ def mla_prefill_masked(q, kv, idx, *, scale=None, out=None, workspace=None):
 
 
 def use_sparse(sparse_prefill: bool, B: int, L: int, N: int,
-               min_context: int = SPARSE_PREFILL_MIN_CONTEXT_DEFAULT) -> bool:
+               min_context: int = SPARSE_PREFILL_MIN_CONTEXT_DEFAULT, batched: bool = False) -> bool:
     """The gate ("Sparse prefill for GLM", section "When it runs"): sparse only when switched
-    on, for one sequence, in prefill (L > 1), once the cache holds min_context positions."""
-    return bool(sparse_prefill) and B == 1 and L > 1 and N >= min_context
+    on, for one sequence, in prefill (L > 1), once the cache holds min_context positions.
+    batched=True drops the one-sequence clause (the sparse calls here take B >= 1; the
+    pages list batches as a limit of their implementation, "Limits and what to do")."""
+    return bool(sparse_prefill) and (B == 1 or (batched and B >= 1)) and L > 1 and N >= min_context
 
 
 def dsa_prefill(q, kv, q_idx, k_idx, w, topk, *, scale=None, block=4096, query_block=1024,
-                sparse_prefill=SPARSE_PREFILL_DEFAULT, min_context=SPARSE_PREFILL_MIN_CONTEXT_DEFAULT):
-    """One chunk of DSA prefill for one sequence: indexer top-k, then gated attention.
+                sparse_prefill=SPARSE_PREFILL_DEFAULT, min_context=SPARSE_PREFILL_MIN_CONTEXT_DEFAULT,
+                batched_sparse=False):
+    """One chunk of DSA prefill: indexer top-k, then gated attention.
 
-    q [L,H,576], kv [N,576] (N includes this chunk), q_idx [L,32,128], k_idx [N,128], w [L,32].
-    Returns (out [L,H,512], idx [L,topk]).
+    q [L,H,576], kv [N,576] (N includes this chunk), q_idx [L,32,128], k_idx [N,128], w [L,32],
+    or all with a leading batch dimension B. Returns (out [..,L,H,512], idx [..,L,topk]).
     """
-    L, N = q.shape[0], kv.shape[0]
+    B = q.shape[0] if q.dim() == 4 else 1
+    L, N = q.shape[-3], kv.shape[-2]
     idx = dsa_indexer_topk(q_idx, k_idx, w, topk, block=block)
-    if use_sparse(sparse_prefill, 1, L, N, min_context):
+    if use_sparse(sparse_prefill, B, L, N, min_context, batched=batched_sparse):
         return mla_prefill_sparse(q, kv, idx, scale=scale, query_block=query_block), idx
     # below the gate: the dense path over every visible key under the top-k selection
     return mla_prefill_masked(q, kv, idx, scale=scale), idx

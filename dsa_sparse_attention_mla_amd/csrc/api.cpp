@@ -118,15 +118,22 @@ int dsa_indexer_topk(int B, int L, int N, int Hi, int Di, const void* q_idx, con
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned4(w) || !aligned4(idx_out) ||
       (score_out != nullptr && !aligned4(score_out)))
     return DSA_MLA_INVALID_ARG;
-  if (B != 1 || Hi != 32 || Di != 128 || topk > 2560) return DSA_MLA_UNSUPPORTED;
+  if (Hi != 32 || Di != 128 || topk > 2560) return DSA_MLA_UNSUPPORTED;
   const dsa::IndexerPlan pl = dsa::indexer_plan(L, N, topk, block);
   const int wsr = workspace_step(pl.ws_bytes, ws, ws_bytes);
   if (wsr >= 0) return wsr;
-  if (L == 0) return DSA_MLA_OK;
+  if (B == 0 || L == 0) return DSA_MLA_OK;
   const int a = check_arch();
   if (a != DSA_MLA_OK) return a;
-  return hip_status(dsa::launch_indexer(pl, (const uint16_t*)q_idx, (const uint16_t*)k_idx, w, L, N, topk, idx_out,
-                                        score_out, ws, (hipStream_t)stream));
+  // batch entries run one after another on the stream, sharing the workspace
+  for (int b = 0; b < B; ++b) {
+    const hipError_t e = dsa::launch_indexer(
+        pl, (const uint16_t*)q_idx + (size_t)b * L * Hi * Di, (const uint16_t*)k_idx + (size_t)b * N * Di,
+        w + (size_t)b * L * Hi, L, N, topk, idx_out + (size_t)b * L * topk,
+        score_out ? score_out + (size_t)b * L * topk : nullptr, ws, (hipStream_t)stream);
+    if (e != hipSuccess) return DSA_MLA_HIP;
+  }
+  return DSA_MLA_OK;
 }
 
 int mla_prefill_sparse(int B, int L, int N, int H, const void* q, const void* kv, const int32_t* idx, int topk,
@@ -136,16 +143,16 @@ int mla_prefill_sparse(int B, int L, int N, int H, const void* q, const void* kv
   if (!std::isfinite(scale)) return DSA_MLA_INVALID_ARG;
   if (q == nullptr || kv == nullptr || idx == nullptr || out == nullptr) return DSA_MLA_INVALID_ARG;
   if (!aligned16(q) || !aligned16(kv) || !aligned4(idx) || !aligned16(out)) return DSA_MLA_INVALID_ARG;
-  if (B != 1 || H % 16 != 0) return DSA_MLA_UNSUPPORTED;
+  if (H % 16 != 0) return DSA_MLA_UNSUPPORTED;
   const int wsr = workspace_step(0, ws, ws_bytes);
   if (wsr >= 0) return wsr;
-  if (L == 0) return DSA_MLA_OK;
+  if (B == 0 || L == 0) return DSA_MLA_OK;
   const int a = check_arch();
   if (a != DSA_MLA_OK) return a;
   for (int q0 = 0; q0 < L; q0 += query_block) {
     const int nq = L - q0 < query_block ? L - q0 : query_block;
     const hipError_t e = dsa::launch_absorbed_attn(1, (const uint16_t*)q, (const uint16_t*)kv, idx, nullptr, (uint16_t*)out,
-                                                   1, L, N, H, topk, q0, nq, 0, scale, (hipStream_t)stream);
+                                                   B, L, N, H, topk, q0, nq, 0, scale, (hipStream_t)stream);
     if (e != hipSuccess) return DSA_MLA_HIP;
   }
   return DSA_MLA_OK;

@@ -93,19 +93,20 @@ int mla_prefill_dense(int mode, int dtype, int B, int L, int N, int H,
  * "Blocked top-k": keys are scored a block at a time and folded into a running
  * top-k list; the full batch x heads x L x N score tensor is never built).
  *
- *   s[i,n] = sum_h w[i,h] * ReLU(q_idx[i,h,:] . k_idx[n,:])     for n <= N - L + i
- *   q_idx [L,Hi,Di] bf16   k_idx [N,Di] bf16   w [L,Hi] fp32   idx_out [L,topk] int32
+ *   s[b,i,n] = sum_h w[b,i,h] * ReLU(q_idx[b,i,h,:] . k_idx[b,n,:])     for n <= N - L + i
+ *   q_idx [B,L,Hi,Di] bf16   k_idx [B,N,Di] bf16   w [B,L,Hi] fp32   idx_out [B,L,topk] int32
  *
  * The result is the EXACT top-k set of the canonical score (dot products in
  * fp64 summed over dims in ascending order, head terms added in ascending head
  * order, every operation separately rounded), ties to the lower key index.
  * Rows are written in ascending key order; a row with fewer than topk visible
- * keys holds all of them followed by -1. score_out (nullable) [L,topk] fp32
+ * keys holds all of them followed by -1. score_out (nullable) [B,L,topk] fp32
  * receives the fp32 MFMA score of each returned key (-inf on padding).
  * `block` (>= 1; the pages use 4096) is the folding granularity of the key
  * sweep and never changes the result.
- * Supported: B == 1, Hi == 32, Di == 128, 1 <= topk <= 2560, 0 <= L <= N.
- * Needs workspace (query its size first).
+ * Supported: B >= 1 (batch entries run one after another and share the
+ * workspace), Hi == 32, Di == 128, 1 <= topk <= 2560, 0 <= L <= N.
+ * Needs workspace (query its size first; it does not depend on B).
  */
 int dsa_indexer_topk(int B, int L, int N, int Hi, int Di, const void* q_idx, const void* k_idx, const float* w,
                      int topk, int block, int32_t* idx_out, float* score_out, void* ws, size_t* ws_bytes,
@@ -117,15 +118,16 @@ int dsa_indexer_topk(int B, int L, int N, int Hi, int Di, const void* q_idx, con
  * gathered, all heads share the gathered block, attention runs in absorbed
  * latent space; chunks longer than the query block are split into blocks).
  *
- *   score[i,h,t] = scale * q[i,h,:] . kv[idx[i,t],:]   over t with idx[i,t] valid
- *   out[i,h,:]   = softmax_t(score) . kv[idx[i,t], 0:512]
- *   q [L,H,576] bf16   kv [N,576] bf16   idx [L,topk] int32   out [L,H,512] bf16
+ *   score[b,i,h,t] = scale * q[b,i,h,:] . kv[b,idx[b,i,t],:]   over t with idx[b,i,t] valid
+ *   out[b,i,h,:]   = softmax_t(score) . kv[b,idx[b,i,t], 0:512]
+ *   q [B,L,H,576] bf16   kv [B,N,576] bf16   idx [B,L,topk] int32   out [B,L,H,512] bf16
  *
  * Index entries outside [0, N) (-1 in particular) are skipped; a row with no
  * valid entry gets zeros. Indices are not re-masked for causality. A repeated
  * index counts once per occurrence. query_block (1..1024) splits the L queries
  * into launches of at most that many; the output does not depend on it.
- * Supported: B == 1, H a multiple of 16. No workspace.
+ * Supported: B >= 1 (the pages' limit of one sequence, section "Limits and what
+ * to do", is lifted here), H a multiple of 16. No workspace.
  */
 int mla_prefill_sparse(int B, int L, int N, int H, const void* q, const void* kv, const int32_t* idx, int topk,
                        float scale, int query_block, void* out, void* ws, size_t* ws_bytes, void* stream);

@@ -67,7 +67,7 @@ def test_dense_validation(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(B=2), _lib.UNSUPPORTED), (dict(Hi=16), _lib.UNSUPPORTED), (dict(Di=64), _lib.UNSUPPORTED),
+    (dict(B=2), _lib.WORKSPACE), (dict(Hi=16), _lib.UNSUPPORTED), (dict(Di=64), _lib.UNSUPPORTED),
     (dict(topk=4096), _lib.UNSUPPORTED), (dict(topk=0), _lib.INVALID_ARG), (dict(block=0), _lib.INVALID_ARG),
     (dict(L=65, N=64), _lib.INVALID_ARG), (dict(N=0), _lib.INVALID_ARG), (dict(w=None), _lib.INVALID_ARG),
     (dict(idx=None), _lib.INVALID_ARG), (dict(q=MIS), _lib.INVALID_ARG),
@@ -89,7 +89,7 @@ def test_indexer_workspace_query_and_size_check():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(B=2), _lib.UNSUPPORTED), (dict(H=24), _lib.UNSUPPORTED), (dict(qb=0), _lib.INVALID_ARG),
+    (dict(B=2), _lib.ARCH), (dict(H=24), _lib.UNSUPPORTED), (dict(qb=0), _lib.INVALID_ARG),
     (dict(qb=1025), _lib.INVALID_ARG), (dict(topk=0), _lib.INVALID_ARG), (dict(idx=None), _lib.INVALID_ARG),
     (dict(out=MIS), _lib.INVALID_ARG), (dict(scale=float("nan")), _lib.INVALID_ARG),
     (dict(), _lib.ARCH), (dict(L=0), _lib.OK),
@@ -115,6 +115,8 @@ def test_gate_helper_matches_predicate():
     assert dm.use_sparse(True, 1, 512, 16384)
     assert not dm.use_sparse(True, 1, 512, 16383)
     assert not dm.use_sparse(True, 2, 512, 131072)
+    assert dm.use_sparse(True, 2, 512, 131072, batched=True)        # the one-sequence clause, lifted
+    assert not dm.use_sparse(True, 2, 1, 131072, batched=True)
     assert not dm.use_sparse(True, 1, 1, 131072)
     assert not dm.use_sparse(False, 1, 512, 131072)
 

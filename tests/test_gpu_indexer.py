@@ -134,3 +134,18 @@ def test_indexer_repeatable_and_inputs_unchanged():
     assert torch.equal(a, out)
     for x, y in zip(snap, (q, k, w)):
         assert torch.equal(x, y)
+
+
+def test_indexer_batched_equals_per_entry():
+    """B = 2: each batch entry's sets equal its own single-sequence call and the oracle."""
+    gs = [gen_indexer(150 + b, 12, 3000) for b in range(2)]
+    q = torch.stack([dev(g["q_idx"]) for g in gs])
+    k = torch.stack([dev(g["k_idx"]) for g in gs])
+    w = torch.stack([dev(g["w"]) for g in gs])
+    idx = dm.dsa_indexer_topk(q, k, w, 256)
+    one = dm.dsa_indexer_topk(q[1], k[1], w[1], 256)
+    torch.cuda.synchronize()
+    assert torch.equal(idx[1], one)
+    for b, g in enumerate(gs):
+        s = oracle.indexer_scores(to_f64(g["q_idx"]), to_f64(g["k_idx"]), to_f64(g["w"]))
+        _check_rows(idx[b].cpu().numpy(), oracle.topk_full(s, 256), np.arange(12), f"batched indexer entry {b}")

@@ -173,3 +173,29 @@ def test_dsa_prefill_gated_uses_masked_dense():
     ref, ref_idx = oracle.dsa_prefill(f["q"], f["kv"], f["q_idx"], f["k_idx"], f["w"], topk, SCALE)
     assert np.array_equal(np.sort(idx.cpu().numpy(), axis=1), np.sort(ref_idx, axis=1))
     assert_close(host_f64(out), ref, TOL_BF16, "gated dsa_prefill")
+
+
+def test_sparse_batched_and_batched_prefill():
+    """B = 2 sparse attention equals per-entry calls; dsa_prefill on a batch takes the
+    masked path by default (the gate's one-sequence clause) and the sparse path with
+    batched_sparse=True, both matching the oracle per entry."""
+    from synth import gen_dsa_prefill
+    L, N, topk = 16, 3000, 64
+    gs = [gen_dsa_prefill(160 + b, L, N, H=64) for b in range(2)]
+    t = {k: torch.stack([dev(g[k]) for g in gs]) for k in gs[0]}
+    idx = dm.dsa_indexer_topk(t["q_idx"], t["k_idx"], t["w"], topk)
+    out = dm.mla_prefill_sparse(t["q"], t["kv"], idx)
+    one = dm.mla_prefill_sparse(t["q"][1], t["kv"][1], idx[1])
+    torch.cuda.synchronize()
+    assert torch.equal(out[1], one)
+    out_m, _ = dm.dsa_prefill(t["q"], t["kv"], t["q_idx"], t["k_idx"], t["w"], topk, min_context=1000)
+    out_s, idx_s = dm.dsa_prefill(t["q"], t["kv"], t["q_idx"], t["k_idx"], t["w"], topk, min_context=1000,
+                                  batched_sparse=True)
+    torch.cuda.synchronize()
+    for b, g in enumerate(gs):
+        f = {k: to_f64(v) for k, v in g.items()}
+        ref, ref_idx = oracle.dsa_prefill(f["q"], f["kv"], f["q_idx"], f["k_idx"], f["w"], topk, SCALE,
+                                          min_context=1000)
+        assert np.array_equal(np.sort(idx_s[b].cpu().numpy(), axis=1), np.sort(ref_idx, axis=1))
+        assert_close(host_f64(out_s[b]), ref, TOL_BF16, f"batched sparse prefill entry {b}")
+        assert_close(host_f64(out_m[b]), ref, TOL_BF16, f"batched masked prefill entry {b}")
