@@ -17,14 +17,18 @@ definition. Sources, cited by page and section:
   (joined 576-wide latent+rope row, gather of the chosen rows, absorbed
   attention) -> ``attention.mla_absorbed`` / ``attention.mla_sparse_gather``;
   section "The dense mask" -> ``attention.mla_masked_dense``; section "Blocked
-  top-k" -> ``indexer.topk_blocked``; section "When it runs" -> ``gate``.
+  top-k" -> ``indexer.topk_blocked``; section "When it runs" -> ``gate`` and
+  the decode step ``attention.mla_decode_paged``.
+* Fornax part 5, section "Paged KV: alignment follows the tile" (rows addressed
+  one at a time through the page table) -> ``attention.paged_rows``.
 
 Every function has at least one pin in tests/test_oracle_*.py that does not go
 through the function's own formula (brute force, closed forms, identities
 with library routines, invariants).
 """
 from .attention import (  # noqa: F401
-    visible_mask, mla_nonabsorbed, mla_absorbed, mla_masked_dense, mla_sparse_gather,
+    visible_mask, mla_nonabsorbed, mla_absorbed, mla_masked_dense, mla_sparse_gather, paged_rows,
+    mla_decode_paged,
 )
 from .indexer import indexer_scores, topk_full, topk_blocked, exact_dot_flags  # noqa: F401
 from .gate import use_sparse, dsa_prefill  # noqa: F401

@@ -132,3 +132,37 @@ def mla_sparse_gather(q, kv, idx, scale, dv=512, rows=None):
         p = _softmax_rows(s, np.ones_like(s, dtype=bool))
         out[r] = p @ g[:, :dv]
     return out
+
+
+def paged_rows(kv_pages, page_table, seq_len):
+    """The contiguous cache of one sequence rebuilt from a paged one: row n of the
+    sequence is row n % page_size of page page_table[n // page_size] ("Apple M3 vs M5
+    kernels", section "Paged KV: alignment follows the tile": every row is addressed
+    on its own through the page pointers, so no tile has to sit inside one page).
+
+    kv_pages [P,page_size,D], page_table [max_pages] int, seq_len int -> [seq_len,D].
+    """
+    page_size = kv_pages.shape[1]
+    n = np.arange(seq_len)
+    return kv_pages[np.asarray(page_table)[n // page_size], n % page_size]
+
+
+def mla_decode_paged(q, kv_pages, page_table, seq_lens, scale, dv=512):
+    """One decode step of absorbed MLA over a paged joined cache.
+
+    "Sparse prefill for GLM", section "When it runs": decode (one new query per
+    sequence) keeps the dense absorbed path; the new token's key is already in the
+    cache, so the query sits at the last of seq_len positions and sees all of them.
+
+    q [B,H,576], kv_pages [P,page_size,576], page_table [B,max_pages], seq_lens [B].
+    A sequence of length 0 gets zeros. Returns out [B,H,dv].
+    """
+    B, H, _ = q.shape
+    out = np.zeros((B, H, dv))
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        kv = paged_rows(kv_pages, page_table[b], n)
+        out[b] = mla_absorbed(q[b][None], kv, scale, dv)[0]
+    return out

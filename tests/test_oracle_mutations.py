@@ -11,6 +11,7 @@ import oracle
 from oracle.attention import _softmax_rows, visible_mask
 
 import test_oracle_attention as A
+import test_oracle_decode as DEC
 import test_oracle_indexer as I
 import test_oracle_sparse as S
 
@@ -138,6 +139,30 @@ def test_score_mutants_caught(mutant, rng):
     assert not I.pin_fraction_brute(mutant, rng)
 
 
+def paged_rows_swapped(kv_pages, page_table, seq_len):
+    page_size = kv_pages.shape[1]
+    n = np.arange(seq_len)
+    return kv_pages[np.asarray(page_table)[n % page_size], n // page_size]
+
+
+def paged_rows_by_slot(kv_pages, page_table, seq_len):
+    n = np.arange(seq_len)                        # ignores the table: physical order
+    return kv_pages.reshape(-1, kv_pages.shape[2])[n]
+
+
+def decode_drops_newest_key(q, kv_pages, page_table, seq_lens, scale, dv=512):
+    return oracle.mla_decode_paged(q, kv_pages, page_table, [max(0, int(n) - 1) for n in seq_lens], scale, dv)
+
+
+@pytest.mark.parametrize("mutant", [paged_rows_swapped, paged_rows_by_slot])
+def test_paged_rows_mutants_caught(mutant):
+    assert not DEC.pin_paged_rows_hand(mutant)
+
+
+def test_decode_mutant_caught(rng):
+    assert not DEC.pin_decode_brute(decode_drops_newest_key, rng)
+
+
 def test_real_oracle_passes_every_pin(rng):
     assert A.pin_nonabs_golden(oracle.mla_nonabsorbed)
     assert A.pin_nonabs_vs_sdpa(oracle.mla_nonabsorbed, rng)
@@ -146,3 +171,5 @@ def test_real_oracle_passes_every_pin(rng):
     assert S.pin_sparse_equals_masked_dense(oracle.mla_sparse_gather, rng, pad=0.3)
     assert I.pin_topk_subsets(oracle.topk_full, rng)
     assert I.pin_golden(oracle.indexer_scores, oracle.topk_full)
+    assert DEC.pin_paged_rows_hand(oracle.paged_rows)
+    assert DEC.pin_decode_brute(oracle.mla_decode_paged, rng)
