@@ -158,6 +158,24 @@ def dense_configs(dm, torch, reps=10):
     return res
 
 
+def decode_config(dm, torch, B=8, n=131072, page_size=64, reps=10):
+    """One decode step (L = 1, 64 heads) for B sequences of n keys each, over a paged
+    joined cache with shuffled page placement. HBM-bound: the step reads every row once."""
+    g = torch.Generator(device="cpu").manual_seed(SEED)
+    npg = (n + page_size - 1) // page_size
+    pages = torch.randn((B * npg, page_size, 576), generator=g).to(torch.bfloat16).cuda()
+    q = torch.randn((B, H, 576), generator=g).to(torch.bfloat16).cuda()
+    table = torch.randperm(B * npg, generator=g).to(torch.int32).view(B, npg).cuda()
+    lens = torch.full((B,), n, dtype=torch.int32).cuda()
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(dm.decode_workspace_bytes(B, H, B * npg, page_size, npg), dtype=torch.uint8, device="cuda")
+    ms = _time(lambda: dm.mla_decode_paged(q, pages, table, lens, out=out, workspace=ws), torch, reps)
+    by = B * n * 1152 + B * H * 576 * 2 + B * H * 512 * 2 + B * npg * 4
+    return {"workload": f"decode step, {B} sequences x {n} keys, {H} heads, pages of {page_size} rows",
+            "ms": ms, "GB_s": by / ms / 1e6, "frac_hbm": by / ms / 1e6 / PEAK_HBM_GBS,
+            "tflops": B * n * H * 2176 / ms / 1e9}
+
+
 def masked_baseline(dm, torch, q, kv, idx, t_sparse_ms, step_ms, reps=3):
     """The path the sparse call replaces, on the same chunk: dense absorbed attention over
     every visible key under the same top-k selection ("Sparse prefill for GLM", "The dense
@@ -304,6 +322,8 @@ def main():
         other = dense_configs(dm, torch)
         log("bench: masked dense baseline")
         baseline = masked_baseline(dm, torch, q, kv, idx, t_att, ms_per_step)
+        log("bench: paged decode")
+        other["paged_decode_B8_N131072_H64"] = decode_config(dm, torch)
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")

@@ -209,6 +209,47 @@ def mla_prefill_masked(q, kv, idx, *, scale=None, out=None, workspace=None):
     return out if batched else out[0]
 
 
+def decode_workspace_bytes(B: int, H: int, num_pages: int, page_size: int, max_pages: int) -> int:
+    """Workspace of mla_decode_paged (row lists and split partials)."""
+    n = ctypes.c_size_t(0)
+    p = ctypes.c_void_p(256)                # placeholder pointers: a size query reads nothing
+    check(lib().mla_decode_paged(B, H, num_pages, page_size, max_pages, p, p, p, p, 1.0, p, None, ctypes.byref(n),
+                                 None), "mla_decode_paged (workspace query)")
+    return n.value
+
+
+def mla_decode_paged(q, kv_pages, page_table, seq_lens, *, scale=None, out=None, workspace=None):
+    """One decode step over a paged joined cache.
+
+    q [B,H,576] bf16, kv_pages [num_pages,page_size,576] bf16, page_table [B,max_pages]
+    int32, seq_lens [B] int32 -> out [B,H,512] bf16.
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_pages, "kv_pages", torch.bfloat16, 3)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, H, D = q.shape
+    P, ps, D2 = kv_pages.shape
+    if D != 576 or D2 != 576 or page_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("shapes must be q [B,H,576], kv_pages [P,page_size,576], page_table [B,max_pages], "
+                         "seq_lens [B]")
+    maxp = page_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(576)
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
+    else:
+        _need(out, "out", torch.bfloat16, 3)
+    nbytes = decode_workspace_bytes(B, H, P, ps, maxp)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    st = lib().mla_decode_paged(B, H, P, ps, maxp, _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
+                                float(scale), _ptr(out), _ptr(workspace), ctypes.byref(n), _stream(q.device))
+    check(st, "mla_decode_paged")
+    return out
+
+
 def use_sparse(sparse_prefill: bool, B: int, L: int, N: int,
                min_context: int = SPARSE_PREFILL_MIN_CONTEXT_DEFAULT, batched: bool = False) -> bool:
     """The gate ("Sparse prefill for GLM", section "When it runs"): sparse only when switched

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -178,6 +179,38 @@ int mla_prefill_masked(int B, int L, int N, int H, const void* q, const void* kv
   e = dsa::launch_absorbed_attn(2, (const uint16_t*)q, (const uint16_t*)kv, idx, mask, (uint16_t*)out, B, L, N, H,
                                 topk, 0, L, 1, scale, (hipStream_t)stream);
   return hip_status(e);
+}
+
+int mla_decode_paged(int B, int H, int num_pages, int page_size, int max_pages, const void* q, const void* kv_pages,
+                     const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, void* ws,
+                     size_t* ws_bytes, void* stream) {
+  if (B < 0 || H < 1 || num_pages < 1 || page_size < 1 || max_pages < 1) return DSA_MLA_INVALID_ARG;
+  if ((long long)num_pages * page_size > INT32_MAX || (long long)max_pages * page_size > INT32_MAX)
+    return DSA_MLA_INVALID_ARG;
+  if (!std::isfinite(scale)) return DSA_MLA_INVALID_ARG;
+  if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
+    return DSA_MLA_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_pages) || !aligned4(page_table) || !aligned4(seq_lens) || !aligned16(out))
+    return DSA_MLA_INVALID_ARG;
+  if (H % 16 != 0) return DSA_MLA_UNSUPPORTED;
+  const int maxlen = max_pages * page_size;
+  // split length: a multiple of 32 keys, 256 .. 4096, aiming at about 512 workgroups
+  long long spl = ((long long)B * maxlen + 511) / 512;
+  spl = (spl + 31) / 32 * 32;
+  spl = spl < 256 ? 256 : (spl > 4096 ? 4096 : spl);
+  const int nsplit = (int)((maxlen + spl - 1) / spl);
+  const size_t rows_bytes = ((size_t)B * maxlen * 4 + 255) / 256 * 256;
+  const size_t part_bytes = (size_t)B * nsplit * H * (512 + 2) * 4;
+  const int wsr = workspace_step(rows_bytes + part_bytes, ws, ws_bytes);
+  if (wsr >= 0) return wsr;
+  if (B == 0) return DSA_MLA_OK;
+  const int a = check_arch();
+  if (a != DSA_MLA_OK) return a;
+  int32_t* rows = (int32_t*)ws;
+  float* part = (float*)((unsigned char*)ws + rows_bytes);
+  return hip_status(dsa::launch_paged_decode((const uint16_t*)q, (const uint16_t*)kv_pages, page_table, seq_lens, B,
+                                             H, num_pages, page_size, max_pages, (int)spl, nsplit, rows, part,
+                                             (uint16_t*)out, scale, (hipStream_t)stream));
 }
 
 }  // extern "C"

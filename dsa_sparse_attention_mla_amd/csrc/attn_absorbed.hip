@@ -60,13 +60,15 @@ constexpr size_t LDS_BYTES = 2 * (size_t)STAGE + SEG * 4 + 2 * T * 4 + XCH_BYTES
 
 // MODE: 0 dense (every visible key), 1 sparse (gathered index lists), 2 masked
 // dense (every visible key, weighted only where the query's selection bitmap has
-// its bit set).
+// its bit set), 3 paged decode split (one query per sequence; workgroup x gathers
+// keys [x*spl, x*spl + spl) of the sequence's row list and writes its unnormalised
+// partial output with the running max and sum, merged afterwards).
 template <int MODE>
 __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const uint32_t* __restrict__ mask, uint16_t* __restrict__ out, int L, int N, int H, int topk, int q0, int causal,
-    float scale_log2) {
-  constexpr bool SPARSE = MODE == 1;
+    float scale_log2, const int32_t* __restrict__ seqlens, float* __restrict__ part, int spl) {
+  constexpr bool SPARSE = MODE == 1 || MODE == 3;   // rows come from an index list
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   unsigned char* ring = dyn;                                // [2][STAGE]
   int* sidx = (int*)(dyn + 2 * (size_t)STAGE);              // [SEG]
@@ -76,14 +78,19 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int b = blockIdx.y;
-  const int i = q0 + blockIdx.x;
+  const int i = MODE == 3 ? 0 : q0 + blockIdx.x;
   const int hg = wave & 3, half = wave >> 2;
   const bool wave_active = (blockIdx.z * 4 + hg) * 16 < H;
   const int head = wave_active ? (blockIdx.z * 4 + hg) * 16 + c16 : c16;
   const int p = N - L + i;
-  const int count = SPARSE ? topk : (causal ? p + 1 : N);
-  const uint16_t* kvb = kv + (size_t)b * N * D;
-  const int32_t* irow = SPARSE ? idx + ((size_t)b * L + i) * topk : nullptr;
+  int count = MODE == 1 ? topk : (causal ? p + 1 : N);
+  // (topk is the row-list length here; a sequence length past it is clamped to it)
+  if constexpr (MODE == 3) count = max(0, min(spl, min(seqlens[b], topk) - (int)blockIdx.x * spl));
+  // paged decode: rows are physical rows of the page pool (N of them), shared by all sequences
+  const uint16_t* kvb = kv + (MODE == 3 ? (size_t)0 : (size_t)b * N * D);
+  const int32_t* irow = MODE == 1   ? idx + ((size_t)b * L + i) * topk
+                        : MODE == 3 ? idx + (size_t)b * topk + (size_t)blockIdx.x * spl
+                                    : nullptr;
   const uint32_t* mrow = MODE == 2 ? mask + ((size_t)b * L + i) * ((N + 31) / 32) : nullptr;
 
   bf16x8 qf[KCH];
@@ -244,6 +251,18 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   }
 
   if (!wave_active) return;
+  if constexpr (MODE == 3) {
+    // partial record of (sequence b, split x, head): 512 unnormalised output values,
+    // then the running max (log2 units) and sum
+    float* rec = part + (((size_t)b * gridDim.x + blockIdx.x) * H + head) * (DV + 2);
+#pragma unroll
+    for (int db = 0; db < NDBH; ++db) *(f32x4*)(rec + 256 * half + 16 * db + 4 * g) = o[db];
+    if (half == 0 && g == 0) {
+      rec[DV] = m;
+      rec[DV + 1] = lsum;
+    }
+    return;
+  }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   uint16_t* orow = out + (((size_t)b * L + i) * H + head) * DV + 256 * half + 4 * g;
 #pragma unroll
@@ -279,6 +298,74 @@ __global__ __launch_bounds__(256) void mask_rows_kernel(const int32_t* __restric
   }
 }
 
+// Row list of each sequence of a paged cache: entry n < seq_len is the physical row
+// page_table[b][n / page_size] * page_size + n % page_size (rows addressed one at a
+// time, so a tile never has to sit inside one page); -1 past the sequence, for a page
+// id outside the pool, or a position past the table.
+__global__ __launch_bounds__(256) void paged_rows_kernel(const int32_t* __restrict__ page_table,
+                                                         const int32_t* __restrict__ seqlens, int max_pages,
+                                                         int page_size, int num_pages, int32_t* __restrict__ rows) {
+  const int b = blockIdx.y;
+  const int maxlen = max_pages * page_size;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= maxlen) return;
+  const int len = seqlens[b];
+  int r = -1;
+  if (n < len) {
+    const int pg = page_table[(size_t)b * max_pages + n / page_size];
+    if (pg >= 0 && pg < num_pages) r = pg * page_size + n % page_size;
+  }
+  rows[(size_t)b * maxlen + n] = r;
+}
+
+// Merge of the split partials of one (sequence, head): out = sum_x 2^(m_x - M) O_x /
+// sum_x 2^(m_x - M) l_x with M the largest split max; splits without a visible key
+// (m = -inf) contribute nothing; a sequence with none gets zeros.
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part, int nsplit, int H,
+                                                             uint16_t* __restrict__ out) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const float* base = part + ((size_t)b * nsplit * H + h) * (DV + 2);
+  const size_t stride = (size_t)H * (DV + 2);
+  float M = -INFINITY;
+  for (int x = 0; x < nsplit; ++x) M = fmaxf(M, base[x * stride + DV]);
+  float acc0 = 0.f, acc1 = 0.f, den = 0.f;
+  if (M != -INFINITY) {
+    for (int x = 0; x < nsplit; ++x) {
+      const float* rec = base + x * stride;
+      const float mx = rec[DV];
+      const float wgt = mx == -INFINITY ? 0.f : exp2_fast(mx - M);
+      den += wgt * rec[DV + 1];
+      acc0 += wgt * rec[2 * tid];
+      acc1 += wgt * rec[2 * tid + 1];
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {acc0 * inv, acc1 * inv};
+  *(bf16x2*)(out + ((size_t)b * H + h) * DV + 2 * tid) = __builtin_convertvector(v, bf16x2);
+}
+
+hipError_t launch_paged_decode(const uint16_t* q, const uint16_t* kv_pages, const int32_t* page_table,
+                               const int32_t* seqlens, int B, int H, int num_pages, int page_size, int max_pages,
+                               int spl, int nsplit, int32_t* rows, float* part, uint16_t* out, float scale,
+                               hipStream_t stream) {
+  const int maxlen = max_pages * page_size;
+  {
+    KernelTrace kt("paged_rows", stream);
+    hipLaunchKernelGGL(paged_rows_kernel, dim3((maxlen + 255) / 256, B), dim3(256), 0, stream, page_table, seqlens,
+                       max_pages, page_size, num_pages, rows);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_absorbed_attn(3, q, kv_pages, rows, nullptr, nullptr, B, 1, num_pages * page_size, H, maxlen, 0, nsplit,
+                           0, scale, stream, seqlens, part, spl);
+  if (e != hipSuccess) return e;
+  KernelTrace kt("decode_combine", stream);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(H, B), dim3(DV / 2), 0, stream, part, nsplit, H, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_mask_rows(const int32_t* idx, int B, int L, int N, int topk, uint32_t* mask, hipStream_t stream) {
   KernelTrace kt("mask_rows", stream);
   hipLaunchKernelGGL(mask_rows_kernel, dim3(L, B), dim3(256), 0, stream, idx, L, N, topk, mask);
@@ -289,11 +376,12 @@ hipError_t launch_mask_rows(const int32_t* idx, int B, int L, int N, int topk, u
 // a workgroup covers 64 heads (grid z walks head groups).
 hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                                 const uint32_t* mask, uint16_t* out, int B, int L, int N, int H, int topk, int q0,
-                                int nq, int causal, float scale, hipStream_t stream) {
+                                int nq, int causal, float scale, hipStream_t stream, const int32_t* seqlens,
+                                float* part, int spl) {
   static bool attr_set = false;
   if (!attr_set) {
-    const void* fns[3] = {(const void*)absorbed_attn_kernel<0>, (const void*)absorbed_attn_kernel<1>,
-                          (const void*)absorbed_attn_kernel<2>};
+    const void* fns[4] = {(const void*)absorbed_attn_kernel<0>, (const void*)absorbed_attn_kernel<1>,
+                          (const void*)absorbed_attn_kernel<2>, (const void*)absorbed_attn_kernel<3>};
     for (const void* f : fns) {
       const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
       if (e != hipSuccess) return e;
@@ -302,17 +390,18 @@ hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv,
   }
   const float scale_log2 = scale * 1.4426950408889634f;
   dim3 grid(nq, B, (H + 63) / 64), block(64 * NW);
-  static const char* names[3] = {"absorbed_dense_attn", "sparse_attn", "masked_dense_attn"};
+  static const char* names[4] = {"absorbed_dense_attn", "sparse_attn", "masked_dense_attn", "paged_decode_attn"};
   KernelTrace kt(names[mode], stream);
-  if (mode == 1)
-    hipLaunchKernelGGL((absorbed_attn_kernel<1>), grid, block, LDS_BYTES, stream, q, kv, idx, mask, out, L, N, H,
-                       topk, q0, causal, scale_log2);
-  else if (mode == 2)
-    hipLaunchKernelGGL((absorbed_attn_kernel<2>), grid, block, LDS_BYTES, stream, q, kv, idx, mask, out, L, N, H,
-                       topk, q0, causal, scale_log2);
-  else
-    hipLaunchKernelGGL((absorbed_attn_kernel<0>), grid, block, LDS_BYTES, stream, q, kv, idx, mask, out, L, N, H,
-                       topk, q0, causal, scale_log2);
+#define DSA_LAUNCH_ABS(M)                                                                                    \
+  hipLaunchKernelGGL((absorbed_attn_kernel<M>), grid, block, LDS_BYTES, stream, q, kv, idx, mask, out, L, N, H, \
+                     topk, q0, causal, scale_log2, seqlens, part, spl)
+  switch (mode) {
+    case 1: DSA_LAUNCH_ABS(1); break;
+    case 2: DSA_LAUNCH_ABS(2); break;
+    case 3: DSA_LAUNCH_ABS(3); break;
+    default: DSA_LAUNCH_ABS(0); break;
+  }
+#undef DSA_LAUNCH_ABS
   return hipGetLastError();
 }
 

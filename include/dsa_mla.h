@@ -2,12 +2,14 @@
  * dsa_mla.h -- C ABI of libdsa_mla.so: MLA prefill and DeepSeek-sparse-attention
  * (DSA) prefill on AMD Instinct MI355X (gfx950).
  *
- * Four calls:
+ * Five calls:
  *   mla_prefill_dense   dense causal MLA prefill, non-absorbed or absorbed
  *   dsa_indexer_topk    indexer scores fused with a running top-k selection
  *   mla_prefill_sparse  absorbed attention over each query's gathered top-k rows
  *   mla_prefill_masked  dense absorbed attention under each query's top-k mask
  *                       (the path the sparse call replaces; the gated case)
+ *   mla_decode_paged    one decode step (L = 1) of absorbed attention over a
+ *                       paged joined cache
  *
  * Conventions shared by all calls
  * -------------------------------
@@ -153,6 +155,31 @@ int mla_prefill_sparse(int B, int L, int N, int H, const void* q, const void* kv
  */
 int mla_prefill_masked(int B, int L, int N, int H, const void* q, const void* kv, const int32_t* idx, int topk,
                        float scale, void* out, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * mla_decode_paged -- one decode step of absorbed MLA over a paged joined cache
+ * ("Sparse prefill for GLM", section "When it runs": decode keeps the dense
+ * absorbed path, also after a sparse prefill; "Apple M3 vs M5 kernels", section
+ * "Paged KV: alignment follows the tile": every row is addressed on its own
+ * through the page table, so no tile has to sit inside one page).
+ *
+ *   row(b, n)   = kv_pages[page_table[b, n / page_size], n % page_size, :]   n < seq_lens[b]
+ *   score[b,h,n] = scale * q[b,h,:] . row(b, n)
+ *   out[b,h,:]   = softmax_n(score) . row(b, n)[0:512]
+ *   q [B,H,576] bf16   kv_pages [num_pages,page_size,576] bf16
+ *   page_table [B,max_pages] int32   seq_lens [B] int32   out [B,H,512] bf16
+ *
+ * The new token's key is already in the cache: the query sees all seq_lens[b]
+ * rows. A length past max_pages*page_size is clamped to it; a page id outside
+ * [0, num_pages) makes its rows count as absent; a sequence without rows gets
+ * zeros. The keys are split across workgroups and the partial results merged
+ * (flash-decoding style). Supported: B >= 0, H a multiple of 16. Needs
+ * workspace: the row lists (B*max_pages*page_size int32) and the split
+ * partials (query its size with ws == NULL).
+ */
+int mla_decode_paged(int B, int H, int num_pages, int page_size, int max_pages, const void* q, const void* kv_pages,
+                     const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, void* ws,
+                     size_t* ws_bytes, void* stream);
 
 /*
  * Per-kernel timing (diagnostics). dsa_mla_trace_enable(1) makes every later

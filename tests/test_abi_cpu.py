@@ -145,3 +145,30 @@ def test_masked_workspace_is_the_bitmaps():
     assert _masked(B=2, L=1024, N=131072, ws=P, ws_bytes=ctypes.byref(ok)) == _lib.ARCH
     small = ctypes.c_size_t(sz.value - 4)
     assert _masked(B=2, L=1024, N=131072, ws=P, ws_bytes=ctypes.byref(small)) == _lib.WORKSPACE
+
+
+def _decode(**kw):
+    a = dict(B=2, H=64, P=16, ps=64, maxp=8, q=P, kv=P, table=P, lens=P, scale=0.1, out=P, ws=None, ws_bytes=None,
+             stream=None)
+    a.update(kw)
+    return dm.lib().mla_decode_paged(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=24), _lib.UNSUPPORTED), (dict(ps=0), _lib.INVALID_ARG), (dict(P=0), _lib.INVALID_ARG),
+    (dict(maxp=0), _lib.INVALID_ARG), (dict(table=None), _lib.INVALID_ARG), (dict(lens=MIS), _lib.INVALID_ARG),
+    (dict(q=MIS), _lib.INVALID_ARG), (dict(scale=float("inf")), _lib.INVALID_ARG), (dict(), _lib.WORKSPACE),
+    (dict(ps=1 << 20, maxp=1 << 12), _lib.INVALID_ARG),                 # rows past int32
+])
+def test_decode_validation(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_workspace_query():
+    sz = ctypes.c_size_t(0)
+    assert _decode(ws_bytes=ctypes.byref(sz)) == _lib.OK
+    assert sz.value >= 2 * 8 * 64 * 4 + 2 * 64 * 514 * 4
+    assert dm.decode_workspace_bytes(2, 64, 16, 64, 8) == sz.value
+    ok = ctypes.c_size_t(sz.value)
+    assert _decode(ws=P, ws_bytes=ctypes.byref(ok)) == _lib.ARCH
+    assert _decode(B=0, ws=P, ws_bytes=ctypes.byref(ok)) == _lib.OK
