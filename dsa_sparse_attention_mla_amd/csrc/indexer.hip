@@ -201,10 +201,10 @@ __device__ __forceinline__ float block512_min(float x, float* red) {
 // compacting them toward its own end (a destination never passes the entry being
 // read, so the in-place moves are safe). Returns this wave's new segment count.
 // The caller guarantees that a flagged list holds at least k entries.
-template <typename Off, int CAPS>
+template <typename Off, int CAPS, int NQ = QPB>
 __device__ int pair_compact(float* cs, Off* co, int mycnt, int kh, bool mine, int k, float eps, float& thr,
                             int* hq, float* red, bool compact = true) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, partner = wave ^ QPB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, partner = wave ^ NQ;
   auto seg = [&](int e) { return kh == 0 ? e : CAPS - 1 - e; };
   if (mine) {
     float mx = -INFINITY, mn = INFINITY;
@@ -526,18 +526,33 @@ __global__ __launch_bounds__(64 * IDX_NW) void score_filter_kernel(
 // ---------------------------------------------------------------- 3b. score + filter, global lists
 // Variant of the score kernel for contexts long enough for the sampled start
 // (every query of the launch sees at least 8 * SAMPLE keys). The threshold is
-// fixed after the sampling prologue, so survivors go straight to the query's list
-// in global memory (one LDS atomic per wave and query for the positions) and no
-// list is kept on chip. That frees the LDS for two 32 KB key stages filled by
-// direct global-to-LDS loads one 128-key tile ahead, and with at most 128 VGPRs two
-// workgroups share a compute unit (four waves per SIMD). A list that would exceed
-// its capacity marks the query for the exact fallback.
+// fixed after the sampling prologue, so no list has to be kept on chip: each wave
+// stages its survivors (score, key) in a small LDS buffer and moves them to the
+// query's list in global memory when the buffer is half full (one LDS atomic per
+// flush for the positions). That frees the LDS for a ring of four key stages
+// filled by direct global-to-LDS loads three 128-key tiles ahead. Sixteen waves
+// (two per query, eight queries) share each tile, so one tile load feeds twice
+// as many MFMAs as with four queries, and with at most 128 VGPRs per wave the one
+// workgroup per compute unit still keeps four waves on every SIMD. A list that
+// would exceed its capacity marks the query for the exact fallback.
+// Stage rows are 272 bytes (a key's 256 plus 16 of padding): the 16 rows one
+// quarter of an MFMA operand read touches then start 68 banks apart and cover all
+// 64 banks, and every operand address is a per-lane base plus an immediate.
 namespace {
+constexpr int GQ = 8;                                    // queries per workgroup
+constexpr int GW = 2 * GQ;                               // waves: two per query
 constexpr int GT = 128;                                  // keys per tile
-constexpr int G_STAGE = GT * ID * 2;                     // 32 KB
-constexpr int G_DMA = G_STAGE / (IDX_NW * 64 * 16);      // 16-byte direct loads per lane per tile
-static_assert(G_DMA * IDX_NW * 64 * 16 == G_STAGE, "tile loads cover the stage");
-static_assert(SAMPLE * QPB * 4 <= G_STAGE, "sample scores fit one stage");
+constexpr int G_ROW = ID * 2 + 16;                       // LDS bytes per key row
+constexpr int G_STAGE = GT * G_ROW;                      // 34816 B
+constexpr int G_NST = 4;                                 // ring stages (G_NST - 1 tiles in flight)
+constexpr int G_LOADS = G_STAGE / 1024;                  // 1 KB direct loads per tile (one per wave instruction)
+constexpr int G_CB = 128;                                // staged survivors per wave
+static_assert(G_LOADS * 1024 == G_STAGE, "tile loads cover the stage");
+static_assert(G_LOADS > 2 * GW && G_LOADS <= 3 * GW, "every wave issues two or three loads per tile");
+static_assert(SAMPLE * GQ * 4 <= 2 * G_STAGE, "sample scores fit two stages");
+static_assert(G_NST >= 4, "the sampling prologue takes two stages for tiles and two for scores");
+static_assert(GQ * 256 <= GW * G_CB, "the prologue's histograms fit the staging buffer");
+static_assert(G_CB >= 128, "a half-full buffer still takes a whole tile of survivors");
 }  // namespace
 
 // 16-byte direct global->LDS load: lane l writes LDS bytes [m0 + 16 l, m0 + 16 l + 16).
@@ -549,27 +564,30 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
 }
 
-__global__ __launch_bounds__(64 * IDX_NW) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_list_kernel(
+__global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_list_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int span, int nsplit, int cap,
     float* __restrict__ cand_s, int* __restrict__ cand_i, int* __restrict__ cand_n, float* __restrict__ cand_t) {
-  __shared__ __attribute__((aligned(1024))) unsigned char stage[2][G_STAGE];
-  __shared__ int hist[QPB * 256];
-  __shared__ int qcnt[QPB];
-  __shared__ int qovf[QPB];
-  __shared__ float red[2 * IDX_NW];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage[G_NST * G_STAGE];
+  // staged survivors: wave v's scores (as bits) at [v G_CB, v G_CB + G_CB), its keys
+  // GW * G_CB words further; the sampling prologue keeps its histograms here
+  __shared__ __attribute__((aligned(16))) int cbuf[2 * GW * G_CB];
+  __shared__ int qcnt[GQ];
+  __shared__ int qovf[GQ];
+  __shared__ float red[2 * GW];
+  int* const hist = cbuf;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qi = wave & (QPB - 1), kh = wave / QPB;
+  const int qi = wave & (GQ - 1), kh = wave / GQ;
   const int split = blockIdx.y;
   const int n_lo = split * span;
-  const int i = blockIdx.x * QPB + qi;
+  const int i = blockIdx.x * GQ + qi;
   const bool active = i < L;
   const int ii = active ? i : L - 1;
   const int p = N - L + ii;
-  const int ilast = min(L - 1, (int)blockIdx.x * QPB + QPB - 1);
+  const int ilast = min(L - 1, (int)blockIdx.x * GQ + GQ - 1);
   const int n_hi = min(min(N, n_lo + span), N - L + ilast + 1);
-  const uint32_t lds_stage = (uint32_t)(uintptr_t)(DSA_LDS void*)&stage[0][0];
+  const uint32_t lds_stage = (uint32_t)(uintptr_t)(DSA_LDS void*)&stage[0];
 
   bf16x8 qa[ID / 16];
   {
@@ -584,96 +602,109 @@ __global__ __launch_bounds__(64 * IDX_NW) __attribute__((amdgpu_waves_per_eu(4, 
   for (int kc = 0; kc < ID / 16; ++kc) asm volatile("" ::"v"(qa[kc]));
 #pragma unroll
   for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(wr[j]));
-  if (tid < QPB) {
+  if (tid < GQ) {
     qcnt[tid] = 0;
     qovf[tid] = 0;
   }
 
-  // Tile loads: wave w's load u covers LDS chunk slots (w*G_DMA + u)*64 + lane, i.e.
-  // key r = slot / 16 of the tile and stored chunk c' = slot % 16, which holds global
-  // chunk c' ^ (r % 16) of that key (the swizzle that keeps MFMA operand reads
-  // conflict-free). key_of maps a tile row to a key index.
+  // Tile loads: load j (0 <= j < G_LOADS) fills stage bytes [1024 j, 1024 j + 1024);
+  // wave w issues loads w, w + GW and, for w < G_LOADS - 2 GW, w + 2 GW. Lane l of
+  // load j writes row (1024 j + 16 l) / G_ROW, 16-byte chunk ((1024 j + 16 l) % G_ROW) / 16;
+  // chunk 16 is the padding, for which the lane loads chunk 15 again.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool third = wave_u < G_LOADS - 2 * GW;
+  int lrow[3], lchk[3];
+  uint32_t voff[3];
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int pos = 1024 * (wave + GW * u) + 16 * lane;
+    lrow[u] = pos / G_ROW;
+    lchk[u] = min((pos % G_ROW) / 16, 15);
+    voff[u] = (uint32_t)(lrow[u] * (ID * 2) + lchk[u] * 16);
+  }
+  // rows mapped to arbitrary keys (sampled tiles, the clamped last tile)
   auto dma_tile = [&](auto key_of, int st) {
 #pragma unroll
-    for (int u = 0; u < G_DMA; ++u) {
-      const int slot = (wave_u * G_DMA + u) * 64 + lane;
-      const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
-      dma16(k + (size_t)key_of(r) * ID + c * 8, lds_stage + st * G_STAGE + (wave_u * G_DMA + u) * 1024);
-    }
+    for (int u = 0; u < 3; ++u)
+      if (u < 2 || third)
+        dma16(k + (size_t)key_of(lrow[u]) * ID + lchk[u] * 8,
+              lds_stage + st * G_STAGE + 1024 * (wave_u + GW * u));
   };
-  // A tile of consecutive keys n0 .. n0+127: load u of wave w covers rows
-  // 4(4w + u) + lane/16, and with r % 16 = 4u + lane/16 the stored chunk lane%16 holds
-  // global chunk (lane%16) ^ (lane/16) ^ 4u, so the byte offset within the tile is
-  // 4096 w + 1024 u (uniform) plus lane_dma ^ 64u (per lane).
-  static_assert(G_DMA == 4, "row and chunk algebra of the tile loads");
-  const uint32_t lane_dma = ((lane >> 4) * 256) | ((((lane & 15) ^ (lane >> 4)) & 15) * 16);
+  // rows n0 .. n0 + GT - 1
   auto dma_run = [&](int n0, int st) {
-    const unsigned char* base = (const unsigned char*)k + (size_t)n0 * (ID * 2) + wave_u * (G_DMA * 1024);
+    const unsigned char* base = (const unsigned char*)k + (size_t)n0 * (ID * 2);
 #pragma unroll
-    for (int u = 0; u < G_DMA; ++u)
-      dma16s(base + u * 1024, lane_dma ^ (64u * u), lds_stage + st * G_STAGE + (wave_u * G_DMA + u) * 1024);
+    for (int u = 0; u < 3; ++u)
+      if (u < 2 || third) dma16s(base, voff[u], lds_stage + st * G_STAGE + 1024 * (wave_u + GW * u));
   };
 
-  // Scores of keys r0 + lane (this query) from stage st: two 32-key chains
-  // (lanes < 32 get keys r0 .. r0+31, lanes >= 32 keys r0+32 .. r0+63), with the
-  // key fragments read two k-steps ahead of the MFMAs.
-  // Fragment addresses: both chains' rows have r % 16 = lane % 16, so stored chunk
-  // (2kc + lane/32) ^ (lane % 16) splits into a per-lane part and (32 kc) ^ (16 (lane & 14)).
-  const int xsw = 16 * (lane & 14);
-  const int lane_off = (lane & 31) * 256 + 16 * (((lane >> 5) ^ lane) & 1);
-  auto score64 = [&](int st, int r0) -> float {
-    const unsigned char* ba = stage[st] + r0 * 256 + lane_off;
-    auto fa = [&](int kc) { return *(const bf16x8*)(ba + ((32 * kc) ^ xsw)); };
-    auto fb = [&](int kc) { return *(const bf16x8*)(ba + 32 * 256 + ((32 * kc) ^ xsw)); };
+  // Scores of keys r0 + lane (this query) from stage st, r0 = 64 kh: two 32-key
+  // chains (lanes < 32 get keys r0 .. r0+31, lanes >= 32 keys r0+32 .. r0+63). The
+  // first chain's eight MFMAs run alone; the second chain's are interleaved with
+  // the first chain's ReLU and weighting. Fragments are read two k-steps ahead.
+  const int lane_rd = (lane & 31) * G_ROW + (lane >> 5) * 16 + kh * 64 * G_ROW;
+  auto score64 = [&](int st) -> float {
+    const unsigned char* ba = stage + st * G_STAGE + lane_rd;
+    auto fa = [&](int kc) { return *(const bf16x8*)(ba + 32 * kc); };
+    auto fb = [&](int kc) { return *(const bf16x8*)(ba + 32 * G_ROW + 32 * kc); };
     f32x16 acca = {}, accb = {};
-    bf16x8 fa0 = fa(0), fb0 = fb(0), fa1 = fa(1), fb1 = fb(1);
+    bf16x8 f[2];
+    f[0] = fa(0);
+    f[1] = fa(1);
 #pragma unroll
     for (int kc = 0; kc < ID / 16; ++kc) {
-      const bf16x8 xa = (kc & 1) ? fa1 : fa0, xb = (kc & 1) ? fb1 : fb0;
-      if (kc + 2 < ID / 16) {
-        if (kc & 1) { fa1 = fa(kc + 2); fb1 = fb(kc + 2); }
-        else { fa0 = fa(kc + 2); fb0 = fb(kc + 2); }
-      }
-      acca = mfma32x32x16(qa[kc], xa, acca);
-      accb = mfma32x32x16(qa[kc], xb, accb);
+      acca = mfma32x32x16(qa[kc], f[kc & 1], acca);
+      f[kc & 1] = kc + 2 < ID / 16 ? fa(kc + 2) : fb(kc + 2 - ID / 16);
     }
-    float pa = 0.f, pb = 0.f;
+    float pa0 = 0.f, pa1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      pa = fmaf(wr[j], __int_as_float(max(__float_as_int(acca[j]), 0)), pa);
-      pb = fmaf(wr[j], __int_as_float(max(__float_as_int(accb[j]), 0)), pb);
+    for (int kc = 0; kc < ID / 16; ++kc) {
+      accb = mfma32x32x16(qa[kc], f[kc & 1], accb);
+      if (kc + 2 < ID / 16) f[kc & 1] = fb(kc + 2);
+      pa0 = fmaf(wr[2 * kc], __int_as_float(max(__float_as_int(acca[2 * kc]), 0)), pa0);
+      pa1 = fmaf(wr[2 * kc + 1], __int_as_float(max(__float_as_int(acca[2 * kc + 1]), 0)), pa1);
     }
+    float pb0 = 0.f, pb1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      pb0 = fmaf(wr[j], __int_as_float(max(__float_as_int(accb[j]), 0)), pb0);
+      pb1 = fmaf(wr[j + 1], __int_as_float(max(__float_as_int(accb[j + 1]), 0)), pb1);
+    }
+    const float pa = pa0 + pa1, pb = pb0 + pb1;
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   };
 
   // Sampling prologue: SAMPLE keys spread evenly over the keys every query of the
   // group sees; the start threshold sits just below the rk-th largest sample score
-  // (see score_filter_kernel). Sample scores go to stage 1 as two segments per
-  // query (front wave from the start, back wave from the end), the layout the
-  // threshold search shares with the list compaction.
+  // (see score_filter_kernel). Sample tiles alternate between stages 0 and 1, one
+  // tile ahead; the scores go to stages 2-3 as two segments per query (front wave
+  // from the start, back wave from the end), the layout the threshold search shares
+  // with the list compaction.
   float thr = -INFINITY;
   {
-    const int nv_min = min(N, N - L + (int)blockIdx.x * QPB + 1);
+    const int nv_min = min(N, N - L + (int)blockIdx.x * GQ + 1);
     const float mean = (float)topk * SAMPLE / (float)max(nv_min, 1);
     if (nv_min >= 8 * SAMPLE && mean <= SAMPLE / 8) {
       const int rk = min(SAMPLE / 2, (int)ceilf(mean + 6.f * sqrtf(mean) + 8.f));
-      float* ss = (float*)stage[1] + qi * SAMPLE;
+      float* ss = (float*)(stage + 2 * G_STAGE) + qi * SAMPLE;
+      auto sample_tile = [&](int t) {
+        dma_tile([&](int r) { return (int)((long long)(t * GT + r) * nv_min / SAMPLE); }, t & 1);
+      };
+      sample_tile(0);
       for (int t = 0; t < SAMPLE / GT; ++t) {
-        dma_tile([&](int r) { return (int)((long long)(t * GT + r) * nv_min / SAMPLE); }, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();
-        const float sv = score64(0, 64 * kh);
+        lds_barrier();                  // tile t landed; every wave is done with tile t - 1
+        if (t + 1 < SAMPLE / GT) sample_tile(t + 1);
+        const float sv = score64(t & 1);
         const int e = t * 64 + lane;
         if (active) ss[kh == 0 ? e : SAMPLE - 1 - e] = sv;
-        lds_barrier();                  // stage 0 fully read before the next tile lands
       }
       float thr_q = -INFINITY;
-      pair_compact<float, SAMPLE>(ss, (float*)nullptr, SAMPLE / 2, kh, active, rk, eps_in[ii], thr_q,
-                                  hist + qi * 256, red, false);
+      pair_compact<float, SAMPLE, GQ>(ss, (float*)nullptr, SAMPLE / 2, kh, active, rk, eps_in[ii], thr_q,
+                                      hist + qi * 256, red, false);
       thr = thr_q;
-      lds_barrier();                    // sample scores fully read before stage 1 is reused
+      lds_barrier();                    // scores and histograms read before the ring reuses them
     }
   }
 
@@ -688,35 +719,63 @@ __global__ __launch_bounds__(64 * IDX_NW) __attribute__((amdgpu_waves_per_eu(4, 
     if (n0 + GT <= N) dma_run(n0, st);
     else dma_tile([=](int r) { return min(n0 + r, N - 1); }, st);
   };
-  if (ntiles > 0) {
-    dma_main(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  lds_barrier();
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    dma_main(min(t + 1, ntiles - 1), st ^ 1);
-    const float sv = score64(st, 64 * kh);
-    const int key = n_lo + t * GT + 64 * kh + lane;
-    const bool keep = active && key < n_hi && key <= p && sv >= thr;
-    const unsigned long long bm = __ballot(keep);
-    if (bm) {
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&qcnt[qi], (int)__popcll(bm));
-      base = __shfl(base, 0);
-      if (keep) {
-        const int pos = base + (int)__popcll(bm & ((1ull << lane) - 1ull));
-        if (pos < cap) {
-          ls[pos] = sv;
-          li[pos] = key;
-        } else {
-          qovf[qi] = 1;
-        }
+  int* const my_s = cbuf + wave * G_CB;
+  int* const my_i = cbuf + (GW + wave) * G_CB;
+  // a key of this wave is kept when key <= lim and its score reaches thr
+  const int lim = active ? min(n_hi - 1, p) : -1;
+  int cnt = 0;                          // staged survivors of this wave (wave-uniform)
+  auto flush = [&]() {
+    wave_sync();
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&qcnt[qi], cnt);
+    base = __shfl(base, 0);
+    for (int e = lane; e < cnt; e += 64) {
+      const int pos = base + e;
+      if (pos < cap) {
+        ls[pos] = __int_as_float(my_s[e]);
+        li[pos] = my_i[e];
+      } else {
+        qovf[qi] = 1;
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
+    cnt = 0;
+  };
+  // Tiles are issued G_NST - 1 ahead (the last tile is loaded again into the spare
+  // stages near the end, so the number of loads in flight is always the same);
+  // stage t % G_NST holds tile t. The wait at the top of iteration t leaves the
+  // loads of tiles t+1 .. t+G_NST-2 in flight, unless survivors were flushed in the
+  // previous iteration: then everything is drained, stores included.
+  if (ntiles > 0)
+    for (int s = 0; s < G_NST - 1; ++s) dma_main(min(s, ntiles - 1), s);
+  bool flushed = false;
+  for (int t = 0; t < ntiles; ++t) {
+    if (flushed) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (third) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((G_NST - 2) * 3) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((G_NST - 2) * 2) : "memory");
+    lds_barrier();                      // tile t landed; every wave is done with tile t - 1
+    dma_main(min(t + G_NST - 1, ntiles - 1), (t + G_NST - 1) % G_NST);
+    // the MFMAs go first when several waves of a SIMD are ready; the VALU work of
+    // the others fills in behind them
+    __builtin_amdgcn_s_setprio(1);
+    const float sv = score64(t % G_NST);
+    __builtin_amdgcn_s_setprio(0);
+    const int key = n_lo + t * GT + 64 * kh + lane;
+    const bool keep = key <= lim && sv >= thr;
+    const unsigned long long bm = __ballot(keep);
+    if (keep) {
+      const int e = cnt + (int)__popcll(bm & ((1ull << lane) - 1ull));
+      my_s[e] = __float_as_int(sv);
+      my_i[e] = key;
+    }
+    cnt += (int)__popcll(bm);
+    flushed = cnt > G_CB - 64;
+    if (flushed) flush();
   }
+  if (cnt > 0) flush();
+  // no load may still be writing the LDS when the workgroup ends (the ring's last
+  // loads repeat the final tile and are never waited for in the loop)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();                        // every flush of the group has taken its positions
   if (active && kh == 0 && lane == 0) {
     cand_n[slot] = qovf[qi] ? -1 : qcnt[qi];
     cand_t[slot] = thr;
@@ -1241,7 +1300,7 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
     KernelTrace kt("indexer_score_filter", stream);
     const dim3 grid((L + QPB - 1) / QPB, pl.nsplit), block(64 * IDX_NW);
     if (pl.global_lists)
-      hipLaunchKernelGGL(score_list_kernel, grid, block, 0, stream, q, k, w, eps, L, N, topk, pl.span, pl.nsplit,
+      hipLaunchKernelGGL(score_list_kernel, dim3((L + GQ - 1) / GQ, pl.nsplit), dim3(64 * GW), 0, stream, q, k, w, eps, L, N, topk, pl.span, pl.nsplit,
                          pl.cap, cand_s, cand_i, cand_n, cand_t);
     else if (pl.small_off)
       hipLaunchKernelGGL((score_filter_kernel<uint16_t>), grid, block, 0, stream, q, k, w, eps, L, N,
