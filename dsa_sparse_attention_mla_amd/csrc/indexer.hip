@@ -638,39 +638,77 @@ __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       if (u < 2 || third) dma16s(base, voff[u], lds_stage + st * G_STAGE + 1024 * (wave_u + GW * u));
   };
 
-  // Scores of keys r0 + lane (this query) from stage st, r0 = 64 kh: two 32-key
-  // chains (lanes < 32 get keys r0 .. r0+31, lanes >= 32 keys r0+32 .. r0+63). The
-  // first chain's eight MFMAs run alone; the second chain's are interleaved with
-  // the first chain's ReLU and weighting. Fragments are read two k-steps ahead.
+  // Scores of keys r0 + lane (this query), r0 = 64 kh, of a stage: chains a (lanes
+  // < 32 get keys r0 .. r0+31) and b (lanes >= 32 get r0+32 .. r0+63), with
+  // accumulators acc_a and acc_b. Phase A runs the eight chain-a MFMAs, phase B the
+  // chain-b ones; the VALU work that turns accumulators into weighted ReLU sums is
+  // interleaved with the other phase's MFMAs: the chain-a sums with phase B of the
+  // same tile, the chain-b sums with phase A of the next tile (the accumulators of
+  // both chains stay live), so no MFMA waits for them. Fragments are read two
+  // k-steps ahead.
   const int lane_rd = (lane & 31) * G_ROW + (lane >> 5) * 16 + kh * 64 * G_ROW;
-  auto score64 = [&](int st) -> float {
+  constexpr int KS = ID / 16;           // k-steps per chain
+  f32x16 acc_a, acc_b = {};
+  // the empty asm pins the running sum at this point of the instruction stream
+  auto relu_w = [&](const f32x16& c, int j, float p) {
+    p = fmaf(wr[j], __int_as_float(max(__float_as_int(c[j]), 0)), p);
+    asm volatile("" : "+v"(p));
+    return p;
+  };
+  // One k-step: the MFMA, the fragment read two k-steps ahead and the two VALU
+  // sums of this step; the scheduling barrier after each step keeps the compiler
+  // from gathering the VALU work in one place.
+  // phase A on stage st; meanwhile the chain-b sums of the previous tile (pb)
+  auto phase_a = [&](int st) -> float {
     const unsigned char* ba = stage + st * G_STAGE + lane_rd;
-    auto fa = [&](int kc) { return *(const bf16x8*)(ba + 32 * kc); };
-    auto fb = [&](int kc) { return *(const bf16x8*)(ba + 32 * G_ROW + 32 * kc); };
-    f32x16 acca = {}, accb = {};
-    bf16x8 f[2];
-    f[0] = fa(0);
-    f[1] = fa(1);
+    bf16x8 f0 = *(const bf16x8*)(ba), f1 = *(const bf16x8*)(ba + 32);
+    float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-    for (int kc = 0; kc < ID / 16; ++kc) {
-      acca = mfma32x32x16(qa[kc], f[kc & 1], acca);
-      f[kc & 1] = kc + 2 < ID / 16 ? fa(kc + 2) : fb(kc + 2 - ID / 16);
+    for (int kc = 0; kc < KS; ++kc) {
+      const bf16x8 x = (kc & 1) ? f1 : f0;
+      acc_a = mfma32x32x16(qa[kc], x, kc ? acc_a : f32x16{});
+      p0 = relu_w(acc_b, 2 * kc, p0);
+      if (kc + 2 < KS) {
+        if (kc & 1) f1 = *(const bf16x8*)(ba + 32 * (kc + 2));
+        else f0 = *(const bf16x8*)(ba + 32 * (kc + 2));
+      }
+      p1 = relu_w(acc_b, 2 * kc + 1, p1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float pa0 = 0.f, pa1 = 0.f;
+    return p0 + p1;
+  };
+  // phase B on stage st; meanwhile the chain-a sums of this tile (pa)
+  auto phase_b = [&](int st) -> float {
+    const unsigned char* ba = stage + st * G_STAGE + lane_rd + 32 * G_ROW;
+    bf16x8 f0 = *(const bf16x8*)(ba), f1 = *(const bf16x8*)(ba + 32);
+    float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-    for (int kc = 0; kc < ID / 16; ++kc) {
-      accb = mfma32x32x16(qa[kc], f[kc & 1], accb);
-      if (kc + 2 < ID / 16) f[kc & 1] = fb(kc + 2);
-      pa0 = fmaf(wr[2 * kc], __int_as_float(max(__float_as_int(acca[2 * kc]), 0)), pa0);
-      pa1 = fmaf(wr[2 * kc + 1], __int_as_float(max(__float_as_int(acca[2 * kc + 1]), 0)), pa1);
+    for (int kc = 0; kc < KS; ++kc) {
+      const bf16x8 x = (kc & 1) ? f1 : f0;
+      acc_b = mfma32x32x16(qa[kc], x, kc ? acc_b : f32x16{});
+      p0 = relu_w(acc_a, 2 * kc, p0);
+      if (kc + 2 < KS) {
+        if (kc & 1) f1 = *(const bf16x8*)(ba + 32 * (kc + 2));
+        else f0 = *(const bf16x8*)(ba + 32 * (kc + 2));
+      }
+      p1 = relu_w(acc_a, 2 * kc + 1, p1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float pb0 = 0.f, pb1 = 0.f;
+    return p0 + p1;
+  };
+  // chain-b sums alone (after the last tile)
+  auto tail_b = [&]() -> float {
+    float p0 = 0.f, p1 = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; j += 2) {
-      pb0 = fmaf(wr[j], __int_as_float(max(__float_as_int(accb[j]), 0)), pb0);
-      pb1 = fmaf(wr[j + 1], __int_as_float(max(__float_as_int(accb[j + 1]), 0)), pb1);
+      p0 = relu_w(acc_b, j, p0);
+      p1 = relu_w(acc_b, j + 1, p1);
     }
-    const float pa = pa0 + pa1, pb = pb0 + pb1;
+    return p0 + p1;
+  };
+  // lanes < 32 hold chain a's half of the heads (and lanes >= 32 chain b's) for key
+  // lane % 32 of each chain; the swap gives every lane both halves of its own key
+  auto combine = [&](float pa, float pb) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   };
@@ -696,7 +734,9 @@ __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();                  // tile t landed; every wave is done with tile t - 1
         if (t + 1 < SAMPLE / GT) sample_tile(t + 1);
-        const float sv = score64(t & 1);
+        phase_a(t & 1);
+        const float pa = phase_b(t & 1);
+        const float sv = combine(pa, tail_b());
         const int e = t * 64 + lane;
         if (active) ss[kh == 0 ? e : SAMPLE - 1 - e] = sv;
       }
@@ -747,7 +787,23 @@ __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   // previous iteration: then everything is drained, stores included.
   if (ntiles > 0)
     for (int s = 0; s < G_NST - 1; ++s) dma_main(min(s, ntiles - 1), s);
+  // survivors of tile t (score sv of key n_lo + t GT + 64 kh + lane)
+  auto stage_keep = [&](int t, float sv, bool valid) {
+    const int key = n_lo + t * GT + 64 * kh + lane;
+    const bool keep = valid && key <= lim && sv >= thr;
+    const unsigned long long bm = __ballot(keep);
+    if (keep) {
+      const int e = cnt + (int)__popcll(bm & ((1ull << lane) - 1ull));
+      my_s[e] = __float_as_int(sv);
+      my_i[e] = key;
+    }
+    cnt += (int)__popcll(bm);
+    const bool fl = cnt > G_CB - 64;
+    if (fl) flush();
+    return fl;
+  };
   bool flushed = false;
+  float pa = 0.f;                       // chain-a sums of the previous tile
   for (int t = 0; t < ntiles; ++t) {
     if (flushed) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     else if (third) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((G_NST - 2) * 3) : "memory");
@@ -757,20 +813,14 @@ __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     // the MFMAs go first when several waves of a SIMD are ready; the VALU work of
     // the others fills in behind them
     __builtin_amdgcn_s_setprio(1);
-    const float sv = score64(t % G_NST);
+    const float pb = phase_a(t % G_NST);   // + chain-b sums of tile t - 1
+    const float pa_t = phase_b(t % G_NST); // + chain-a sums of tile t
     __builtin_amdgcn_s_setprio(0);
-    const int key = n_lo + t * GT + 64 * kh + lane;
-    const bool keep = key <= lim && sv >= thr;
-    const unsigned long long bm = __ballot(keep);
-    if (keep) {
-      const int e = cnt + (int)__popcll(bm & ((1ull << lane) - 1ull));
-      my_s[e] = __float_as_int(sv);
-      my_i[e] = key;
-    }
-    cnt += (int)__popcll(bm);
-    flushed = cnt > G_CB - 64;
-    if (flushed) flush();
+    // tile t - 1 (nothing is kept at t = 0, whose previous-tile sums are zeros)
+    flushed = stage_keep(t - 1, combine(pa, pb), t > 0);
+    pa = pa_t;
   }
+  if (ntiles > 0) stage_keep(ntiles - 1, combine(pa, tail_b()), true);
   if (cnt > 0) flush();
   // no load may still be writing the LDS when the workgroup ends (the ring's last
   // loads repeat the final tile and are never waited for in the loop)
