@@ -42,13 +42,12 @@ constexpr int IDX_NW = 8;               // waves per score workgroup: 2 per quer
 constexpr int SAMPLE = 2048;            // keys scored up front to start the filter threshold
 constexpr int RANK_WORDS = 4096;        // bitmap words for ordering the output (131072 keys per window)
 static_assert(RANK_WORDS * 4 >= 64 * IH * 8, "band dots alias the word-prefix table");
-constexpr int RANK_CAP = 1024;          // band entries ranked in select_refine
+constexpr int BAND_CAP = 256;           // band entries re-scored and ranked in select_refine
+constexpr int BIN_CAP = 1024;           // entries of the threshold bin ranked in select_refine
+constexpr int SR_J = 48;                // candidates per thread (in registers) in select_refine
+constexpr int SR_MAX = SR_J * 256;      // candidates per query select_refine holds
 constexpr int NORM_BLOCKS = 256;
 constexpr int FB_ROWS = 256;            // block size of the fallback kernel
-// LDS of the refine kernel besides the candidate arrays: band scores/keys/bin values/flags,
-// the staged query, the rank bitmap, rank bases, histogram, scratch
-constexpr size_t SELECT_FIXED = RANK_CAP * 8 + RANK_CAP * 4 + RANK_CAP * 4 + RANK_CAP + IH * ID * 2 + RANK_WORDS * 4 +
-                                RANK_WORDS * 4 + 256 * 4 + 256 * 4 + 16 * 4;
 }  // namespace
 
 __device__ __forceinline__ void wave_sync() {
@@ -119,15 +118,39 @@ __global__ __launch_bounds__(64) void query_eps_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------- 3. score + running candidates
+// Wave-wide reduction with an associative, commutative op, every lane getting the
+// result: DPP exchanges within each row of 16 lanes (xor 1, xor 2, half-row mirror,
+// row mirror), then the permlane swaps across rows 16 and 32 lanes apart. All VALU:
+// no LDS round trips.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_bits(uint32_t x, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(b[0], b[1]);
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+  return __uint_as_float(wave_reduce_bits(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 __device__ __forceinline__ float wave_min(float x) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x = fminf(x, __shfl_xor(x, off));
-  return x;
+  return __uint_as_float(wave_reduce_bits(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ int wave_sum_int(int x) {
+  return (int)wave_reduce_bits((uint32_t)x, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return wave_reduce_bits(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return wave_reduce_bits(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
 // Bucket of x in a 256-bin linear histogram over [mn, mx]; non-decreasing in x.
@@ -833,80 +856,54 @@ __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 }
 
 // ---------------------------------------------------------------- 4. select + band refine
-// Block-level (256 threads) exact k-th largest of vals[0..n) (finite, n >= k):
-// linear histogram to find the bin, then an exact rank count inside the bin.
-// Returns false (and nothing) when the bin holds more than cap_bin entries.
-__device__ bool block_kth_exact(const float* vals, int n, int k, int* hist, int* misc, float* red,
-                                float* bin_vals, int cap_bin, float& out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float mx = -INFINITY, mn = INFINITY;
-  for (int e = tid; e < n; e += 256) {
-    const float v = vals[e];
-    mx = fmaxf(mx, v);
-    mn = fminf(mn, v);
-  }
-  mx = wave_max(mx);
-  mn = wave_min(mn);
-  if (lane == 0) { red[wave] = mx; red[4 + wave] = mn; }
-  hist[tid] = 0;
-  if (tid == 0) misc[2] = 0;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  mn = fminf(fminf(red[4], red[5]), fminf(red[6], red[7]));
-  if (!(mx > mn)) {
-    out = mx;
-    __syncthreads();
-    return true;
-  }
-  const float inv_w = 256.0f / (mx - mn);
-  for (int e = tid; e < n; e += 256) atomicAdd(&hist[lin_bucket(vals[e], mn, inv_w)], 1);
-  __syncthreads();
-  if (wave == 0) {
-    int bin, above;
-    wave_find_bin(hist, k, lane, bin, above);
-    if (lane == 0) { misc[0] = bin; misc[1] = above; }
-  }
-  __syncthreads();
-  const int bin = misc[0], need = k - misc[1];
-  for (int e = tid; e < n; e += 256) {
-    const float v = vals[e];
-    if (lin_bucket(v, mn, inv_w) == bin) {
-      const int slot = atomicAdd(&misc[2], 1);
-      if (slot < cap_bin) bin_vals[slot] = v;
-    }
-  }
-  __syncthreads();
-  const int nb = misc[2];
-  if (nb > cap_bin) {
-    __syncthreads();
-    return false;
-  }
-  // the need-th largest inside the bin: the largest v with #{u >= v} >= need
-  float best = -INFINITY;
-  for (int e = tid; e < nb; e += 256) {
-    const float v = bin_vals[e];
-    int c = 0;
-    for (int f = 0; f < nb; ++f) c += bin_vals[f] >= v;
-    if (c >= need) best = fmaxf(best, v);
-  }
-  best = wave_max(best);
-  __syncthreads();
-  if (lane == 0) red[wave] = best;
-  __syncthreads();
-  out = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return true;
-}
+// One workgroup (256 threads) per query. The query's candidates (the concatenated
+// split lists, M <= SR_MAX) sit in registers: thread t holds entries t + 256 j,
+// j < SR_J, with per-thread bit masks for "kept" and "in the band". The LDS holds
+// only the histograms, the band, the staged query and the rank bitmap (about 75 KB,
+// two workgroups per compute unit).
+//   1. tk = the exact topk-th largest candidate score (linear histogram over
+//      [min, max], then an exact rank count inside the bin that holds it);
+//   2. scores above tk + band are kept, scores in [tk - band, tk + band] form the
+//      band, whose keys get canonical fp64 scores; the best (topk - #above) of them
+//      by (fp64 score desc, key asc) are kept;
+//   3. kept keys are written in ascending order: a bitmap over a window of keys and
+//      prefix popcounts give every kept key its output slot.
+namespace {
+constexpr int Q_ROW = ID + 8;           // staged query row, in bf16 (16 B of padding)
+constexpr int DH_ROW = IH + 1;          // per-key head dots, in doubles (8 B of padding)
+
+struct RefineLds {
+  uint32_t bitmap[RANK_WORDS];                         // kept keys of the window; band key rows while re-scoring
+  union {
+    int wpre[RANK_WORDS];                              // kept keys before each bitmap word
+    double dh[64 * DH_ROW];                            // head dots of a band batch
+  } u;
+  uint16_t qrow[IH * Q_ROW];
+  double bscore[BAND_CAP];
+  int bkey[BAND_CAP];
+  float bval[BAND_CAP];
+  float binv[BIN_CAP];
+  unsigned char bsel[BAND_CAP];
+  int hist[4][256];
+  int misc[16];
+  float red[8];
+};
+static_assert(64 * ID * 2 <= RANK_WORDS * 4, "a band batch of key rows fits the bitmap");
+static_assert(BAND_CAP <= 256, "one thread per band slot in the emit");
+static_assert(sizeof(RefineLds) <= 80 * 1024, "two refine workgroups per compute unit");
+}  // namespace
 
 // Canonical fp64 scores of up to 64 band keys whose rows are staged in LDS
 // (krows, 256 B each): lane l32 of 32-lane group g owns head l32 and keys
 // g, g+8, ..., g+56 (eight independent chains). d_h is summed over dims in
 // ascending order; the head terms are then added in ascending head order by one
-// lane per key. Every product and sum is a separate IEEE operation.
+// lane per key. A bf16 x bf16 product is exact in fp64, so the fused multiply-add
+// rounds exactly as a product followed by a sum; the weight products are rounded
+// separately.
 __device__ void canonical_scores_batch(const uint16_t* qrow_lds, const uint16_t* krows, int nkeys,
                                        const float* __restrict__ wrow, double* dh, double* out) {
   const int tid = threadIdx.x, g = tid >> 5, l32 = tid & 31;
-  const uint16_t* qh = qrow_lds + l32 * ID;
+  const uint16_t* qh = qrow_lds + l32 * Q_ROW;
   double d[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) d[j] = 0.0;
@@ -921,17 +918,17 @@ __device__ void canonical_scores_batch(const uint16_t* qrow_lds, const uint16_t*
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const double kd = (double)bf_bits2f((uint16_t)((kv[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
-        d[j] = __dadd_rn(d[j], __dmul_rn(qd, kd));
+        d[j] = __fma_rn(qd, kd, d[j]);
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dh[(g + 8 * j) * IH + l32] = d[j];
+  for (int j = 0; j < 8; ++j) dh[(g + 8 * j) * DH_ROW + l32] = d[j];
   __syncthreads();
   if (tid < nkeys) {
     double sc = 0.0;
     for (int h = 0; h < IH; ++h) {
-      const double v = dh[tid * IH + h];
+      const double v = dh[tid * DH_ROW + h];
       sc = __dadd_rn(sc, __dmul_rn((double)wrow[h], v > 0.0 ? v : 0.0));
     }
     out[tid] = sc;
@@ -939,32 +936,20 @@ __device__ void canonical_scores_batch(const uint16_t* qrow_lds, const uint16_t*
   __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void select_refine_kernel(
+// Order-preserving map of a float to an unsigned integer (for -0 < +0 it does not
+// matter: both are scored alike).
+__device__ __forceinline__ uint32_t ord_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(256, 2) void select_refine_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int nsplit, int cap,
     const float* __restrict__ cand_s, const int* __restrict__ cand_i, const int* __restrict__ cand_n,
     const float* __restrict__ cand_t, int* __restrict__ fb_flag, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-  const int M_cap = nsplit * cap;
-  float* vs = (float*)dyn;                              // [M_cap] candidate scores
-  int* vi = (int*)(vs + M_cap);                         // [M_cap] candidate keys
-  unsigned char* cls = (unsigned char*)(vi + M_cap);    // [M_cap] 0 out, 1 in, 2 band
-  short* bid = (short*)(cls + ((M_cap + 15) & ~15));    // [M_cap] band id
-  double* bscore = (double*)(bid + ((M_cap + 7) & ~7)); // [RANK_CAP]
-  int* bkey = (int*)(bscore + RANK_CAP);                // [RANK_CAP]
-  float* binv = (float*)(bkey + RANK_CAP);              // [RANK_CAP] values of the threshold bin
-  unsigned char* bsel = (unsigned char*)(binv + RANK_CAP);  // [RANK_CAP]
-  uint16_t* qrow = (uint16_t*)(bsel + RANK_CAP);        // [IH*ID]
-  uint32_t* bitmap = (uint32_t*)(qrow + IH * ID);       // [RANK_WORDS]; band key rows while re-scoring
-  int* wpre = (int*)(bitmap + RANK_WORDS);              // [RANK_WORDS] kept keys before each word
-  double* dh = (double*)wpre;                           // [64][IH] per-head dots of a band batch (same bytes;
-                                                        // the band re-score ends before the emit starts)
-  int* tbase = wpre + RANK_WORDS;                       // [256] per-thread rank bases
-  int* hist = tbase + 256;                              // [256]
-  int* misc = hist + 256;                               // [16]
-  float* red = (float*)(misc + 8);                      // [8] (aliases misc[8..15])
-
+  __shared__ __attribute__((aligned(16))) RefineLds sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = blockIdx.x;
   const int p = N - L + i;
@@ -972,43 +957,52 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
   int32_t* orow = idx_out + (size_t)i * topk;
   float* srow = score_out ? score_out + (size_t)i * topk : nullptr;
 
+  // ---- candidates into registers. Split sp's list fills slots [pre4[sp], pre4[sp] +
+  // cnt rounded up to 4); thread t loads slot groups t + 256 u (4 slots each, one
+  // 16-byte load of scores and one of keys). Unused slots hold key -1.
+  int cnt[4] = {0, 0, 0, 0}, pre4[5] = {0, 0, 0, 0, 0};
+  bool overflow = nsplit > 4;
   int M = 0;
-  bool overflow = false;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const int c = cand_n[(size_t)i * nsplit + sp];
-    if (c < 0) { overflow = true; break; }
-    // 16-byte loads, four in flight per thread; a list region holds cap entries
-    // (a multiple of 64), so the last partial vector stays inside it
-    const float4* src_s = (const float4*)(cand_s + ((size_t)i * nsplit + sp) * cap);
-    const int4* src_i = (const int4*)(cand_i + ((size_t)i * nsplit + sp) * cap);
-    const int nv4 = (c + 3) / 4;
-    for (int e0 = tid; e0 < nv4; e0 += 256 * 4) {
-      float4 a[4];
-      int4 b[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + 256 * u;
-        if (e < nv4) { a[u] = src_s[e]; b[u] = src_i[e]; }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + 256 * u;
-        if (e < nv4) {
-          const float av[4] = {a[u].x, a[u].y, a[u].z, a[u].w};
-          const int bv[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            if (4 * e + x < c) { vs[M + 4 * e + x] = av[x]; vi[M + 4 * e + x] = bv[x]; }
-        }
-      }
-    }
-    M += c;
+  for (int sp = 0; sp < nsplit && sp < 4; ++sp) {
+    cnt[sp] = cand_n[(size_t)i * nsplit + sp];
+    if (cnt[sp] < 0) overflow = true;
+    M += max(cnt[sp], 0);
+    pre4[sp + 1] = pre4[sp] + (max(cnt[sp], 0) + 3) / 4 * 4;
   }
-  if (overflow) {
+  const int M4 = pre4[min(nsplit, 4)];
+  for (int sp = min(nsplit, 4) + 1; sp < 5; ++sp) pre4[sp] = INT_MAX;   // no slot maps past the last split
+  if (overflow || M4 > SR_MAX) {
     if (tid == 0) fb_flag[i] = 1;
     return;
   }
-  __syncthreads();
+  constexpr int SR_U = SR_J / 4;
+  // slot groups of this wave that hold anything: those below M4 / 4
+  const int uw = min(SR_U, (M4 / 4 - wave * 64 + 255) / 256);
+  float sc[SR_J];
+  int ky[SR_J];
+#pragma unroll
+  for (int u = 0; u < SR_U; ++u) {
+    float4 s4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    int4 k4 = {-1, -1, -1, -1};
+    if (u < uw) {
+      const int slot = 4 * (tid + 256 * u);
+      if (slot < M4) {
+        const int sp = (slot >= pre4[1]) + (slot >= pre4[2]) + (slot >= pre4[3]);
+        const int off = slot - pre4[sp];
+        const size_t o = ((size_t)i * nsplit + sp) * cap + off;   // cap is a multiple of 64
+        s4 = *(const float4*)(cand_s + o);
+        k4 = *(const int4*)(cand_i + o);
+        if (off + 1 > cnt[sp]) k4.x = -1;
+        if (off + 2 > cnt[sp]) k4.y = -1;
+        if (off + 3 > cnt[sp]) k4.z = -1;
+        if (off + 4 > cnt[sp]) k4.w = -1;
+      }
+    }
+    sc[4 * u] = s4.x; sc[4 * u + 1] = s4.y; sc[4 * u + 2] = s4.z; sc[4 * u + 3] = s4.w;
+    ky[4 * u] = k4.x; ky[4 * u + 1] = k4.y; ky[4 * u + 2] = k4.z; ky[4 * u + 3] = k4.w;
+  }
+  const int jw = 4 * uw;                // register slots of this wave that may hold entries
+  uint64_t kept = 0;
 
   const float eps = eps_in[i];
   // Each split's list holds every key scoring at least that split's final filter
@@ -1017,18 +1011,93 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
   // the lists themselves, to be checked for the sampled start).
   float thr_max = -INFINITY;
   for (int sp = 0; sp < nsplit; ++sp) thr_max = fmaxf(thr_max, cand_t[(size_t)i * nsplit + sp]);
+  int nb = 0;                           // band entries (slots [0, nb) of the LDS band arrays)
   if (nv <= topk) {
     // every visible key must be in the lists: only an untouched threshold guarantees it
     if (thr_max > -INFINITY) {
       if (tid == 0) fb_flag[i] = 1;
       return;
     }
-    for (int e = tid; e < M; e += 256) cls[e] = 1;
+#pragma unroll
+    for (int j = 0; j < SR_J; ++j)
+      if (j < jw && ky[j] >= 0) kept |= 1ull << j;
   } else {
+    // ---- 1. tk, the topk-th largest score: a 256-bin histogram linear in the
+    // order-preserving integer image of the scores (so a heavy low tail spreads over
+    // many bins), then an exact rank count inside the bin that holds it
+    uint32_t umx = 0u, umn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < SR_J; ++j)
+      if (j < jw && ky[j] >= 0) {
+        const uint32_t u = ord_bits(sc[j]);
+        umx = max(umx, u);
+        umn = min(umn, u);
+      }
+    umx = wave_max_u32(umx);
+    umn = wave_min_u32(umn);
+    if (lane == 0) {
+      sm.misc[8 + wave] = (int)umx;
+      sm.misc[12 + wave] = (int)umn;
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) sm.hist[x][tid] = 0;
+    if (tid == 0) sm.misc[2] = 0;
+    __syncthreads();
+    umx = max(max((uint32_t)sm.misc[8], (uint32_t)sm.misc[9]), max((uint32_t)sm.misc[10], (uint32_t)sm.misc[11]));
+    umn = min(min((uint32_t)sm.misc[12], (uint32_t)sm.misc[13]), min((uint32_t)sm.misc[14], (uint32_t)sm.misc[15]));
+    // bin = (u - umn) >> shift with (umx - umn) >> shift < 256
+    const uint32_t span = umx - umn;
+    const int shift = span < 256u ? 0 : 32 - __clz((int)(span >> 8)) ;
     float tk;
-    if (!block_kth_exact(vs, M, topk, hist, misc, red, binv, RANK_CAP, tk)) {
-      if (tid == 0) fb_flag[i] = 1;
-      return;
+    if (span == 0u) {
+      // all scores equal
+      tk = __uint_as_float((umx & 0x80000000u) ? (umx & 0x7FFFFFFFu) : ~umx);
+    } else {
+#pragma unroll
+      for (int j = 0; j < SR_J; ++j)
+        if (j < jw && ky[j] >= 0) atomicAdd(&sm.hist[wave][(ord_bits(sc[j]) - umn) >> shift], 1);
+      __syncthreads();
+      sm.hist[0][tid] += sm.hist[1][tid] + sm.hist[2][tid] + sm.hist[3][tid];
+      __syncthreads();
+      if (wave == 0) {
+        int bin, above;
+        wave_find_bin(sm.hist[0], topk, lane, bin, above);
+        if (lane == 0) {
+          sm.misc[0] = bin;
+          sm.misc[1] = above;
+        }
+      }
+      __syncthreads();
+      const uint32_t bin = (uint32_t)sm.misc[0];
+      const int need = topk - sm.misc[1];
+#pragma unroll
+      for (int j = 0; j < SR_J; ++j)
+        if (j < jw && ky[j] >= 0 && ((ord_bits(sc[j]) - umn) >> shift) == bin) {
+          const int slot = atomicAdd(&sm.misc[2], 1);
+          if (slot < BIN_CAP) sm.binv[slot] = sc[j];
+        }
+      __syncthreads();
+      const int nbin = sm.misc[2];
+      if (nbin > BIN_CAP) {
+        if (tid == 0) fb_flag[i] = 1;
+        return;
+      }
+      // the need-th largest inside the bin: the largest v with #{u >= v} >= need
+      float best = -INFINITY;
+      for (int e = tid; e < nbin; e += 256) {
+        const float v = sm.binv[e];
+        int c = 0, f = 0;
+        for (; f + 4 <= nbin; f += 4) {
+          const float4 u = *(const float4*)&sm.binv[f];
+          c += (u.x >= v) + (u.y >= v) + (u.z >= v) + (u.w >= v);
+        }
+        for (; f < nbin; ++f) c += sm.binv[f] >= v;
+        if (c >= need) best = fmaxf(best, v);
+      }
+      best = wave_max(best);
+      if (lane == 0) sm.red[wave] = best;
+      __syncthreads();
+      tk = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
     }
     const float hw = band_halfwidth(eps, tk);
     const float hi = tk + hw, lo = tk - hw;
@@ -1036,110 +1105,158 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
       if (tid == 0) fb_flag[i] = 1;
       return;
     }
-    if (tid == 0) { misc[2] = 0; misc[3] = 0; }
-    __syncthreads();
-    for (int e0 = 0; e0 < M; e0 += 256) {
-      const int e = e0 + tid;
-      const float v = e < M ? vs[e] : -INFINITY;
-      const bool isin = e < M && v > hi, isband = e < M && !isin && v >= lo;
-      const unsigned long long bin_ = __ballot(isin), bband = __ballot(isband);
-      int base_in = 0, base_b = 0;
-      if (lane == 0) {
-        if (bin_) atomicAdd(&misc[2], (int)__popcll(bin_));
-        if (bband) base_b = atomicAdd(&misc[3], (int)__popcll(bband));
-      }
-      base_b = __builtin_amdgcn_readfirstlane(base_b);
-      (void)base_in;
-      if (e < M) cls[e] = isin ? 1 : (isband ? 2 : 0);
-      if (isband) {
-        const int b = base_b + __popcll(bband & ((1ull << lane) - 1ull));
-        if (b < RANK_CAP) { bid[e] = (short)b; bkey[b] = vi[e]; }
-      }
+    // ---- 2. above the band: kept; inside: band slots (key and fp32 score)
+    if (tid == 0) {
+      sm.misc[2] = 0;
+      sm.misc[3] = 0;
     }
     __syncthreads();
-    const int n_in = misc[2], nb = misc[3];
+    int my_in = 0;
+#pragma unroll
+    for (int j = 0; j < SR_J; ++j) {
+      if (j < jw) {
+        const bool ok = ky[j] >= 0;
+        const bool isin = ok && sc[j] > hi, isband = ok && !isin && sc[j] >= lo;
+        if (isin) kept |= 1ull << j;
+        my_in += isin;
+        const unsigned long long bb = __ballot(isband);
+        if (bb) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&sm.misc[3], (int)__popcll(bb));
+          base = __shfl(base, 0);
+          if (isband) {
+            const int b = base + (int)__popcll(bb & ((1ull << lane) - 1ull));
+            if (b < BAND_CAP) {
+              sm.bkey[b] = ky[j];
+              sm.bval[b] = sc[j];
+            }
+          }
+        }
+      }
+    }
+    my_in = wave_sum_int(my_in);
+    if (lane == 0) atomicAdd(&sm.misc[2], my_in);
+    __syncthreads();
+    const int n_in = sm.misc[2];
+    nb = sm.misc[3];
     const int need_band = topk - n_in;
-    if (nb > RANK_CAP || need_band < 0 || need_band > nb) {
+    if (nb > BAND_CAP || need_band < 0 || need_band > nb) {
       if (tid == 0) fb_flag[i] = 1;
       return;
     }
-    for (int e = tid; e < IH * ID / 8; e += 256)
-      *(u32x4*)(qrow + 8 * e) = *(const u32x4*)(q + (size_t)i * IH * ID + 8 * e);
-    const float* wrow = w + (size_t)i * IH;
-    uint16_t* krows = (uint16_t*)bitmap;                // 64 rows x 256 B = the bitmap's 16 KB
-    for (int b0 = 0; b0 < nb; b0 += 64) {
-      const int nk = min(64, nb - b0);
-      for (int x = tid; x < 64 * (ID / 8); x += 256) {   // row r, chunk c; missing rows repeat row 0
-        const int r = x >> 4, c = x & 15;
-        const int n = bkey[b0 + (r < nk ? r : 0)];
-        *(u32x4*)(krows + r * ID + 8 * c) = *(const u32x4*)(k + (size_t)n * ID + 8 * c);
+    if (nb > 0) {
+      for (int e = tid; e < IH * ID / 8; e += 256) {
+        const int h = e / (ID / 8), c = e % (ID / 8);
+        *(u32x4*)(sm.qrow + h * Q_ROW + 8 * c) = *(const u32x4*)(q + (size_t)i * IH * ID + 8 * e);
       }
-      __syncthreads();
-      canonical_scores_batch(qrow, krows, nk, wrow, dh, bscore + b0);
-    }
-    for (int b = tid; b < nb; b += 256) {
-      const double sc = bscore[b];
-      const int key = bkey[b];
-      int r = 0;
-      for (int o = 0; o < nb; ++o) {
-        const double so = bscore[o];
-        r += (so > sc) || (so == sc && bkey[o] < key);
+      const float* wrow = w + (size_t)i * IH;
+      uint16_t* krows = (uint16_t*)sm.bitmap;           // 64 rows x 256 B
+      for (int b0 = 0; b0 < nb; b0 += 64) {
+        const int nk = min(64, nb - b0);
+        for (int x = tid; x < 64 * (ID / 8); x += 256) {  // row r, chunk c; missing rows repeat row 0
+          const int r = x >> 4, c = x & 15;
+          const int n = sm.bkey[b0 + (r < nk ? r : 0)];
+          *(u32x4*)(krows + r * ID + 8 * c) = *(const u32x4*)(k + (size_t)n * ID + 8 * c);
+        }
+        __syncthreads();
+        canonical_scores_batch(sm.qrow, krows, nk, wrow, sm.u.dh, sm.bscore + b0);
       }
-      bsel[b] = r < need_band;
+      // rank by (fp64 score desc, key asc); the best need_band are kept
+      if (nb <= 64) {
+        if (wave == 0 && lane < 64) {
+          const double s0 = lane < nb ? sm.bscore[lane] : -INFINITY;
+          const int key = lane < nb ? sm.bkey[lane] : INT_MAX;
+          const uint64_t sb = (uint64_t)__double_as_longlong(s0);
+          int r = 0;
+          for (int o = 0; o < nb; ++o) {
+            const uint32_t lo32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sb, o);
+            const uint32_t hi32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(sb >> 32), o);
+            const double so = __longlong_as_double((long long)(((uint64_t)hi32 << 32) | lo32));
+            const int ko = __builtin_amdgcn_readlane(key, o);
+            r += (so > s0) || (so == s0 && ko < key);
+          }
+          if (lane < nb) sm.bsel[lane] = r < need_band;
+        }
+      } else
+      for (int b = tid; b < nb; b += 256) {
+        const double s0 = sm.bscore[b];
+        const int key = sm.bkey[b];
+        int r = 0, o = 0;
+        for (; o + 4 <= nb; o += 4) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const double so = sm.bscore[o + x];
+            r += (so > s0) || (so == s0 && sm.bkey[o + x] < key);
+          }
+        }
+        for (; o < nb; ++o) {
+          const double so = sm.bscore[o];
+          r += (so > s0) || (so == s0 && sm.bkey[o] < key);
+        }
+        sm.bsel[b] = r < need_band;
+      }
     }
-    __syncthreads();
   }
   if (tid == 0) fb_flag[i] = 0;
 
-  // Emit the kept keys in ascending order: for each window of RANK_WORDS*32 keys,
-  // mark kept keys in a bitmap; a key's output slot is the number of kept keys
-  // below it (prefix popcounts).
+  // ---- 3. kept keys in ascending order, one window of RANK_WORDS * 32 keys at a time:
+  // the kept candidates in registers plus the selected band slots (thread b owns slot b)
+  const bool band_kept = tid < nb && sm.bsel[tid];
+  const int bk = tid < nb ? sm.bkey[tid] : -1;
   int done = 0;
   for (int w0 = 0; w0 < N; w0 += RANK_WORDS * 32) {
-    for (int x = tid; x < RANK_WORDS; x += 256) bitmap[x] = 0u;
+    auto in_win = [&](int key) { return key >= w0 && key < w0 + RANK_WORDS * 32; };
+    __syncthreads();                    // the band rows (or the last window) are no longer read
+    for (int x = tid; x < RANK_WORDS / 4; x += 256) ((u32x4*)sm.bitmap)[x] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
-    for (int e = tid; e < M; e += 256) {
-      const int key = vi[e];
-      const bool kept = cls[e] == 1 || (cls[e] == 2 && bsel[bid[e]]);
-      if (kept && key >= w0 && key < w0 + RANK_WORDS * 32)
-        atomicOr(&bitmap[(key - w0) >> 5], 1u << ((key - w0) & 31));
-    }
+#pragma unroll
+    for (int j = 0; j < SR_J; ++j)
+      if (((kept >> j) & 1) && in_win(ky[j])) atomicOr(&sm.bitmap[(ky[j] - w0) >> 5], 1u << ((ky[j] - w0) & 31));
+    if (band_kept && in_win(bk)) atomicOr(&sm.bitmap[(bk - w0) >> 5], 1u << ((bk - w0) & 31));
     __syncthreads();
-    constexpr int WPT = RANK_WORDS / 256;        // words per thread
+    constexpr int WPT = RANK_WORDS / 256;        // consecutive words per thread
+    u32x4 wv[WPT / 4];
     int own = 0;
 #pragma unroll
-    for (int x = 0; x < WPT; ++x) own += __popc(bitmap[tid * WPT + x]);
+    for (int x = 0; x < WPT / 4; ++x) {
+      wv[x] = ((const u32x4*)sm.bitmap)[tid * (WPT / 4) + x];
+      own += __popc(wv[x][0]) + __popc(wv[x][1]) + __popc(wv[x][2]) + __popc(wv[x][3]);
+    }
     int incl = own;                              // inclusive scan within the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int v = __shfl_up(incl, off);
       if (lane >= off) incl += v;
     }
-    if (lane == 63) misc[4 + wave] = incl;
+    if (lane == 63) sm.misc[4 + wave] = incl;
     __syncthreads();
     int run = incl - own;
-    for (int x = 0; x < wave; ++x) run += misc[4 + x];
+    for (int x = 0; x < wave; ++x) run += sm.misc[4 + x];
 #pragma unroll
-    for (int x = 0; x < WPT; ++x) {
-      wpre[tid * WPT + x] = run;
-      run += __popc(bitmap[tid * WPT + x]);
-    }
-    const int total = misc[4] + misc[5] + misc[6] + misc[7];
-    __syncthreads();
-    for (int e = tid; e < M; e += 256) {
-      const int key = vi[e];
-      const bool kept = cls[e] == 1 || (cls[e] == 2 && bsel[bid[e]]);
-      if (kept && key >= w0 && key < w0 + RANK_WORDS * 32) {
-        const int word = (key - w0) >> 5, bit = (key - w0) & 31;
-        const int pos = done + wpre[word] + __popc(bitmap[word] & ((1u << bit) - 1u));
-        if (pos < topk) {
-          orow[pos] = key;
-          if (srow) srow[pos] = vs[e];
-        }
+    for (int x = 0; x < WPT / 4; ++x) {
+      u32x4 pre;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        pre[y] = (uint32_t)run;
+        run += __popc(wv[x][y]);
       }
+      ((u32x4*)sm.u.wpre)[tid * (WPT / 4) + x] = pre;
     }
-    done += total;
+    const int total = sm.misc[4] + sm.misc[5] + sm.misc[6] + sm.misc[7];
     __syncthreads();
+    auto emit = [&](int key, float v) {
+      const int word = (key - w0) >> 5, bit = (key - w0) & 31;
+      const int pos = done + sm.u.wpre[word] + __popc(sm.bitmap[word] & ((1u << bit) - 1u));
+      if (pos < topk) {
+        orow[pos] = key;
+        if (srow) srow[pos] = v;
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < SR_J; ++j)
+      if (((kept >> j) & 1) && in_win(ky[j])) emit(ky[j], sc[j]);
+    if (band_kept && in_win(bk)) emit(bk, sm.bval[tid]);
+    done += total;
   }
   for (int e = done + tid; e < topk; e += 256) {
     orow[e] = -1;
@@ -1283,8 +1400,8 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   pl.nstage = 1;
   // candidate capacity: what the LDS holds after the ring, per query, in multiples of 64
   pl.cap = pl.small_off ? FilterCap<uint16_t>::value : FilterCap<int>::value;
-  // the refine kernel holds nsplit * cap candidates (11 bytes each) next to SELECT_FIXED bytes
-  const int cap_sel = (int)(((163840 - SELECT_FIXED) / 11 / ns) / 64 * 64);
+  // the refine kernel holds nsplit * cap candidates (SR_MAX at most, in registers)
+  const int cap_sel = SR_MAX / ns / 64 * 64;
   if (pl.cap > cap_sel) pl.cap = cap_sel;
   {
     // Long contexts use the global-list kernel, whose lists live in memory and are
@@ -1313,9 +1430,8 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   pl.off_cand_i = take(sizeof(int) * (size_t)L * ns * pl.cap);
   pl.off_scratch = take(sizeof(double) * (size_t)pl.fb_blocks * N);
   pl.ws_bytes = off;
-  pl.filter_lds = 0;                    // all LDS of the score kernel is static
-  const size_t M = (size_t)ns * pl.cap;
-  pl.select_lds = M * 4 + M * 4 + ((M + 15) & ~(size_t)15) + ((M + 7) & ~(size_t)7) * 2 + SELECT_FIXED;
+  pl.filter_lds = 0;                    // all LDS of the score and refine kernels is static
+  pl.select_lds = 0;
   return pl;
 }
 
@@ -1331,13 +1447,6 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
   int* cand_i = (int*)(base + pl.off_cand_i);
   double* scratch = (double*)(base + pl.off_scratch);
   hipError_t e;
-  static bool attr_set = false;
-  if (!attr_set) {
-
-    e = hipFuncSetAttribute((const void*)select_refine_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   {
     KernelTrace kt("key_norm_partial", stream);
     hipLaunchKernelGGL(key_norm_partial_kernel, dim3(NORM_BLOCKS), dim3(256), 0, stream, k, N, partial);
@@ -1361,7 +1470,7 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
   }
   {
     KernelTrace kt("indexer_select_refine", stream);
-    hipLaunchKernelGGL(select_refine_kernel, dim3(L), dim3(256), pl.select_lds, stream, q, k, w, eps, L, N, topk,
+    hipLaunchKernelGGL(select_refine_kernel, dim3(L), dim3(256), 0, stream, q, k, w, eps, L, N, topk,
                        pl.nsplit, pl.cap, cand_s, cand_i, cand_n, cand_t, fb, idx_out, score_out);
   }
   {
