@@ -55,10 +55,10 @@ FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 # Counter readings (KiB per dispatch, mean of 5 launches of this workload) and a
 # digest of the kernel sources they were taken on.
 COUNTERS = {
-    "indexer_score_filter": {"fetch_kib": 202503.6, "write_kib": 39248.1,
-                             "sources": ("indexer.hip", "common.h"), "sha256_16": "aaf48d8f488a25d7"},
-    "sparse_attn": {"fetch_kib": 890765.9, "write_kib": 65536.0,
-                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "0d2630e32c2f7446"},
+    "indexer_score_filter": {"fetch_kib": 165227.3, "write_kib": 40930.9,
+                             "sources": ("indexer.hip", "common.h"), "sha256_16": "49aa37755211156f"},
+    "sparse_attn": {"fetch_kib": 890772.6, "write_kib": 65536.0,
+                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "e9a32dbacca8c11d"},
 }
 METRIC = "prefill tok/s at 128K ctx (sparse MLA); MFMA util %, HBM GB/s % of peak"
 
