@@ -12,28 +12,26 @@
 //    query's top-k selection marks in a bitmap get weight.
 //
 // Work decomposition (gfx950): one workgroup per query and 64-head group, 8
-// waves. Wave w owns the 16 heads of head group w%4 and one half h = w/4 of the
-// row: it contracts dims [288h, 288h+288) of the 576-wide score and accumulates
-// value dims [256h, 256h+256). All 64 heads share every gathered row, which is
-// read from HBM once into LDS. Per tile of 32 keys:
-//   partial S^T[32 keys x 16 heads] = K_tile[:, half] . Q^T[half]
-//                        (16x16x32 bf16 MFMA, K from LDS, Q fragments in registers)
-//   the two halves swap partials through LDS; both form S = part0 + part1 in the
-//   same order, so both run the identical online softmax per head (a head is one
-//   MFMA column: its running max and sum live in the lane owning the column,
-//   reduced across the 4 lane groups)
-//   O^T[256 x 16 heads] += V_tile^T[half] . P^T
-//                        (P^T is the softmax output in the exact register layout
-//                        the MFMA B operand wants; V^T comes from LDS by transpose
-//                        reads)
-// Splitting the row between two waves halves the per-wave registers (Q 36, O 64
-// VGPRs), which lets two waves share a SIMD and keep LDS reads in flight.
-// Row fetch: each tile's rows are loaded into registers PF tiles ahead of use
-// (five 16-byte loads per thread at most) and written to one of two LDS stages
-// just before they are needed; the tile loop is unrolled PF times so every
-// register slot is static and the compiler waits only for the loads it must.
-// The index list of a segment of up to 4096 keys is staged in LDS first, so a
-// row address never waits on an index load.
+// waves, with the 32x32x16 bf16 MFMA so that every operand fragment read from LDS
+// serves 32 heads. Waves 0-3 score: wave w contracts half w/2 (288 dims) of the
+// 576-wide score for head group w%2 (32 heads): partial S^T[32 keys x 32 heads] =
+// K_tile[:, half] . Q^T[half] (K fragments from LDS, Q^T fragments in registers),
+// written to LDS. Waves 4-7 produce output: wave 4+w owns value half w/2 (256 dims)
+// of head group w%2; it sums the two partial scores of a tile in a fixed order (so
+// both output waves of a group run the identical online softmax; a head is one MFMA
+// column, its running max and sum live in the two lanes owning the column) and
+// accumulates O^T[256 dims x 32 heads] += V_tile^T[half] . P^T (V^T fragments by
+// transpose reads from LDS, P^T already in the operand layout in registers).
+// The two roles are pipelined one tile apart: while the output waves consume the
+// scores of tile t, the score waves compute those of tile t+1, and the rows of tile
+// t+2 are written into the third LDS stage, so one barrier per tile suffices. Waves
+// w and w+4 share a SIMD: one score and one output wave each. Each role runs its own
+// loop, so its registers (Q^T for scoring, the 256x32 accumulator for output) do not
+// add up. All 64 heads share every gathered row, which is read from HBM once.
+// Row fetch: each tile's rows are loaded into registers a tile ahead of use (five
+// 16-byte loads per thread) and written to their LDS stage; the index list of a
+// segment of up to 2048 keys is staged in LDS first, so a row address never waits
+// on an index load.
 #include "common.h"
 #include "kernels.h"
 
@@ -46,16 +44,19 @@ constexpr int T = 32;                   // keys per tile
 constexpr int CH = D * 2 / 16;          // 16-byte chunks per row (72)
 constexpr int ROWCH = CH + 1;           // padded LDS row, in chunks (bank spread)
 constexpr int ROWB = ROWCH * 16;        // 1168 bytes
-constexpr int STAGE = T * ROWB;         // 37376 bytes per LDS stage (two stages)
-constexpr int PF = 2;                   // tiles in flight in registers
-constexpr int CPT = (T * CH + 511) / 512;   // 16-byte chunks per thread per tile (5)
-constexpr int SEG = 4096;               // index entries staged per segment
-constexpr int KCH = D / 32 / 2;         // MFMA k-steps per half row (9)
-constexpr int NDBH = DV / 16 / 2;       // 16-wide value blocks per half (16)
-constexpr int NW = 8;                   // waves per workgroup: 4 head groups x 2 row halves
+constexpr int STAGE = T * ROWB;         // 37376 bytes per LDS stage
+constexpr int NST = 3;                  // LDS stages: tiles t (output), t+1 (scores), t+2 (filling)
+constexpr int CPT = (CH + 15) / 16;     // 16-byte chunks per thread per tile (5): 16 threads per row
+constexpr int SEG = 2048;               // index entries staged per segment
+constexpr int KST = D / 2 / 16;         // 32x32x16 k-steps per score half (18)
+constexpr int NW = 8;                   // waves per workgroup: 4 scoring, 4 producing output
+constexpr int DH = DV / 2;              // value dims per output wave (256)
+constexpr int NDB = DH / 32;            // 32-row value blocks per output wave (8)
 constexpr float SLACK = 8.f;            // log2 of the largest unnormalised softmax weight
-constexpr int XCH_BYTES = NW * 64 * 32; // partial-score exchange: 8 floats per lane
-constexpr size_t LDS_BYTES = 2 * (size_t)STAGE + SEG * 4 + 2 * T * 4 + XCH_BYTES;
+constexpr int XCH_TILE = 4 * 4 * 64 * 16;   // partial scores of a tile: 4 score waves x 16 floats x 64 lanes
+constexpr size_t LDS_BYTES = NST * (size_t)STAGE + SEG * 4 + 16 + 2 * XCH_TILE;
+static_assert(T * 16 == 512, "sixteen threads per tile row");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
 }  // namespace
 
 // MODE: 0 dense (every visible key), 1 sparse (gathered index lists), 2 masked
@@ -70,18 +71,20 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     float scale_log2, const int32_t* __restrict__ seqlens, float* __restrict__ part, int spl) {
   constexpr bool SPARSE = MODE == 1 || MODE == 3;   // rows come from an index list
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
-  unsigned char* ring = dyn;                                // [2][STAGE]
-  int* sidx = (int*)(dyn + 2 * (size_t)STAGE);              // [SEG]
-  int* sflag = sidx + SEG;                                  // [2][T]
-  f32x4* xch = (f32x4*)(sflag + 2 * T);                     // [NW][2][64] partial scores
+  unsigned char* ring = dyn;                                // [NST][STAGE]
+  int* sidx = (int*)(dyn + NST * (size_t)STAGE);            // [SEG]
+  uint32_t* smask = (uint32_t*)(sidx + SEG);                // [NST] valid keys of the staged tile (bit r = row r)
+  f32x4* xch = (f32x4*)((unsigned char*)smask + 16);        // [2 tile parities][4 score waves][4][64]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int l32 = lane & 31, up = lane >> 5;
   const int b = blockIdx.y;
   const int i = MODE == 3 ? 0 : q0 + blockIdx.x;
-  const int hg = wave & 3, half = wave >> 2;
-  const bool wave_active = (blockIdx.z * 4 + hg) * 16 < H;
-  const int head = wave_active ? (blockIdx.z * 4 + hg) * 16 + c16 : c16;
+  const bool score_wave = wave < 4;
+  const int hg = wave & 1;
+  const int half = (wave >> 1) & 1;                         // score half, or value half of an output wave
+  const int head = blockIdx.z * 64 + 32 * hg + l32;
+  const bool head_ok = head < H;
   const int p = N - L + i;
   int count = MODE == 1 ? topk : (causal ? p + 1 : N);
   // (topk is the row-list length here; a sequence length past it is clamped to it)
@@ -93,136 +96,43 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
                                     : nullptr;
   const uint32_t* mrow = MODE == 2 ? mask + ((size_t)b * L + i) * ((N + 31) / 32) : nullptr;
 
-  bf16x8 qf[KCH];
-  {
-    const uint16_t* qrow = q + (((size_t)b * L + i) * H + head) * D + 288 * half + 8 * g;
-#pragma unroll
-    for (int kc = 0; kc < KCH; ++kc) qf[kc] = *(const bf16x8*)(qrow + 32 * kc);
-    // Consume the fragments here, so their loads are known complete before the tile loop;
-    // otherwise the loop's merged wait state would drain the row prefetch every tile.
-#pragma unroll
-    for (int kc = 0; kc < KCH; ++kc) asm volatile("" ::"v"(qf[kc]));
-  }
-  f32x4 o[NDBH];
-#pragma unroll
-  for (int db = 0; db < NDBH; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
-
-  // chunk u of this thread in a tile: c = tid + 512u (c < 32*72): row c/72, 16-byte column c%72
+  // Tile rows: thread tid handles row tid / 16 of the tile and its 16-byte columns
+  // tid % 16 + 16 u (u < CPT; columns past 71 exist only for u = 4 and are clamped
+  // for the load, not staged), so a thread looks up one key per tile and its loads
+  // and LDS writes are one base plus immediates.
+  const int frow = tid >> 4, fcol = tid & 15;
   auto key_of = [&](int t, int r, int seg_base, int seg_cnt) -> int {
     const int slot = t * T + r;
     if (slot >= seg_cnt) return -1;
     return SPARSE ? sidx[slot] : seg_base + slot;
   };
-  // Every thread issues CPT loads for every fetch, also past the tile's chunks and past
-  // the last tile (those read row 0 and are never staged), so the number of outstanding
-  // loads is the same on every path and the compiler's waits stay exact.
+  // Every thread issues CPT loads for every fetch, also past the last tile (those read
+  // row 0 and are never staged), so the number of outstanding loads is the same on
+  // every path and the compiler's waits stay exact.
   auto fetch = [&](int t, u32x4 (&dst)[CPT], int seg_base, int seg_cnt) {
+    const int key = key_of(t, frow, seg_base, seg_cnt);
+    const uint16_t* rp = kvb + (size_t)(key >= 0 ? key : 0) * D;   // invalid: row 0, masked
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = min(tid + 512 * u, T * CH - 1);
-      const int r = c / CH, col = c - r * CH;
-      const int key = key_of(t, r, seg_base, seg_cnt);
-      dst[u] = *(const u32x4*)(kvb + (size_t)(key >= 0 ? key : 0) * D + col * 8);   // invalid: row 0, masked
-    }
+    for (int u = 0; u < CPT; ++u) dst[u] = *(const u32x4*)(rp + 8 * min(fcol + 16 * u, CH - 1));
   };
   auto stage_in = [&](int t, int st_i, const u32x4 (&src)[CPT], int seg_base, int seg_cnt) {
-    unsigned char* st = ring + (size_t)st_i * STAGE;
+    unsigned char* st = ring + (size_t)st_i * STAGE + frow * ROWB + 16 * fcol;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + 512 * u;
-      if (c < T * CH) {
-        const int r = c / CH, col = c - r * CH;
-        *(u32x4*)(st + r * ROWB + col * 16) = src[u];
-      }
-    }
-    if (tid < T) {
-      bool v = key_of(t, tid, seg_base, seg_cnt) >= 0;
-      if constexpr (MODE == 2) v = v && ((mrow[(seg_base + t * T) / 32] >> tid) & 1u);
-      sflag[st_i * T + tid] = v;
+    for (int u = 0; u < CPT; ++u)
+      if (u < CPT - 1 || fcol + 16 * u < CH) *(u32x4*)(st + 256 * u) = src[u];
+    if (wave == 0) {
+      bool v = lane < T && key_of(t, lane, seg_base, seg_cnt) >= 0;
+      if constexpr (MODE == 2) v = v && ((mrow[(seg_base + t * T) / 32] >> lane) & 1u);
+      const unsigned long long bm = __ballot(v);
+      if (lane == 0) smask[st_i] = (uint32_t)bm;
     }
   };
-  u32x4 pf[PF][CPT];
-
-  // One tile. Barrier 1 publishes tile t; the partial-score exchange needs barrier 2.
-  // After the value product (stage t%2 and the exchange buffer fully read by this
-  // wave; every wave has passed barrier 2, so the other stage is free) tile t+1
-  // moves from its register slot into the other stage and the slot refetches t+1+PF.
-  auto body = [&](int t, u32x4 (&slot)[CPT], int ntiles, int seg_base, int seg_cnt) {
-    lds_barrier();
-    const int s = t & 1;
-    const unsigned char* st = ring + (size_t)s * STAGE;
-    f32x4 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const unsigned char* rowp = st + (16 * kb + c16) * ROWB + 576 * half + 16 * g;
-#pragma unroll
-      for (int kc = 0; kc < KCH; ++kc) sacc[kb] = mfma16x16x32(*(const bf16x8*)(rowp + 64 * kc), qf[kc], sacc[kb]);
-    }
-    // swap partial scores with the other half of this head group; both sum in the same order
-    xch[(wave * 2 + 0) * 64 + lane] = sacc[0];
-    xch[(wave * 2 + 1) * 64 + lane] = sacc[1];
-    lds_barrier();
-    {
-      const int pw = wave ^ 4;
-      const f32x4 o0 = xch[(pw * 2 + 0) * 64 + lane], o1 = xch[(pw * 2 + 1) * 64 + lane];
-      sacc[0] = half == 0 ? sacc[0] + o0 : o0 + sacc[0];
-      sacc[1] = half == 0 ? sacc[1] + o1 : o1 + sacc[1];
-    }
-    float x[8];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool v = sflag[s * T + 16 * kb + 4 * g + j] != 0;
-        const float xv = v ? sacc[kb][j] * scale_log2 : -INFINITY;
-        x[kb * 4 + j] = xv;
-        tmax = fmaxf(tmax, xv);
-      }
-    tmax = group4_max(tmax);
-    // The reference max moves only when a score exceeds it by more than 2^SLACK (or
-    // on the first valid key): softmax does not depend on the reference, and weights
-    // up to 2^SLACK lose nothing in bf16 / fp32, so the output rescale is rare.
-    const bool bump = tmax - m > SLACK;
-    const float mnew = bump ? tmax : m;
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    float pv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = exp2_fast(x[e] - mref);
-    // The normaliser sums the bf16-rounded weights the value product uses, so the
-    // output is an exact convex combination of those weights (a dominant key gives
-    // back its value row, whatever the rounding of its weight).
-    const bf16x8 pk = pack_bf16x8(pv);
-    const float psum = group4_sum(sum_bf16x8(pk));
-    if (__ballot(bump)) {
-      const float alpha = bump ? exp2_fast(m - mref) : 1.f;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDBH; ++db) o[db] *= alpha;
-    }
-    lsum += psum;
-    m = mnew;
-    // V^T operand: lane (g, c16) points at row 4g + c16/4 (and 16 + that), columns 4*(c16%4)
-    const unsigned char* vb = st + (4 * g + (c16 >> 2)) * ROWB + 512 * half + 8 * (c16 & 3);
-#pragma unroll
-    for (int db = 0; db < NDBH; ++db) {
-      const short4v lo = lds_read_tr16(vb + 32 * db);
-      const short4v hi = lds_read_tr16(vb + 16 * ROWB + 32 * db);
-      o[db] = mfma16x16x32(join_bf16x8(lo, hi), pk, o[db]);
-    }
-    if (t + 1 < ntiles) stage_in(t + 1, (t + 1) & 1, slot, seg_base, seg_cnt);
-    fetch(t + 1 + PF, slot, seg_base, seg_cnt);
-  };
-
-  const int nseg = count > 0 ? (SPARSE ? (count + SEG - 1) / SEG : 1) : 0;
-  for (int seg = 0; seg < nseg; ++seg) {
-    const int seg_base = SPARSE ? seg * SEG : 0;
-    const int seg_cnt = SPARSE ? min(SEG, count - seg_base) : count;
+  u32x4 pf[CPT];
+  // Index list of a segment into LDS (all of this thread's index loads in flight
+  // before any is used), then the first tiles: 0 and 1 staged, 2 in registers.
+  auto segment_start = [&](int seg_base, int seg_cnt, int ntiles) {
     if (SPARSE) {
       lds_barrier();                               // the previous segment's indices are no longer read
-      // all of this thread's index loads in flight before any is used
       constexpr int PER = SEG / (64 * NW);
       int xs[PER];
 #pragma unroll
@@ -236,40 +146,208 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
         if (e < seg_cnt) sidx[e] = (xs[u] >= 0 && xs[u] < N) ? xs[u] : -1;
       }
       lds_barrier();
+    } else {
+      lds_barrier();                               // the previous segment's stages are no longer read
     }
-    const int ntiles = (seg_cnt + T - 1) / T;
+    fetch(0, pf, seg_base, seg_cnt);
+    if (ntiles > 0) stage_in(0, 0, pf, seg_base, seg_cnt);
+    fetch(1, pf, seg_base, seg_cnt);
+    if (ntiles > 1) stage_in(1, 1, pf, seg_base, seg_cnt);
+    fetch(2, pf, seg_base, seg_cnt);
+    lds_barrier();
+  };
+  // after tile t's role work: tile t+2 into its stage (its last readers worked on
+  // tile t-1, before this tile's barrier), the register slot refetches t+3
+  auto advance = [&](int t, int ntiles, int seg_base, int seg_cnt) {
+    if (t + 2 < ntiles) stage_in(t + 2, (t + 2) % NST, pf, seg_base, seg_cnt);
+    fetch(t + 3, pf, seg_base, seg_cnt);
+  };
+
+  const int nseg = count > 0 ? (SPARSE ? (count + SEG - 1) / SEG : 1) : 0;
+
+  if (score_wave) {
+    // ---------------------------------------------------------------- scoring
+    // Q^T fragments: lane (up, l32) holds head l32 of the group, dims 288 half +
+    // 16 kc + 8 up .. +8 (zero for heads past H)
+    bf16x8 qt[KST];
+    {
+      const uint16_t* qrow = q + (((size_t)b * L + i) * H + (head_ok ? head : 0)) * D + 288 * half + 8 * up;
 #pragma unroll
-    for (int t = 0; t < PF; ++t) fetch(t, pf[t], seg_base, seg_cnt);
-    if (ntiles > 0) stage_in(0, 0, pf[0], seg_base, seg_cnt);
-    fetch(PF, pf[0], seg_base, seg_cnt);
-    // tile t+1 sits in register slot (t+1) % PF
-    static_assert(PF == 2, "the unrolled tile loop below assumes two register slots");
-    for (int t0 = 0; t0 < ntiles; t0 += PF) {
-      body(t0, pf[1], ntiles, seg_base, seg_cnt);
-      if (t0 + 1 < ntiles) body(t0 + 1, pf[0], ntiles, seg_base, seg_cnt);
+      for (int kc = 0; kc < KST; ++kc) {
+        bf16x8 v = {};
+        if (head_ok) v = *(const bf16x8*)(qrow + 16 * kc);
+        qt[kc] = v;
+      }
+      // Consume the fragments here, so their loads are known complete before the tile
+      // loop; otherwise the loop's merged wait state would drain the row prefetch.
+#pragma unroll
+      for (int kc = 0; kc < KST; ++kc) asm volatile("" ::"v"(qt[kc]));
+    }
+    const int kofs = l32 * ROWB + 576 * half + 16 * up;
+    auto score_tile = [&](int t) {
+      const unsigned char* kp = ring + (size_t)(t % NST) * STAGE + kofs;
+      f32x16 sc = {};
+      // K fragments in two batches of nine reads, each issued before its MFMAs
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 kf[KST / 2];
+#pragma unroll
+        for (int kc = 0; kc < KST / 2; ++kc) kf[kc] = *(const bf16x8*)(kp + 32 * (KST / 2 * h2 + kc));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kc = 0; kc < KST / 2; ++kc) sc = mfma32x32x16(kf[kc], qt[KST / 2 * h2 + kc], sc);
+      }
+      f32x4* xw = xch + (size_t)(((t & 1) * 4 + wave) * 4) * 64;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xw[c * 64 + lane] = f32x4{sc[4 * c], sc[4 * c + 1], sc[4 * c + 2], sc[4 * c + 3]};
+    };
+    for (int seg = 0; seg < nseg; ++seg) {
+      const int seg_base = SPARSE ? seg * SEG : 0;
+      const int seg_cnt = SPARSE ? min(SEG, count - seg_base) : count;
+      const int ntiles = (seg_cnt + T - 1) / T;
+      segment_start(seg_base, seg_cnt, ntiles);
+      if (ntiles > 0) score_tile(0);
+      for (int t = 0; t < ntiles; ++t) {
+        lds_barrier();                             // scores of t, rows of t+1 published
+        if (t + 1 < ntiles) score_tile(t + 1);
+        advance(t, ntiles, seg_base, seg_cnt);
+      }
+    }
+    return;
+  }
+
+  // ---------------------------------------------------------------- output
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, lsum = 0.f;                          // per head (lane column)
+  // V^T operand by transpose reads: lane (G = lane/16, j = lane%16) points at key row
+  // 8 (G/2) + j/4 and value dim 256 half + 16 (G%2) + 4 (j%4); the read returns dims
+  // 256 half + 16 (G%2) + j (= lane % 32) of four consecutive keys
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int voff = (8 * (g16 >> 1) + (j16 >> 2)) * ROWB + (DH * half + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
+  auto output_tile = [&](int t) {
+    const int s3 = t % NST;
+    // S = part0 + part1, in that order in both output waves of the group
+    const f32x4* x0 = xch + (size_t)(((t & 1) * 4 + hg) * 4) * 64;         // score wave hg: half 0
+    const f32x4* x1 = xch + (size_t)(((t & 1) * 4 + 2 + hg) * 4) * 64;     // score wave 2 + hg: half 1
+    // valid keys of the tile; C row of element j is key 8 (j/4) + 4 up + j%4
+    const uint32_t vm = smask[s3] >> (4 * up);
+    float x[16];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 a0 = x0[c * 64 + lane], a1 = x1[c * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * c + e;
+        x[j] = ((vm >> (8 * c + e)) & 1u) ? (a0[e] + a1[e]) * scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[j]);
+      }
+    }
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    // The reference max moves only when a score exceeds it by more than 2^SLACK (or
+    // on the first valid key): softmax does not depend on the reference, and weights
+    // up to 2^SLACK lose nothing in bf16 / fp32, so the output rescale is rare.
+    const bool bump = tmax - m > SLACK;
+    const float mnew = bump ? tmax : m;
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    float pv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pv[e] = exp2_fast(x[e] - mref);
+    // The normaliser sums the bf16-rounded weights the value product uses, so the
+    // output is an exact convex combination of those weights (a dominant key gives
+    // back its value row, whatever the rounding of its weight).
+    const bf16x8 pk0 = pack_bf16x8(pv), pk1 = pack_bf16x8(pv + 8);
+    float psum = sum_bf16x8(pk0) + sum_bf16x8(pk1);
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
+      psum = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if (__ballot(bump)) {
+      const float alpha = bump ? exp2_fast(m - mref) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    }
+    lsum += psum;
+    m = mnew;
+    // P^T operand: lane (up, l32) needs keys 16 ks + 8 up + e of head l32. It holds
+    // keys 8 g + 4 up + (0..3) for g = 0..3 (bf16 pairs: dwords 2g, 2g+1 of pk0|pk1);
+    // the swap of groups (0, 1) gives the lower lanes keys 0-7 and the upper lanes
+    // keys 8-15, that of groups (2, 3) keys 16-23 and 24-31.
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v w0 = __builtin_bit_cast(u32x4v, pk0), w1 = __builtin_bit_cast(u32x4v, pk1);
+    const auto a0 = __builtin_amdgcn_permlane32_swap(w0[0], w0[2], false, false);
+    const auto a1 = __builtin_amdgcn_permlane32_swap(w0[1], w0[3], false, false);
+    const auto b0 = __builtin_amdgcn_permlane32_swap(w1[0], w1[2], false, false);
+    const auto b1 = __builtin_amdgcn_permlane32_swap(w1[1], w1[3], false, false);
+    const bf16x8 pt0 = __builtin_bit_cast(bf16x8, u32x4v{a0[0], a1[0], a0[1], a1[1]});
+    const bf16x8 pt1 = __builtin_bit_cast(bf16x8, u32x4v{b0[0], b1[0], b0[1], b1[1]});
+    // value product in two batches of four 32-dim blocks: the eight transpose-read
+    // pairs of a batch are issued before its MFMAs
+    const unsigned char* vb = ring + (size_t)s3 * STAGE + voff;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      bf16x8 vf[NDB / 2][2];
+#pragma unroll
+      for (int d = 0; d < NDB / 2; ++d)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int db = NDB / 2 * h2 + d;
+          vf[d][ks] = join_bf16x8(lds_read_tr16(vb + (16 * ks) * ROWB + 64 * db),
+                                  lds_read_tr16(vb + (16 * ks + 4) * ROWB + 64 * db));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = 0; d < NDB / 2; ++d)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) o[NDB / 2 * h2 + d] = mfma32x32x16(vf[d][ks], ks ? pt1 : pt0, o[NDB / 2 * h2 + d]);
+    }
+  };
+  for (int seg = 0; seg < nseg; ++seg) {
+    const int seg_base = SPARSE ? seg * SEG : 0;
+    const int seg_cnt = SPARSE ? min(SEG, count - seg_base) : count;
+    const int ntiles = (seg_cnt + T - 1) / T;
+    segment_start(seg_base, seg_cnt, ntiles);
+    for (int t = 0; t < ntiles; ++t) {
+      lds_barrier();                               // scores of t, rows of t+1 published
+      output_tile(t);
+      advance(t, ntiles, seg_base, seg_cnt);
     }
   }
 
-  if (!wave_active) return;
+  if (!head_ok) return;
+  // O^T element j of block db: dim 256 half + 32 db + 8 (j/4) + 4 up + j%4 of head `head`
   if constexpr (MODE == 3) {
     // partial record of (sequence b, split x, head): 512 unnormalised output values,
     // then the running max (log2 units) and sum
     float* rec = part + (((size_t)b * gridDim.x + blockIdx.x) * H + head) * (DV + 2);
 #pragma unroll
-    for (int db = 0; db < NDBH; ++db) *(f32x4*)(rec + 256 * half + 16 * db + 4 * g) = o[db];
-    if (half == 0 && g == 0) {
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(rec + DH * half + 32 * db + 8 * g + 4 * up) =
+            f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+    if (half == 0 && up == 0) {
       rec[DV] = m;
       rec[DV + 1] = lsum;
     }
     return;
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  uint16_t* orow = out + (((size_t)b * L + i) * H + head) * DV + 256 * half + 4 * g;
+  uint16_t* orow = out + (((size_t)b * L + i) * H + head) * DV + DH * half + 4 * up;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int db = 0; db < NDBH; ++db) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    *(bf16x4*)(orow + 16 * db) = __builtin_convertvector(o[db] * inv, bf16x4);
-  }
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]} * inv;
+      *(bf16x4*)(orow + 32 * db + 8 * g) = __builtin_convertvector(v, bf16x4);
+    }
 }
 
 // One workgroup per (query, batch): the query's selection bitmap (bit n of word n/32
