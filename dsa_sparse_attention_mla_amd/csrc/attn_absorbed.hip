@@ -231,20 +231,29 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     // S = part0 + part1, in that order in both output waves of the group
     const f32x4* x0 = xch + (size_t)(((t & 1) * 4 + hg) * 4) * 64;         // score wave hg: half 0
     const f32x4* x1 = xch + (size_t)(((t & 1) * 4 + 2 + hg) * 4) * 64;     // score wave 2 + hg: half 1
-    // valid keys of the tile; C row of element j is key 8 (j/4) + 4 up + j%4
-    const uint32_t vm = smask[s3] >> (4 * up);
-    float x[16];
-    float tmax = -INFINITY;
+    // valid keys of the tile; C row of element j is key 8 (j/4) + 4 up + j%4. With all
+    // 32 keys valid and a positive scale (the usual tile) the scale goes into the
+    // exponent's fused multiply-add; otherwise scores are scaled and masked first.
+    const uint32_t vmask = smask[s3];
+    float sv[16];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const f32x4 a0 = x0[c * 64 + lane], a1 = x1[c * 64 + lane];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 4 * c + e;
-        x[j] = ((vm >> (8 * c + e)) & 1u) ? (a0[e] + a1[e]) * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[j]);
-      }
+      for (int e = 0; e < 4; ++e) sv[4 * c + e] = a0[e] + a1[e];
     }
+    const bool plain = vmask == 0xFFFFFFFFu && scale_log2 > 0.f;
+    float mul = scale_log2;
+    if (!plain) {
+      const uint32_t vm = vmask >> (4 * up);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sv[j] = ((vm >> (8 * (j >> 2) + (j & 3))) & 1u) ? sv[j] * scale_log2 : -INFINITY;
+      mul = 1.f;
+    }
+    float tmax = sv[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, sv[j]);
+    tmax *= mul;
     {
       const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
       tmax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const float mref = mnew == -INFINITY ? 0.f : mnew;
     float pv[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) pv[e] = exp2_fast(x[e] - mref);
+    for (int e = 0; e < 16; ++e) pv[e] = exp2_fast(fmaf(sv[e], mul, -mref));
     // The normaliser sums the bf16-rounded weights the value product uses, so the
     // output is an exact convex combination of those weights (a dominant key gives
     // back its value row, whatever the rounding of its weight).
