@@ -28,10 +28,11 @@
 // w and w+4 share a SIMD: one score and one output wave each. Each role runs its own
 // loop, so its registers (Q^T for scoring, the 256x32 accumulator for output) do not
 // add up. All 64 heads share every gathered row, which is read from HBM once.
-// Row fetch: each tile's rows are loaded into registers a tile ahead of use (five
-// 16-byte loads per thread) and written to their LDS stage; the index list of a
-// segment of up to 2048 keys is staged in LDS first, so a row address never waits
-// on an index load.
+// Row fetch (score waves only, so the output waves' critical path has none of it):
+// each tile's rows are loaded into registers two tiles ahead of staging (nine
+// 16-byte loads per thread, eight threads per row) and written to their LDS stage;
+// the index list of a segment of up to 2048 keys is staged in LDS first, so a row
+// address never waits on an index load.
 #include "common.h"
 #include "kernels.h"
 
@@ -46,7 +47,9 @@ constexpr int ROWCH = CH + 1;           // padded LDS row, in chunks (bank sprea
 constexpr int ROWB = ROWCH * 16;        // 1168 bytes
 constexpr int STAGE = T * ROWB;         // 37376 bytes per LDS stage
 constexpr int NST = 3;                  // LDS stages: tiles t (output), t+1 (scores), t+2 (filling)
-constexpr int CPT = (CH + 15) / 16;     // 16-byte chunks per thread per tile (5): 16 threads per row
+constexpr int FPR = 8;                  // score-wave threads per tile row in the row fetch
+constexpr int CPT = CH / FPR;           // 16-byte chunks per fetching thread per tile (9)
+constexpr int PF = 2;                   // tiles in flight in the fetching threads' registers
 constexpr int SEG = 2048;               // index entries staged per segment
 constexpr int KST = D / 2 / 16;         // 32x32x16 k-steps per score half (18)
 constexpr int NW = 8;                   // waves per workgroup: 4 scoring, 4 producing output
@@ -55,7 +58,7 @@ constexpr int NDB = DH / 32;            // 32-row value blocks per output wave (
 constexpr float SLACK = 8.f;            // log2 of the largest unnormalised softmax weight
 constexpr int XCH_TILE = 4 * 4 * 64 * 16;   // partial scores of a tile: 4 score waves x 16 floats x 64 lanes
 constexpr size_t LDS_BYTES = NST * (size_t)STAGE + SEG * 4 + 16 + 2 * XCH_TILE;
-static_assert(T * 16 == 512, "sixteen threads per tile row");
+static_assert(T * FPR == 256 && CPT * FPR == CH, "the score waves fetch whole tiles");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
 }  // namespace
 
@@ -96,30 +99,28 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
                                     : nullptr;
   const uint32_t* mrow = MODE == 2 ? mask + ((size_t)b * L + i) * ((N + 31) / 32) : nullptr;
 
-  // Tile rows: thread tid handles row tid / 16 of the tile and its 16-byte columns
-  // tid % 16 + 16 u (u < CPT; columns past 71 exist only for u = 4 and are clamped
-  // for the load, not staged), so a thread looks up one key per tile and its loads
-  // and LDS writes are one base plus immediates.
-  const int frow = tid >> 4, fcol = tid & 15;
+  // Tile rows (score waves, tid < 256): thread tid handles row tid / 8 of the tile and
+  // its 16-byte columns tid % 8 + 8 u, so a thread looks up one key per tile and its
+  // loads and LDS writes are one base plus immediates.
+  const int frow = (tid & 255) >> 3, fcol = tid & 7;
   auto key_of = [&](int t, int r, int seg_base, int seg_cnt) -> int {
     const int slot = t * T + r;
     if (slot >= seg_cnt) return -1;
     return SPARSE ? sidx[slot] : seg_base + slot;
   };
-  // Every thread issues CPT loads for every fetch, also past the last tile (those read
-  // row 0 and are never staged), so the number of outstanding loads is the same on
-  // every path and the compiler's waits stay exact.
+  // Every fetching thread issues CPT loads for every fetch, also past the last tile
+  // (those read row 0 and are never staged), so the number of outstanding loads is the
+  // same on every path and the compiler's waits stay exact.
   auto fetch = [&](int t, u32x4 (&dst)[CPT], int seg_base, int seg_cnt) {
     const int key = key_of(t, frow, seg_base, seg_cnt);
-    const uint16_t* rp = kvb + (size_t)(key >= 0 ? key : 0) * D;   // invalid: row 0, masked
+    const uint16_t* rp = kvb + (size_t)(key >= 0 ? key : 0) * D + 8 * fcol;   // invalid: row 0, masked
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) dst[u] = *(const u32x4*)(rp + 8 * min(fcol + 16 * u, CH - 1));
+    for (int u = 0; u < CPT; ++u) dst[u] = *(const u32x4*)(rp + 64 * u);
   };
   auto stage_in = [&](int t, int st_i, const u32x4 (&src)[CPT], int seg_base, int seg_cnt) {
     unsigned char* st = ring + (size_t)st_i * STAGE + frow * ROWB + 16 * fcol;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u)
-      if (u < CPT - 1 || fcol + 16 * u < CH) *(u32x4*)(st + 256 * u) = src[u];
+    for (int u = 0; u < CPT; ++u) *(u32x4*)(st + 128 * u) = src[u];
     if (wave == 0) {
       bool v = lane < T && key_of(t, lane, seg_base, seg_cnt) >= 0;
       if constexpr (MODE == 2) v = v && ((mrow[(seg_base + t * T) / 32] >> lane) & 1u);
@@ -127,12 +128,11 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
       if (lane == 0) smask[st_i] = (uint32_t)bm;
     }
   };
-  u32x4 pf[CPT];
   // Index list of a segment into LDS (all of this thread's index loads in flight
-  // before any is used), then the first tiles: 0 and 1 staged, 2 in registers.
-  auto segment_start = [&](int seg_base, int seg_cnt, int ntiles) {
+  // before any is used).
+  auto segment_indices = [&](int seg_base, int seg_cnt) {
+    lds_barrier();                                 // the previous segment's indices and stages are no longer read
     if (SPARSE) {
-      lds_barrier();                               // the previous segment's indices are no longer read
       constexpr int PER = SEG / (64 * NW);
       int xs[PER];
 #pragma unroll
@@ -146,21 +146,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
         if (e < seg_cnt) sidx[e] = (xs[u] >= 0 && xs[u] < N) ? xs[u] : -1;
       }
       lds_barrier();
-    } else {
-      lds_barrier();                               // the previous segment's stages are no longer read
     }
-    fetch(0, pf, seg_base, seg_cnt);
-    if (ntiles > 0) stage_in(0, 0, pf, seg_base, seg_cnt);
-    fetch(1, pf, seg_base, seg_cnt);
-    if (ntiles > 1) stage_in(1, 1, pf, seg_base, seg_cnt);
-    fetch(2, pf, seg_base, seg_cnt);
-    lds_barrier();
-  };
-  // after tile t's role work: tile t+2 into its stage (its last readers worked on
-  // tile t-1, before this tile's barrier), the register slot refetches t+3
-  auto advance = [&](int t, int ntiles, int seg_base, int seg_cnt) {
-    if (t + 2 < ntiles) stage_in(t + 2, (t + 2) % NST, pf, seg_base, seg_cnt);
-    fetch(t + 3, pf, seg_base, seg_cnt);
   };
 
   const int nseg = count > 0 ? (SPARSE ? (count + SEG - 1) / SEG : 1) : 0;
@@ -201,16 +187,33 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) xw[c * 64 + lane] = f32x4{sc[4 * c], sc[4 * c + 1], sc[4 * c + 2], sc[4 * c + 3]};
     };
+    u32x4 pf[PF][CPT];
+    // tile t: scores of t+1, then tile t+2 from register slot t%2 into its stage (its
+    // last readers worked on tile t-1, before this tile's barrier) and the slot
+    // refetches t+4
+    auto step = [&](int t, u32x4 (&slot)[CPT], int ntiles, int seg_base, int seg_cnt) {
+      lds_barrier();                               // scores of t, rows of t+1 published
+      if (t + 1 < ntiles) score_tile(t + 1);
+      if (t + 2 < ntiles) stage_in(t + 2, (t + 2) % NST, slot, seg_base, seg_cnt);
+      fetch(t + 2 + PF, slot, seg_base, seg_cnt);
+    };
     for (int seg = 0; seg < nseg; ++seg) {
       const int seg_base = SPARSE ? seg * SEG : 0;
       const int seg_cnt = SPARSE ? min(SEG, count - seg_base) : count;
       const int ntiles = (seg_cnt + T - 1) / T;
-      segment_start(seg_base, seg_cnt, ntiles);
+      segment_indices(seg_base, seg_cnt);
+      // tiles 0 and 1 staged, 2 and 3 in registers, scores of 0
+      fetch(0, pf[0], seg_base, seg_cnt);
+      fetch(1, pf[1], seg_base, seg_cnt);
+      if (ntiles > 0) stage_in(0, 0, pf[0], seg_base, seg_cnt);
+      if (ntiles > 1) stage_in(1, 1, pf[1], seg_base, seg_cnt);
+      fetch(2, pf[0], seg_base, seg_cnt);
+      fetch(3, pf[1], seg_base, seg_cnt);
+      lds_barrier();
       if (ntiles > 0) score_tile(0);
-      for (int t = 0; t < ntiles; ++t) {
-        lds_barrier();                             // scores of t, rows of t+1 published
-        if (t + 1 < ntiles) score_tile(t + 1);
-        advance(t, ntiles, seg_base, seg_cnt);
+      for (int t = 0; t < ntiles; t += 2) {
+        step(t, pf[0], ntiles, seg_base, seg_cnt);
+        if (t + 1 < ntiles) step(t + 1, pf[1], ntiles, seg_base, seg_cnt);
       }
     }
     return;
@@ -321,11 +324,11 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const int seg_base = SPARSE ? seg * SEG : 0;
     const int seg_cnt = SPARSE ? min(SEG, count - seg_base) : count;
     const int ntiles = (seg_cnt + T - 1) / T;
-    segment_start(seg_base, seg_cnt, ntiles);
+    segment_indices(seg_base, seg_cnt);
+    lds_barrier();                                 // tiles 0 and 1 staged, scores of 0 under way
     for (int t = 0; t < ntiles; ++t) {
       lds_barrier();                               // scores of t, rows of t+1 published
       output_tile(t);
-      advance(t, ntiles, seg_base, seg_cnt);
     }
   }
 

@@ -66,6 +66,15 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
 // every outstanding global load (vmcnt(0)), which would drain the direct-to-LDS
 // prefetch ring; tile data is instead waited for explicitly with s_waitcnt
 // vmcnt(n) before the barrier that publishes a tile.
+// 16-byte direct global->LDS load: lane l writes LDS bytes [m0 + 16 l, m0 + 16 l + 16).
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
+}
+// Same with a wave-uniform base address (SGPRs) plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

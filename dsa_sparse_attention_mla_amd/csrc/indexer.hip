@@ -578,14 +578,6 @@ static_assert(GQ * 256 <= GW * G_CB, "the prologue's histograms fit the staging 
 static_assert(G_CB >= 128, "a half-full buffer still takes a whole tile of survivors");
 }  // namespace
 
-// 16-byte direct global->LDS load: lane l writes LDS bytes [m0 + 16 l, m0 + 16 l + 16).
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_base) : "memory");
-}
-// Same with a wave-uniform base address (SGPRs) plus a per-lane 32-bit byte offset.
-__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
-}
 
 __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_list_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
