@@ -46,7 +46,7 @@ constexpr int BAND_CAP = 256;           // band entries re-scored and ranked in 
 constexpr int BIN_CAP = 1024;           // entries of the threshold bin ranked in select_refine
 constexpr int SR_J = 48;                // candidates per thread (in registers) in select_refine
 constexpr int SR_MAX = SR_J * 256;      // candidates per query select_refine holds
-constexpr int NORM_BLOCKS = 256;
+constexpr int NORM_BLOCKS = 1024;
 constexpr int FB_ROWS = 256;            // block size of the fallback kernel
 }  // namespace
 
@@ -68,18 +68,28 @@ __global__ __launch_bounds__(256) void key_norm_partial_kernel(const uint16_t* _
   __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = tid >> 4, l16 = tid & 15;   // 16 keys per pass, 16 lanes per key
+  constexpr int U = 8;                        // passes in flight per thread
   float mx = 0.f;
-  for (int n = blockIdx.x * 16 + sub; n < N; n += gridDim.x * 16) {
-    const u32x4 v = *(const u32x4*)(k + (size_t)n * ID + 8 * l16);
-    float acc = 0.f;
+  const int stride = gridDim.x * 16;
+  for (int n0 = blockIdx.x * 16 + sub; n0 < N; n0 += U * stride) {
+    u32x4 v[U];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = bf_bits2f((uint16_t)(v[e] & 0xFFFFu)), b = bf_bits2f((uint16_t)(v[e] >> 16));
-      acc += a * a + b * b;
+    for (int u = 0; u < U; ++u) {
+      const int n = n0 + u * stride;
+      v[u] = n < N ? *(const u32x4*)(k + (size_t)n * ID + 8 * l16) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
-    mx = fmaxf(mx, acc);
+    for (int u = 0; u < U; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf_bits2f((uint16_t)(v[u][e] & 0xFFFFu)), b = bf_bits2f((uint16_t)(v[u][e] >> 16));
+        acc += a * a + b * b;
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
+      mx = fmaxf(mx, acc);
+    }
   }
 #pragma unroll
   for (int off = 16; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -99,17 +109,32 @@ __global__ __launch_bounds__(64) void query_eps_kernel(const uint16_t* __restric
                                                        float* __restrict__ eps) {
   const int i = blockIdx.x, lane = threadIdx.x;
   float km = 0.f;
-  for (int b = lane; b < nparts; b += 64) km = fmaxf(km, partial[b]);
+  {
+    // all of this lane's partial maxima in flight at once (nparts = NORM_BLOCKS)
+    constexpr int PPL = NORM_BLOCKS / 64;
+    float pv[PPL];
+#pragma unroll
+    for (int x = 0; x < PPL; ++x) pv[x] = lane + 64 * x < nparts ? partial[lane + 64 * x] : 0.f;
+#pragma unroll
+    for (int x = 0; x < PPL; ++x) km = fmaxf(km, pv[x]);
+  }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) km = fmaxf(km, __shfl_xor(km, off));
   float contrib = 0.f;
   if (lane < IH) {
     const uint16_t* qh = q + ((size_t)i * IH + lane) * ID;
+    u32x4 v[ID / 8];
+#pragma unroll
+    for (int c = 0; c < ID / 8; ++c) v[c] = *(const u32x4*)(qh + 8 * c);
     float acc = 0.f;
-    for (int c = 0; c < ID; ++c) {
-      const float a = bf_bits2f(qh[c]);
-      acc += a * a;
-    }
+#pragma unroll
+    for (int c = 0; c < ID / 8; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf_bits2f((uint16_t)(v[c][e] & 0xFFFFu)), b = bf_bits2f((uint16_t)(v[c][e] >> 16));
+        acc += a * a;
+        acc += b * b;
+      }
     contrib = w[(size_t)i * IH + lane] * sqrtf(acc);
   }
 #pragma unroll
@@ -1271,6 +1296,11 @@ __global__ __launch_bounds__(FB_ROWS) void exact_fallback_kernel(
   __shared__ int wave_tot[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   double* sc = scratch + (size_t)blockIdx.x * N;
+  // this block's rows i = blockIdx.x + gridDim.x e: all flags read at once first, so a
+  // launch with no flagged row costs one load round trip
+  int any = 0;
+  for (int e = tid; blockIdx.x + gridDim.x * e < L; e += FB_ROWS) any |= fb_flag[blockIdx.x + gridDim.x * e];
+  if (!__syncthreads_or(any)) return;
   for (int i = blockIdx.x; i < L; i += gridDim.x) {
     if (fb_flag[i] == 0) continue;
     const int nv = min(N, N - L + i + 1);
