@@ -55,10 +55,10 @@ FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 # Counter readings (KiB per dispatch, mean of 5 launches of this workload) and a
 # digest of the kernel sources they were taken on.
 COUNTERS = {
-    "indexer_score_filter": {"fetch_kib": 165227.3, "write_kib": 40930.9,
-                             "sources": ("indexer.hip", "common.h"), "sha256_16": "49aa37755211156f"},
-    "sparse_attn": {"fetch_kib": 890772.6, "write_kib": 65536.0,
-                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "e9a32dbacca8c11d"},
+    "indexer_score_filter": {"fetch_kib": 165253.7, "write_kib": 40960.9,
+                             "sources": ("indexer.hip", "common.h"), "sha256_16": "6ff09890993a1c55"},
+    "sparse_attn": {"fetch_kib": 890923.1, "write_kib": 65757.8,
+                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "c5f2a2ed7c647aed"},
 }
 METRIC = "prefill tok/s at 128K ctx (sparse MLA); MFMA util %, HBM GB/s % of peak"
 
