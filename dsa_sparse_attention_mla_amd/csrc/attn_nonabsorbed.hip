@@ -15,6 +15,8 @@
 //
 // bf16 path: 16x16x32 bf16 MFMA; P is rounded to bf16 for the value product,
 // accumulation is fp32. fp32 path: 16x16x4 fp32 MFMA throughout.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -233,35 +235,58 @@ __global__ __launch_bounds__(256) void nonabsorbed_attn_kernel(
 // to back: every workgroup carries the same work, and with one workgroup per
 // compute unit none of them idles at the end.
 //
-// Workgroup: 8 waves. Wave w owns queries 32*(w%4) .. +31 of the tile (the 32
-// columns of 32x32x16 MFMAs) and key half w/4 of every 64-key step, so the two
-// waves of a query group split the keys and merge their (max, sum, output)
-// through LDS at the end of the tile.
+// Workgroup: 8 / NBLK waves. A wave owns NBLK blocks of 32 queries (the 32 columns
+// of 32x32x16 MFMAs) and one key half of every 64-key step; the two waves of a
+// query group (halves 0 and 1) merge their (max, sum, output) through LDS at the
+// end of the tile. With two blocks a wave reads each K and V^T fragment from LDS
+// once for two MFMAs.
 //
-// Keys stream through two LDS stages; the next step is loaded into registers
-// while the current one is consumed, then stored to the other stage: one
-// barrier per step.
-//
-// Per step and wave: S^T (32 keys x 32 queries) = K_row . Q^T in 12 MFMAs over
+// Per step and block: S^T (32 keys x 32 queries) = K_row . Q^T in 12 MFMAs over
 // the 192-deep [K_nope | K_rope] row; lanes l and l+32 hold the 32 scores of one
-// query; P^T rounded to bf16 is the B operand of O^T += V^T . P^T (8 MFMAs, V^T
+// query. P^T rounded to bf16 is the B operand of O^T += V^T . P^T (8 MFMAs, V^T
 // read with LDS transpose reads in the key order of the S^T accumulator layout).
+//
+// Software pipeline: step t issues the MFMAs of S(t+1) and of P(t-1) V while its
+// vector instructions turn S(t) into the weights P(t), so the exponentials of a
+// wave run under its own matrix work. The output rescale of a moved maximum is
+// applied after the value MFMAs of the step.
+//
+// K and V stream through two-stage LDS rings by direct global->LDS loads issued a
+// step ahead (K(t+2) and V(t) at the top of step t): one barrier per step.
+#ifndef NB_NBLK
+#define NB_NBLK 1
+#endif
+#ifndef NB_VALU_PER_MFMA
+#define NB_VALU_PER_MFMA 4
+#endif
 namespace {
-constexpr int NB_T = 32;                               // keys per wave per step
-constexpr int NB_KT = 2 * NB_T;                        // keys per step
-constexpr int NB_KROW = DQK * 2 + 16;                  // LDS K row: [K_nope(h) | K_rope] + pad
-constexpr int NB_VROW = DVN * 2 + 64;                  // LDS V row + pad: rows 16 banks apart, transpose reads conflict-free
-constexpr int NB_KREG = NB_KT * NB_KROW;
-constexpr int NB_STAGE = NB_KREG + NB_KT * NB_VROW;
-constexpr int NB_NW = 8;
-constexpr int NB_RCH = (DQK + DVN) * 2 / 16;           // 16-byte chunks per key: 16 K_nope, 8 K_rope, 16 V
-constexpr int NB_PER = NB_KT * NB_RCH / (NB_NW * 64);  // chunks per thread per step
-constexpr int NB_QT = 128;
-constexpr float NB_SLACK = 8.f;                        // log2 of the largest unnormalised weight
-constexpr int NB_XCH = 2 + 2 * 16;                     // merge record per lane: m, l, two output blocks
-static_assert(NB_KT * NB_RCH % (NB_NW * 64) == 0, "step chunks must divide the workgroup");
-static_assert(NB_NW * NB_XCH * 64 * 4 <= 2 * NB_STAGE, "merge area fits the stages");
+constexpr int NB_QT = 128;                              // queries per tile
+constexpr int NB_KT = 64;                               // keys per step
+constexpr int NB_NROW = DN * 2 + 16;                    // LDS K_nope row + pad (272 B)
+constexpr int NB_RROW = DR * 2 + 16;                    // LDS K_rope row + pad (144 B)
+constexpr int NB_VROW = DVN * 2 + 64;                   // LDS V row + pad: rows 16 banks apart, transpose reads conflict-free
+constexpr int NB_NCH = NB_NROW / 16, NB_RCH = NB_RROW / 16, NB_VCH = NB_VROW / 16;  // 16-byte chunks per row
+constexpr int NB_KSTAGE = NB_KT * (NB_NROW + NB_RROW);  // K_nope rows, then K_rope rows
+constexpr int NB_VSTAGE = NB_KT * NB_VROW;
+constexpr int NB_DN = NB_KT * NB_NROW / 1024;           // 1 KB direct loads per step: K_nope
+constexpr int NB_DK = NB_DN + NB_KT * NB_RROW / 1024;   // K_nope + K_rope
+constexpr int NB_DV = NB_KT * NB_VROW / 1024;           // V
+constexpr int NB_LDS = 2 * NB_KSTAGE + 2 * NB_VSTAGE;
+constexpr float NB_SLACK = 8.f;                         // log2 of the largest unnormalised weight
+constexpr int NB_XREC = 2 + 2 * 16;                     // merge record per lane and block: m, l, two output blocks
+static_assert(NB_KT * NB_NROW % 1024 == 0 && NB_KT * NB_RROW % 1024 == 0 && NB_KT * NB_VROW % 1024 == 0,
+              "rows fill whole 1 KB loads");
+static_assert(8 * NB_XREC * 64 * 4 <= NB_LDS, "merge area fits the rings");
 }  // namespace
+
+// A wave-uniform pointer, held in scalar registers (the direct loads take their
+// base address from there).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Combine lanes l and l^32 (the two row halves of a 32x32 accumulator column).
 // Both lanes see the operands in the same order, so they agree bit for bit.
@@ -274,197 +299,331 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-__global__ __launch_bounds__(512) void nonabsorbed_bf16_kernel(
-    const uint16_t* __restrict__ qn, const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kn,
-    const uint16_t* __restrict__ kr, const uint16_t* __restrict__ vv, uint16_t* __restrict__ out, int L, int N,
-    int H, int nq, int causal, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * NB_STAGE];
+template <int NBLK>
+__global__ __launch_bounds__(512 / NBLK) __attribute__((amdgpu_waves_per_eu(2 / NBLK, 2 / NBLK))) void
+nonabsorbed_bf16_kernel(const uint16_t* __restrict__ qn, const uint16_t* __restrict__ qr,
+                        const uint16_t* __restrict__ kn, const uint16_t* __restrict__ kr,
+                        const uint16_t* __restrict__ vv, uint16_t* __restrict__ out, int L, int N, int H, int nq,
+                        int causal, float scale_log2) {
+  constexpr int QG = 4 / NBLK;                  // query groups per tile
+  constexpr int NW = 2 * QG;                    // waves
+  constexpr int KSLOT = (NB_DK + NW - 1) / NW, VSLOT = (NB_DV + NW - 1) / NW;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NB_LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, g = lane >> 5;
-  const int qg = wave & 3, half = wave >> 2;
+  const int qg = wave % QG, kh = wave / QG;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int pair = blockIdx.x / H, h = blockIdx.x - pair * H, b = blockIdx.y;
-  const size_t kb0 = (size_t)b * N;
-  const float sl = scale_log2;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(DSA_LDS void*)&smem[0];
+  // With a positive scale, masks and maxima work on raw scores and the scale goes
+  // into the exponent's fused multiply-add; otherwise scores are scaled first.
+  const bool pos = scale_log2 > 0.f;
+  const float mul = pos ? scale_log2 : 1.f;
 
-  // Loads of one step (64 keys): loads 0-1 take K_nope (16 lanes per 256-byte
-  // row, keys tid/16 and 32 + tid/16), load 2 K_rope (8 lanes per 128-byte row,
-  // key tid/8), loads 3-4 V like K_nope. Keys past the context repeat the last
-  // key (their scores are masked).
-  static_assert(NB_PER == 5 && NB_KT == 64 && NB_NW * 64 == 512, "load map assumes 64 keys x 512 threads");
-  const int r16 = tid >> 4, c16b = (tid & 15) * 16, r8 = tid >> 3, c8b = (tid & 7) * 16;
-  const unsigned char* kn_b = (const unsigned char*)kn + (size_t)h * DN * 2 + c16b;
-  const unsigned char* kr_b = (const unsigned char*)kr + c8b;
-  const unsigned char* v_b = (const unsigned char*)vv + (size_t)h * DVN * 2 + c16b;
-  const size_t kstride = (size_t)H * DN * 2;
-  auto fetch = [&](u32x4 (&pf)[NB_PER], int t) {
-    const int kt = t * NB_KT;
-    const size_t ka = kb0 + min(kt + r16, N - 1), kb = kb0 + min(kt + 32 + r16, N - 1);
-    const size_t kc = kb0 + min(kt + r8, N - 1);
-    pf[0] = *(const u32x4*)(kn_b + ka * kstride);
-    pf[1] = *(const u32x4*)(kn_b + kb * kstride);
-    pf[2] = *(const u32x4*)(kr_b + kc * (DR * 2));
-    pf[3] = *(const u32x4*)(v_b + ka * kstride);
-    pf[4] = *(const u32x4*)(v_b + kb * kstride);
+  // Direct loads of one step. K load j (j < NB_DK) fills K-stage bytes
+  // [1024 j, 1024 j + 1024), lane l chunk 64 j + l of the K_nope rows (NB_NCH
+  // chunks per key, the last one padding) for j < NB_DN, else of the K_rope rows;
+  // V load v fills chunk 64 v + l of the V rows (NB_VCH chunks per key, the last
+  // four padding). A padding chunk loads the row's last data chunk again; rows past
+  // the last key repeat it (their scores are masked). Wave w issues K loads w,
+  // w + NW, ... and V loads w, w + NW, ...
+  const size_t nstride = (size_t)H * DN * 2, vstride = (size_t)H * DVN * 2;
+  constexpr int rstride = DR * 2;
+  const unsigned char* kn_b = (const unsigned char*)kn + (size_t)b * N * nstride + (size_t)h * DN * 2;
+  const unsigned char* kr_b = (const unsigned char*)kr + (size_t)b * N * rstride;
+  const unsigned char* v_b = (const unsigned char*)vv + (size_t)b * N * vstride + (size_t)h * DVN * 2;
+  // (the empty asm keeps the row arithmetic of the rare clamped tile where it is used)
+  auto k_off = [&](int j, int rmax) __attribute__((always_inline)) -> uint32_t {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    if (j < NB_DN) {
+      const int c = 64 * j + l, r = min(c / NB_NCH, rmax), u = min(c % NB_NCH, DN * 2 / 16 - 1);
+      return (uint32_t)(r * nstride) + 16 * u;
+    }
+    const int c = 64 * (j - NB_DN) + l, r = min(c / NB_RCH, rmax), u = min(c % NB_RCH, DR * 2 / 16 - 1);
+    return (uint32_t)(r * rstride) + 16 * u;
   };
-  const int ldk0 = r16 * NB_KROW + c16b, ldk1 = (32 + r16) * NB_KROW + c16b;
-  const int ldr = r8 * NB_KROW + DN * 2 + c8b;
-  const int ldv0 = NB_KREG + r16 * NB_VROW + c16b, ldv1 = NB_KREG + (32 + r16) * NB_VROW + c16b;
-  auto stage_in = [&](const u32x4 (&pf)[NB_PER], int st) {
-    unsigned char* sb = smem + st * NB_STAGE;
-    *(u32x4*)(sb + ldk0) = pf[0];
-    *(u32x4*)(sb + ldk1) = pf[1];
-    *(u32x4*)(sb + ldr) = pf[2];
-    *(u32x4*)(sb + ldv0) = pf[3];
-    *(u32x4*)(sb + ldv1) = pf[4];
+  auto v_off = [&](int v, int rmax) __attribute__((always_inline)) -> uint32_t {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    const int c = 64 * v + l, r = min(c / NB_VCH, rmax), u = min(c % NB_VCH, DVN * 2 / 16 - 1);
+    return (uint32_t)(r * vstride) + 16 * u;
+  };
+  uint32_t ko[KSLOT], vo[VSLOT];
+#pragma unroll
+  for (int s = 0; s < KSLOT; ++s) ko[s] = k_off(min(NW * s + wave_u, NB_DK - 1), NB_KT - 1);
+#pragma unroll
+  for (int s = 0; s < VSLOT; ++s) vo[s] = v_off(min(NW * s + wave_u, NB_DV - 1), NB_KT - 1);
+  // (the empty asm makes the scalar address arithmetic of a call local to it, so the
+  // compiler does not keep every slot's addresses live across the loop)
+  auto issue_k = [&](int tile, int st) __attribute__((always_inline)) {
+    int wu = wave_u;
+    asm volatile("" : "+s"(wu));
+    const int key0 = tile * NB_KT, rmax = N - 1 - key0;
+    const unsigned char* nb = kn_b + (size_t)key0 * nstride;
+    const unsigned char* rb = kr_b + (size_t)key0 * rstride;
+    const uint32_t dst = lds0 + st * NB_KSTAGE;
+#pragma unroll
+    for (int s = 0; s < KSLOT; ++s) {
+      const int j = NW * s + wu;
+      if (j < NB_DK)
+        dma16s(uniform_ptr(j < NB_DN ? nb : rb), rmax >= NB_KT - 1 ? ko[s] : k_off(j, rmax), dst + 1024 * j);
+    }
+  };
+  auto issue_v = [&](int tile, int st) __attribute__((always_inline)) {
+    int wu = wave_u;
+    asm volatile("" : "+s"(wu));
+    const int key0 = tile * NB_KT, rmax = N - 1 - key0;
+    const unsigned char* vb = v_b + (size_t)key0 * vstride;
+    const uint32_t dst = lds0 + 2 * NB_KSTAGE + st * NB_VSTAGE;
+#pragma unroll
+    for (int s = 0; s < VSLOT; ++s) {
+      const int v = NW * s + wu;
+      if (v < NB_DV) dma16s(uniform_ptr(vb), rmax >= NB_KT - 1 ? vo[s] : v_off(v, rmax), dst + 1024 * v);
+    }
+  };
+
+  // LDS fragment addresses. K (A operand of S^T): row = key 32 kh + col of the
+  // step, k = dims 16 kk + 8 g + e. V^T (A operand of O^T): lane points at key
+  // 32 kh + 16 ks + 4 g + (lane%16)/4 (+8 for the upper four k entries), dims
+  // 32 db + 16 ((lane/16)%2) + 4 (lane%4).
+  const int krow = 32 * kh + col;
+  const uint32_t ka_n = krow * NB_NROW + 16 * g, ka_r = NB_KT * NB_NROW + krow * NB_RROW + 16 * g;
+  const uint32_t va = 2 * NB_KSTAGE + (32 * kh + 4 * g + ((lane & 15) >> 2)) * NB_VROW +
+                      2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  auto kfrag = [&](int st, int kk) __attribute__((always_inline)) {
+    return *(const bf16x8*)(smem + st * NB_KSTAGE + (kk < DN / 16 ? ka_n + 32 * kk : ka_r + 32 * (kk - DN / 16)));
+  };
+  auto vfrag = [&](int st, int ks, int db) __attribute__((always_inline)) {
+    const unsigned char* p = smem + va + st * NB_VSTAGE + 16 * ks * NB_VROW + 64 * db;
+    return join_bf16x8(lds_read_tr16(p), lds_read_tr16(p + 8 * NB_VROW));
   };
 
   const int npass = (nq - 1 - pair == pair) ? 1 : 2;
   for (int pass = 0; pass < npass; ++pass) {
     const int qt = pass == 0 ? pair : nq - 1 - pair;
-    const int i0 = qt * NB_QT, iw = i0 + 32 * qg, i = iw + col;
-    const bool qvalid = i < L;
-    const int p = causal ? N - L + i : N - 1;             // last visible key of this lane's query
+    const int i0 = qt * NB_QT, iw = i0 + 32 * NBLK * qg;
     const int count = causal ? N - L + min(L - 1, i0 + NB_QT - 1) + 1 : N;
-    const int wcount = iw >= L ? 0 : (causal ? N - L + min(L - 1, iw + 31) + 1 : N);
-    const int wsafe = causal ? N - L + iw : N;            // keys below this are visible to all queries of the wave
     const int ntiles = (count + NB_KT - 1) / NB_KT;
-
-    // Query fragments (B operand): column = query, k = dims 16kk + 8g + e of [Q_nope | Q_rope].
-    bf16x8 qb[DQK / 16];
-    {
-      const size_t qrow = ((size_t)b * L + (qvalid ? i : 0)) * H + h;
+    const int plim = causal ? N - L + iw : N - 1;          // keys up to plim are visible to every query of the wave
+    int qi[NBLK], p[NBLK];
+    bf16x8 qf[NBLK][DQK / 16];
+#pragma unroll
+    for (int x = 0; x < NBLK; ++x) {
+      qi[x] = iw + 32 * x + col;
+      p[x] = causal ? N - L + qi[x] : N - 1;                // last visible key of this lane's query
+      // Query fragments (B operand): column = query, k = dims 16kk + 8g + e of [Q_nope | Q_rope].
+      const size_t qrow = ((size_t)b * L + (qi[x] < L ? qi[x] : 0)) * H + h;
 #pragma unroll
       for (int kk = 0; kk < DQK / 16; ++kk)
-        qb[kk] = kk < DN / 16 ? *(const bf16x8*)(qn + qrow * DN + 16 * kk + 8 * g)
-                              : *(const bf16x8*)(qr + qrow * DR + 16 * (kk - DN / 16) + 8 * g);
-#pragma unroll
-      for (int kk = 0; kk < DQK / 16; ++kk) asm volatile("" ::"v"(qb[kk]));
+        qf[x][kk] = kk < DN / 16 ? *(const bf16x8*)(qn + qrow * DN + 16 * kk + 8 * g)
+                                 : *(const bf16x8*)(qr + qrow * DR + 16 * (kk - DN / 16) + 8 * g);
     }
-    f32x16 o[DVN / 32];
+    f32x16 o[NBLK][DVN / 32];
 #pragma unroll
-    for (int db = 0; db < DVN / 32; ++db)
+    for (int x = 0; x < NBLK; ++x)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
-    float m = -INFINITY, lsum = 0.f;
+      for (int db = 0; db < DVN / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[x][db][j] = 0.f;
+    float m[NBLK], lsum[NBLK];
+#pragma unroll
+    for (int x = 0; x < NBLK; ++x) {
+      m[x] = -INFINITY;
+      lsum[x] = 0.f;
+    }
+    f32x16 s0[NBLK], s1[NBLK];
+    bf16x8 p0[NBLK][2], p1[NBLK][2];
 
-    // Steps alternate between LDS stages 0 and 1; the next step's rows are
-    // loaded into registers while this one is consumed.
-    auto step = [&](int t, int st) {
-      const int k0 = t * NB_KT + NB_T * half;
-      if (k0 >= wcount) return;
-      const unsigned char* ks = smem + st * NB_STAGE + NB_T * half * NB_KROW;
-      const unsigned char* vs = smem + st * NB_STAGE + NB_KREG + NB_T * half * NB_VROW;
-      f32x16 sacc;
+    // S of every block from K stage st; K fragments are read three k-steps ahead
+    auto scores = [&](int st, f32x16 (&sn)[NBLK]) __attribute__((always_inline)) {
+      bf16x8 kf[3];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
-      const unsigned char* kp = ks + col * NB_KROW + 16 * g;
-      // K fragments rotate through four registers so that four LDS reads are in
-      // flight ahead of the MFMA chain
-      bf16x8 kf[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kf[kk] = *(const bf16x8*)(kp + 32 * kk);
+      for (int kk = 0; kk < 3; ++kk) kf[kk] = kfrag(st, kk);
 #pragma unroll
       for (int kk = 0; kk < DQK / 16; ++kk) {
-        sacc = mfma32x32x16(kf[kk & 3], qb[kk], sacc);
-        if (kk + 4 < DQK / 16) kf[kk & 3] = *(const bf16x8*)(kp + 32 * (kk + 4));
+        const bf16x8 a = kf[kk % 3];
+#pragma unroll
+        for (int x = 0; x < NBLK; ++x) sn[x] = mfma32x32x16(a, qf[x][kk], kk ? sn[x] : f32x16{});
+        if (kk + 3 < DQK / 16) kf[kk % 3] = kfrag(st, kk + 3);
       }
-      // schedule: 4 LDS reads, then (MFMA, LDS read) x 8, then the last 4 MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int kk = 0; kk < DQK / 16 - 4; ++kk) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      // this lane holds keys k0 + 8*(j/4) + 4g + j%4 of query i
-      if (k0 + NB_T - 1 >= wsafe) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (k0 + 8 * (j >> 2) + 4 * g + (j & 3) > p) sacc[j] = -INFINITY;
-      }
-      float tmax = sacc[0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, sacc[j]);
-      tmax = half_max(tmax);
-      // The reference max m moves only when the new scores exceed it by more than
-      // 2^NB_SLACK (or on the first visible key): softmax does not depend on the
-      // reference, and weights up to 2^NB_SLACK are exact enough in bf16 / fp32.
-      // The output rescale then happens a few times per query instead of most steps.
-      const bool bump = (tmax - m) * sl > NB_SLACK;
-      const float mnew = bump ? tmax : m;
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float nb = -mref * sl;
-      float pv[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) pv[j] = exp2_fast(fmaf(sacc[j], sl, nb));
-      // the normaliser sums the bf16-rounded weights the value product uses
-      bf16x8 pk[2];
-      pk[0] = pack_bf16x8(pv);
-      pk[1] = pack_bf16x8(pv + 8);
-      const float psum = half_sum(sum_bf16x8(pk[0]) + sum_bf16x8(pk[1]));
-      if (__ballot(bump)) {
-        const float alpha = bump ? exp2_fast((m - mref) * sl) : 1.f;
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < DVN / 32; ++db) o[db] *= alpha;
-      }
-      lsum += psum;
-      m = mnew;
-      // V^T fragment: lane points at key 16ks + 4g + (lane%16)/4 (+8 for the upper
-      // four k entries), dims 32db + 16*((lane/16)%2) + 4*(lane%4).
-      const unsigned char* vb = vs + (4 * g + ((lane & 15) >> 2)) * NB_VROW + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int db = 0; db < DVN / 32; ++db) {
-          const short4v lo = lds_read_tr16(vb + 16 * ks2 * NB_VROW + 64 * db);
-          const short4v hi = lds_read_tr16(vb + (16 * ks2 + 8) * NB_VROW + 64 * db);
-          o[db] = mfma32x32x16(join_bf16x8(lo, hi), pk[ks2], o[db]);
-        }
     };
-
-    u32x4 pf[NB_PER];
-    fetch(pf, 0);
-    stage_in(pf, 0);
-    lds_barrier();
-    for (int t = 0; t < ntiles; ++t) {
-      fetch(pf, min(t + 1, ntiles - 1));
-      step(t, t & 1);
-      stage_in(pf, (t + 1) & 1);
+    // One pipeline step t: S(t+1) if DS, softmax of S(t) if DSM, P(t-1) V if DPV.
+    auto iter = [&](auto DS, auto DSM, auto DPV, int t, f32x16 (&sc)[NBLK], f32x16 (&sn)[NBLK],
+                    const bf16x8 (&pp)[NBLK][2], bf16x8 (&pc)[NBLK][2]) __attribute__((always_inline)) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this wave's loads of K(t+1) and V(t-1) landed
+      lds_barrier();                                       // everyone's landed; stages of K(t), V(t-2) free
+      if (DS && t + 2 < ntiles) issue_k(t + 2, t & 1);
+      if (DSM) issue_v(t, t & 1);
+      bool bump[NBLK];
+      float alpha[NBLK];
+#pragma unroll
+      for (int x = 0; x < NBLK; ++x) {
+        bump[x] = false;
+        alpha[x] = 1.f;
+      }
+      if (DSM) {
+        // keys 32 kh + 8 (j/4) + 4 g + j%4 of the step: mask what lies past the query's
+        // limit (diagonal and last steps), scale first for a non-positive scale
+        const int k0 = t * NB_KT + 32 * kh;
+        if (k0 + 31 > plim || !pos) {
+#pragma unroll
+          for (int x = 0; x < NBLK; ++x)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const float v = pos ? sc[x][j] : sc[x][j] * scale_log2;
+              sc[x][j] = k0 + 8 * (j >> 2) + 4 * g + (j & 3) <= p[x] ? v : -INFINITY;
+            }
+        }
+      }
+      if (DS) scores((t + 1) & 1, sn);
+      if (DPV) {
+        const int st = (t - 1) & 1;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < DVN / 32; ++db) {
+            const bf16x8 vf = vfrag(st, ks, db);
+#pragma unroll
+            for (int x = 0; x < NBLK; ++x) o[x][db] = mfma32x32x16(vf, pp[x][ks], o[x][db]);
+          }
+      }
+      if (DSM) {
+#pragma unroll
+        for (int x = 0; x < NBLK; ++x) {
+          float tmax = sc[x][0];
+#pragma unroll
+          for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, sc[x][j]);
+          tmax = half_max(tmax);
+          // The reference max moves only when the new scores exceed it by more than
+          // 2^NB_SLACK (or on the first visible key): softmax does not depend on the
+          // reference, and weights up to 2^NB_SLACK are exact enough in bf16 / fp32.
+          bump[x] = (tmax - m[x]) * mul > NB_SLACK;
+          const float mnew = bump[x] ? tmax : m[x];
+          const float mref = mnew == -INFINITY ? 0.f : mnew;
+          const float nb = -mref * mul;
+          float pv[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) pv[j] = exp2_fast(fmaf(sc[x][j], mul, nb));
+          float ps[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ps[e] = (pv[4 * e] + pv[4 * e + 1]) + (pv[4 * e + 2] + pv[4 * e + 3]);
+          const float psum = half_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
+          alpha[x] = bump[x] ? exp2_fast((m[x] - mref) * mul) : 1.f;
+          lsum[x] = lsum[x] * alpha[x] + psum;
+          m[x] = mnew;
+          pc[x][0] = pack_bf16x8(pv);
+          pc[x][1] = pack_bf16x8(pv + 8);
+        }
+      }
+      // Interleave for the steady-state step: every MFMA is followed by a few
+      // vector instructions of the softmax, and the LDS reads run ahead of the
+      // MFMAs that use them (K fragments three k-steps, V^T fragments two).
+      if constexpr (std::is_same<decltype(DS), std::true_type>::value &&
+                    std::is_same<decltype(DSM), std::true_type>::value &&
+                    std::is_same<decltype(DPV), std::true_type>::value) {
+        constexpr int VPM = NB_VALU_PER_MFMA;
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int kk = 0; kk < DQK / 16; ++kk) {
+#pragma unroll
+          for (int x = 0; x < NBLK; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+          }
+          if (kk + 3 < DQK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (kk == DQK / 16 - 2) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < DVN / 16; ++i) {
+#pragma unroll
+          for (int x = 0; x < NBLK; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+          }
+          if (i + 2 < DVN / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      }
+      // rescale after the value MFMAs of P(t-1), before those of P(t)
+      bool any = false;
+#pragma unroll
+      for (int x = 0; x < NBLK; ++x) any = any || bump[x];
+      if (DSM && __ballot(any)) {
+#pragma unroll
+        for (int x = 0; x < NBLK; ++x)
+#pragma unroll
+          for (int db = 0; db < DVN / 32; ++db) o[x][db] *= alpha[x];
+      }
+    };
+    // Even steps read S from s0 and write P to p0, odd steps s1 and p1; the loop
+    // runs steps in pairs, so every buffer role is fixed at compile time.
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
+    if (ntiles > 0) {
+      issue_k(0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       lds_barrier();
+      if (ntiles > 1) issue_k(1, 1);
+      scores(0, s0);
+      iter(ntiles > 1, yes, no, 0, s0, s1, p1, p0);
+      int t = 1;
+      for (; t + 2 < ntiles; t += 2) {
+        iter(yes, yes, yes, t, s1, s0, p0, p1);
+        iter(yes, yes, yes, t + 1, s0, s1, p1, p0);
+      }
+      // t is odd here and steps t .. ntiles remain (at most three)
+      if (t < ntiles) {
+        iter(t + 1 < ntiles, yes, yes, t, s1, s0, p0, p1);
+        if (t + 1 < ntiles) {
+          iter(no, yes, yes, t + 1, s0, s1, p1, p0);
+          iter(no, no, yes, t + 2, s1, s0, p0, p1);
+        } else {
+          iter(no, no, yes, t + 1, s0, s1, p1, p0);
+        }
+      } else {
+        iter(no, no, yes, t, s1, s0, p0, p1);
+      }
     }
 
     // Merge the two key halves: each wave hands over the output blocks it does
     // not write (half 0 writes dims 0-63, half 1 dims 64-127) with its m and l.
-    float* xw = (float*)smem + wave * NB_XCH * 64 + lane;
-    xw[0] = m;
-    xw[64] = lsum;
+    lds_barrier();                                         // every wave is done with the rings
+    float* xw = (float*)smem + wave * NBLK * NB_XREC * 64 + lane;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      xw[(2 + j) * 64] = o[half == 0 ? 2 : 0][j];
-      xw[(18 + j) * 64] = o[half == 0 ? 3 : 1][j];
+    for (int x = 0; x < NBLK; ++x) {
+      float* xr = xw + NB_XREC * x * 64;
+      xr[0] = m[x];
+      xr[64] = lsum[x];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        xr[(2 + j) * 64] = o[x][kh == 0 ? 2 : 0][j];
+        xr[(18 + j) * 64] = o[x][kh == 0 ? 3 : 1][j];
+      }
     }
     lds_barrier();
-    const float* xp = (const float*)smem + (wave ^ 4) * NB_XCH * 64 + lane;
-    const float m2 = xp[0], l2 = xp[64];
-    const float mx = fmaxf(m, m2);
-    const float a1 = mx == -INFINITY ? 0.f : exp2_fast((m - mx) * sl);
-    const float a2 = mx == -INFINITY ? 0.f : exp2_fast((m2 - mx) * sl);
-    const float lt = lsum * a1 + l2 * a2;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (qvalid) {
-      uint16_t* op = out + (((size_t)b * L + i) * H + h) * DVN + 4 * g;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int db = 2 * half + e;
-        const f32x16 mine = half == 0 ? o[e] : o[2 + e];
+    for (int x = 0; x < NBLK; ++x) {
+      const float* xp = (const float*)smem + ((wave + QG) % NW) * NBLK * NB_XREC * 64 + NB_XREC * x * 64 + lane;
+      const float m2 = xp[0], l2 = xp[64];
+      const float mx = fmaxf(m[x], m2);
+      const float a1 = mx == -INFINITY ? 0.f : exp2_fast((m[x] - mx) * mul);
+      const float a2 = mx == -INFINITY ? 0.f : exp2_fast((m2 - mx) * mul);
+      const float lt = lsum[x] * a1 + l2 * a2;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if (qi[x] < L) {
+        uint16_t* op = out + (((size_t)b * L + qi[x]) * H + h) * DVN + 4 * g;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          f32x4 v4;
+        for (int e = 0; e < 2; ++e) {
+          const int db = 2 * kh + e;
+          const f32x16 mine = kh == 0 ? o[x][e] : o[x][2 + e];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v4[q] = (mine[4 * jj + q] * a1 + xp[(2 + 16 * e + 4 * jj + q) * 64] * a2) * inv;
-          *(bf16x4*)(op + 32 * db + 8 * jj) = __builtin_convertvector(v4, bf16x4);
+          for (int jj = 0; jj < 4; ++jj) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            f32x4 v4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v4[q] = (mine[4 * jj + q] * a1 + xp[(2 + 16 * e + 4 * jj + q) * 64] * a2) * inv;
+            *(bf16x4*)(op + 32 * db + 8 * jj) = __builtin_convertvector(v4, bf16x4);
+          }
         }
       }
     }
@@ -472,15 +631,16 @@ __global__ __launch_bounds__(512) void nonabsorbed_bf16_kernel(
   }
 }
 
+
 hipError_t launch_nonabsorbed_attn(bool bf16, const void* qn, const void* qr, const void* kn, const void* kr,
                                    const void* v, void* out, int B, int L, int N, int H, int causal, float scale,
                                    hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   if (bf16) {
     const int nq = (L + NB_QT - 1) / NB_QT;
-    dim3 grid((nq + 1) / 2 * H, B), block(512);
+    dim3 grid((nq + 1) / 2 * H, B), block(64 * 8 / NB_NBLK);
     KernelTrace kt("nonabsorbed_attn_bf16", stream);
-    hipLaunchKernelGGL(nonabsorbed_bf16_kernel, grid, block, 0, stream, (const uint16_t*)qn, (const uint16_t*)qr,
+    hipLaunchKernelGGL(nonabsorbed_bf16_kernel<NB_NBLK>, grid, block, 0, stream, (const uint16_t*)qn, (const uint16_t*)qr,
                        (const uint16_t*)kn, (const uint16_t*)kr, (const uint16_t*)v, (uint16_t*)out, L, N, H, nq,
                        causal, scale_log2);
     return hipGetLastError();

@@ -96,6 +96,19 @@ def test_nonabsorbed_bf16_sharpened_and_first_row():
     assert np.array_equal(got[0], f["v"][0])
 
 
+@pytest.mark.parametrize("dtype,tol", [("bf16", TOL_BF16), ("f32", TOL_F32)])
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_nonabsorbed_nonpositive_scale(dtype, tol, scale):
+    """A negative scale turns the largest raw score into the smallest weight and zero gives
+    equal weights over the visible keys: masking and the running maximum have to follow the
+    scaled scores (a causal mask applied before a negative scale would give +inf)."""
+    L, N = 160, 200
+    t, f = _nonabs(49, L, N, 16, dtype, scale=0.5)
+    got = _run_nonabs(t, scale=scale)
+    ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], scale)
+    assert_close(got, ref, tol, f"nonabs {dtype} scale={scale}")
+
+
 def test_nonabsorbed_bf16_noncausal_batch():
     """Non-causal, B = 2: each entry matches the oracle and its own single-sequence call."""
     L, N, H = 70, 333, 16
@@ -144,6 +157,16 @@ def test_absorbed_sharpened():
     torch.cuda.synchronize()
     ref = oracle.mla_absorbed(qf, kvf, scale)
     assert_close(host_f64(out[0]), ref, TOL_BF16, "absorbed sharpened")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_absorbed_nonpositive_scale(scale):
+    """Non-positive scales: the kernel scales and masks before the maximum."""
+    q, kv, qf, kvf = _abs(42, 24, 90, 64)
+    out = dm.mla_prefill_dense(q[None], kv[None], scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.mla_absorbed(qf, kvf, scale)
+    assert_close(host_f64(out[0]), ref, TOL_BF16, f"absorbed scale={scale}")
 
 
 def test_absorbed_full_size_sampled():

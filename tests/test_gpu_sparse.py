@@ -33,6 +33,16 @@ def test_sparse_small(L, N, topk, pad):
     assert_close(host_f64(out), ref2, TOL_BF16, "sparse vs masked dense")
 
 
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_sparse_nonpositive_scale(scale):
+    """Non-positive scales with padded index rows: scaled before masking and the maximum."""
+    q, kv, idx, qf, kvf, idxn = _case(66, 12, 400, 80, pad=0.2)
+    out = dm.mla_prefill_sparse(q, kv, idx, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.mla_sparse_gather(qf, kvf, idxn, scale)
+    assert_close(host_f64(out), ref, TOL_BF16, f"sparse scale={scale}")
+
+
 def test_sparse_full_size_sampled():
     """N = 131072 joined rows, L = 1024 queries, top-k 2048, 64 heads: sampled rows."""
     L, N, topk = 1024, 131072, 2048
