@@ -225,12 +225,25 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   float m = -INFINITY, lsum = 0.f;                          // per head (lane column)
   // V^T operand by transpose reads: lane (G = lane/16, j = lane%16) points at key row
-  // 8 (G/2) + j/4 and value dim 256 half + 16 (G%2) + 4 (j%4); the read returns dims
-  // 256 half + 16 (G%2) + j (= lane % 32) of four consecutive keys
+  // 4 (G/2) + j/4 and value dim 256 half + 16 (G%2) + 4 (j%4); the read returns dims
+  // 256 half + 16 (G%2) + j (= lane % 32) of four consecutive keys. The upper four k
+  // entries come from eight rows further, so k entry 8 up + e of k-step ks is key
+  // 16 ks + 4 up + e (e < 4) or 16 ks + 8 + 4 up + e - 4: the key order of the score
+  // accumulator's rows, and the packed weights serve as the B operand unchanged.
   const int g16 = lane >> 4, j16 = lane & 15;
-  const int voff = (8 * (g16 >> 1) + (j16 >> 2)) * ROWB + (DH * half + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
+  const int voff = (4 * (g16 >> 1) + (j16 >> 2)) * ROWB + (DH * half + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
   auto output_tile = [&](int t) {
     const int s3 = t % NST;
+    // the first batch of V^T fragments does not depend on the scores: read it now,
+    // under the softmax
+    const unsigned char* vb = ring + (size_t)s3 * STAGE + voff;
+    bf16x8 vf0[NDB / 2][2];
+#pragma unroll
+    for (int d = 0; d < NDB / 2; ++d)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        vf0[d][ks] = join_bf16x8(lds_read_tr16(vb + (16 * ks) * ROWB + 64 * d),
+                                 lds_read_tr16(vb + (16 * ks + 8) * ROWB + 64 * d));
     // S = part0 + part1, in that order in both output waves of the group
     const f32x4* x0 = xch + (size_t)(((t & 1) * 4 + hg) * 4) * 64;         // score wave hg: half 0
     const f32x4* x1 = xch + (size_t)(((t & 1) * 4 + 2 + hg) * 4) * 64;     // score wave 2 + hg: half 1
@@ -287,37 +300,30 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     }
     lsum += psum;
     m = mnew;
-    // P^T operand: lane (up, l32) needs keys 16 ks + 8 up + e of head l32. It holds
-    // keys 8 g + 4 up + (0..3) for g = 0..3 (bf16 pairs: dwords 2g, 2g+1 of pk0|pk1);
-    // the swap of groups (0, 1) gives the lower lanes keys 0-7 and the upper lanes
-    // keys 8-15, that of groups (2, 3) keys 16-23 and 24-31.
-    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-    const u32x4v w0 = __builtin_bit_cast(u32x4v, pk0), w1 = __builtin_bit_cast(u32x4v, pk1);
-    const auto a0 = __builtin_amdgcn_permlane32_swap(w0[0], w0[2], false, false);
-    const auto a1 = __builtin_amdgcn_permlane32_swap(w0[1], w0[3], false, false);
-    const auto b0 = __builtin_amdgcn_permlane32_swap(w1[0], w1[2], false, false);
-    const auto b1 = __builtin_amdgcn_permlane32_swap(w1[1], w1[3], false, false);
-    const bf16x8 pt0 = __builtin_bit_cast(bf16x8, u32x4v{a0[0], a1[0], a0[1], a1[1]});
-    const bf16x8 pt1 = __builtin_bit_cast(bf16x8, u32x4v{b0[0], b1[0], b0[1], b1[1]});
-    // value product in two batches of four 32-dim blocks: the eight transpose-read
-    // pairs of a batch are issued before its MFMAs
-    const unsigned char* vb = ring + (size_t)s3 * STAGE + voff;
+    // P^T operand of k-step ks: this lane's weights of keys 16 ks + 4 up + (0..3) and
+    // 16 ks + 8 + 4 up + (0..3), exactly pk0 (ks = 0) and pk1 (ks = 1).
+    const bf16x8 pt0 = pk0, pt1 = pk1;
+    // value product in two batches of four 32-dim blocks; the second batch's eight
+    // transpose-read pairs are issued before its MFMAs
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+    for (int d = 0; d < NDB / 2; ++d)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) o[d] = mfma32x32x16(vf0[d][ks], ks ? pt1 : pt0, o[d]);
+    {
       bf16x8 vf[NDB / 2][2];
 #pragma unroll
       for (int d = 0; d < NDB / 2; ++d)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int db = NDB / 2 * h2 + d;
+          const int db = NDB / 2 + d;
           vf[d][ks] = join_bf16x8(lds_read_tr16(vb + (16 * ks) * ROWB + 64 * db),
-                                  lds_read_tr16(vb + (16 * ks + 4) * ROWB + 64 * db));
+                                  lds_read_tr16(vb + (16 * ks + 8) * ROWB + 64 * db));
         }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int d = 0; d < NDB / 2; ++d)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) o[NDB / 2 * h2 + d] = mfma32x32x16(vf[d][ks], ks ? pt1 : pt0, o[NDB / 2 * h2 + d]);
+        for (int ks = 0; ks < 2; ++ks) o[NDB / 2 + d] = mfma32x32x16(vf[d][ks], ks ? pt1 : pt0, o[NDB / 2 + d]);
     }
   };
   for (int seg = 0; seg < nseg; ++seg) {
