@@ -199,17 +199,15 @@ int mla_decode_paged(int B, int H, int num_pages, int page_size, int max_pages, 
   spl = (spl + 31) / 32 * 32;
   spl = spl < 256 ? 256 : (spl > 4096 ? 4096 : spl);
   const int nsplit = (int)((maxlen + spl - 1) / spl);
-  const size_t rows_bytes = ((size_t)B * maxlen * 4 + 255) / 256 * 256;
   const size_t part_bytes = (size_t)B * nsplit * H * (512 + 2) * 4;
-  const int wsr = workspace_step(rows_bytes + part_bytes, ws, ws_bytes);
+  const int wsr = workspace_step(part_bytes, ws, ws_bytes);
   if (wsr >= 0) return wsr;
   if (B == 0) return DSA_MLA_OK;
   const int a = check_arch();
   if (a != DSA_MLA_OK) return a;
-  int32_t* rows = (int32_t*)ws;
-  float* part = (float*)((unsigned char*)ws + rows_bytes);
+  float* part = (float*)ws;
   return hip_status(dsa::launch_paged_decode((const uint16_t*)q, (const uint16_t*)kv_pages, page_table, seq_lens, B,
-                                             H, num_pages, page_size, max_pages, (int)spl, nsplit, rows, part,
+                                             H, num_pages, page_size, max_pages, (int)spl, nsplit, part,
                                              (uint16_t*)out, scale, (hipStream_t)stream));
 }
 

@@ -71,7 +71,7 @@ template <int MODE>
 __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const uint32_t* __restrict__ mask, uint16_t* __restrict__ out, int L, int N, int H, int topk, int q0, int causal,
-    float scale_log2, const int32_t* __restrict__ seqlens, float* __restrict__ part, int spl) {
+    float scale_log2, const int32_t* __restrict__ seqlens, float* __restrict__ part, int spl, int psz) {
   constexpr bool SPARSE = MODE == 1 || MODE == 3;   // rows come from an index list
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   unsigned char* ring = dyn;                                // [NST][STAGE]
@@ -94,8 +94,10 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   if constexpr (MODE == 3) count = max(0, min(spl, min(seqlens[b], topk) - (int)blockIdx.x * spl));
   // paged decode: rows are physical rows of the page pool (N of them), shared by all sequences
   const uint16_t* kvb = kv + (MODE == 3 ? (size_t)0 : (size_t)b * N * D);
+  // sparse: the query's index list; paged decode: the sequence's page table row
+  // (topk = max_pages * page_size there)
   const int32_t* irow = MODE == 1   ? idx + ((size_t)b * L + i) * topk
-                        : MODE == 3 ? idx + (size_t)b * topk + (size_t)blockIdx.x * spl
+                        : MODE == 3 ? idx + (size_t)b * (topk / psz)
                                     : nullptr;
   const uint32_t* mrow = MODE == 2 ? mask + ((size_t)b * L + i) * ((N + 31) / 32) : nullptr;
 
@@ -138,7 +140,14 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
         const int e = tid + 64 * NW * u;
-        xs[u] = e < seg_cnt ? irow[seg_base + e] : -1;
+        if constexpr (MODE == 3) {
+          // position n of the sequence lives in row n % page_size of page table[n / page_size]
+          const int n = (int)blockIdx.x * spl + seg_base + e;
+          const int pg = e < seg_cnt ? irow[n / psz] : -1;
+          xs[u] = pg >= 0 && pg < N / psz ? pg * psz + n % psz : -1;
+        } else {
+          xs[u] = e < seg_cnt ? irow[seg_base + e] : -1;
+        }
       }
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
@@ -394,68 +403,79 @@ __global__ __launch_bounds__(256) void mask_rows_kernel(const int32_t* __restric
   }
 }
 
-// Row list of each sequence of a paged cache: entry n < seq_len is the physical row
-// page_table[b][n / page_size] * page_size + n % page_size (rows addressed one at a
-// time, so a tile never has to sit inside one page); -1 past the sequence, for a page
-// id outside the pool, or a position past the table.
-__global__ __launch_bounds__(256) void paged_rows_kernel(const int32_t* __restrict__ page_table,
-                                                         const int32_t* __restrict__ seqlens, int max_pages,
-                                                         int page_size, int num_pages, int32_t* __restrict__ rows) {
-  const int b = blockIdx.y;
-  const int maxlen = max_pages * page_size;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= maxlen) return;
-  const int len = seqlens[b];
-  int r = -1;
-  if (n < len) {
-    const int pg = page_table[(size_t)b * max_pages + n / page_size];
-    if (pg >= 0 && pg < num_pages) r = pg * page_size + n % page_size;
-  }
-  rows[(size_t)b * maxlen + n] = r;
-}
-
 // Merge of the split partials of one (sequence, head): out = sum_x 2^(m_x - M) O_x /
 // sum_x 2^(m_x - M) l_x with M the largest split max; splits without a visible key
-// (m = -inf) contribute nothing; a sequence with none gets zeros.
+// (m = -inf) contribute nothing; a sequence with none gets zeros. The maxima and sums
+// of all splits are reduced by the whole workgroup first; the weights of 256 splits
+// at a time then go through LDS and each thread accumulates its two output dims with
+// eight split records in flight.
+__device__ __forceinline__ float block_reduce256(float v, bool is_max, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float w = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, w) : v + w;
+  }
+  __syncthreads();                                  // earlier readers of red are done
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part, int nsplit, int H,
                                                              uint16_t* __restrict__ out) {
+  __shared__ float wsh[256];
+  __shared__ float red[4];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const float* base = part + ((size_t)b * nsplit * H + h) * (DV + 2);
   const size_t stride = (size_t)H * (DV + 2);
-  float M = -INFINITY;
-  for (int x = 0; x < nsplit; ++x) M = fmaxf(M, base[x * stride + DV]);
-  float acc0 = 0.f, acc1 = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-    for (int x = 0; x < nsplit; ++x) {
-      const float* rec = base + x * stride;
-      const float mx = rec[DV];
-      const float wgt = mx == -INFINITY ? 0.f : exp2_fast(mx - M);
-      den += wgt * rec[DV + 1];
-      acc0 += wgt * rec[2 * tid];
-      acc1 += wgt * rec[2 * tid + 1];
+  float mloc = -INFINITY;
+  for (int x = tid; x < nsplit; x += 256) mloc = fmaxf(mloc, base[x * stride + DV]);
+  const float M = block_reduce256(mloc, true, red);
+  float dl = 0.f;
+  if (M != -INFINITY)
+    for (int x = tid; x < nsplit; x += 256) {
+      const float mx = base[x * stride + DV];
+      if (mx != -INFINITY) dl += exp2_fast(mx - M) * base[x * stride + DV + 1];
     }
-  }
+  const float den = block_reduce256(dl, false, red);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 acc = {0.f, 0.f};
+  if (M != -INFINITY)
+    for (int c = 0; c < nsplit; c += 256) {
+      __syncthreads();                              // the previous chunk's weights are consumed
+      const int x = c + tid;
+      float w = 0.f;
+      if (x < nsplit) {
+        const float mx = base[(size_t)x * stride + DV];
+        w = mx == -INFINITY ? 0.f : exp2_fast(mx - M);
+      }
+      wsh[tid] = w;
+      __syncthreads();
+      const int n = min(256, nsplit - c);
+      const float* col = base + (size_t)c * stride + 2 * tid;
+      int u = 0;
+      for (; u + 8 <= n; u += 8) {
+        f32x2 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = *(const f32x2*)(col + (size_t)(u + k) * stride);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += wsh[u + k] * v[k];
+      }
+      for (; u < n; ++u) acc += wsh[u] * *(const f32x2*)(col + (size_t)u * stride);
+    }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 v = {acc0 * inv, acc1 * inv};
+  const f32x2 v = acc * inv;
   *(bf16x2*)(out + ((size_t)b * H + h) * DV + 2 * tid) = __builtin_convertvector(v, bf16x2);
 }
 
 hipError_t launch_paged_decode(const uint16_t* q, const uint16_t* kv_pages, const int32_t* page_table,
                                const int32_t* seqlens, int B, int H, int num_pages, int page_size, int max_pages,
-                               int spl, int nsplit, int32_t* rows, float* part, uint16_t* out, float scale,
-                               hipStream_t stream) {
+                               int spl, int nsplit, float* part, uint16_t* out, float scale, hipStream_t stream) {
   const int maxlen = max_pages * page_size;
-  {
-    KernelTrace kt("paged_rows", stream);
-    hipLaunchKernelGGL(paged_rows_kernel, dim3((maxlen + 255) / 256, B), dim3(256), 0, stream, page_table, seqlens,
-                       max_pages, page_size, num_pages, rows);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = launch_absorbed_attn(3, q, kv_pages, rows, nullptr, nullptr, B, 1, num_pages * page_size, H, maxlen, 0, nsplit,
-                           0, scale, stream, seqlens, part, spl);
+  hipError_t e = launch_absorbed_attn(3, q, kv_pages, page_table, nullptr, nullptr, B, 1, num_pages * page_size, H,
+                                      maxlen, 0, nsplit, 0, scale, stream, seqlens, part, spl, page_size);
   if (e != hipSuccess) return e;
   KernelTrace kt("decode_combine", stream);
   hipLaunchKernelGGL(decode_combine_kernel, dim3(H, B), dim3(DV / 2), 0, stream, part, nsplit, H, out);
@@ -473,7 +493,7 @@ hipError_t launch_mask_rows(const int32_t* idx, int B, int L, int N, int topk, u
 hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                                 const uint32_t* mask, uint16_t* out, int B, int L, int N, int H, int topk, int q0,
                                 int nq, int causal, float scale, hipStream_t stream, const int32_t* seqlens,
-                                float* part, int spl) {
+                                float* part, int spl, int psz) {
   static bool attr_set = false;
   if (!attr_set) {
     const void* fns[4] = {(const void*)absorbed_attn_kernel<0>, (const void*)absorbed_attn_kernel<1>,
@@ -490,7 +510,7 @@ hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv,
   KernelTrace kt(names[mode], stream);
 #define DSA_LAUNCH_ABS(M)                                                                                    \
   hipLaunchKernelGGL((absorbed_attn_kernel<M>), grid, block, LDS_BYTES, stream, q, kv, idx, mask, out, L, N, H, \
-                     topk, q0, causal, scale_log2, seqlens, part, spl)
+                     topk, q0, causal, scale_log2, seqlens, part, spl, psz)
   switch (mode) {
     case 1: DSA_LAUNCH_ABS(1); break;
     case 2: DSA_LAUNCH_ABS(2); break;

@@ -24,11 +24,10 @@ class KernelTrace {
 hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                                 const uint32_t* mask, uint16_t* out, int B, int L, int N, int H, int topk, int q0,
                                 int nq, int causal, float scale, hipStream_t stream, const int32_t* seqlens = nullptr,
-                                float* part = nullptr, int spl = 0);
+                                float* part = nullptr, int spl = 0, int psz = 1);
 hipError_t launch_paged_decode(const uint16_t* q, const uint16_t* kv_pages, const int32_t* page_table,
                                const int32_t* seqlens, int B, int H, int num_pages, int page_size, int max_pages,
-                               int spl, int nsplit, int32_t* rows, float* part, uint16_t* out, float scale,
-                               hipStream_t stream);
+                               int spl, int nsplit, float* part, uint16_t* out, float scale, hipStream_t stream);
 hipError_t launch_mask_rows(const int32_t* idx, int B, int L, int N, int topk, uint32_t* mask, hipStream_t stream);
 
 hipError_t launch_nonabsorbed_attn(bool bf16, const void* qn, const void* qr, const void* kn, const void* kr,

@@ -174,8 +174,8 @@ int mla_prefill_masked(int B, int L, int N, int H, const void* q, const void* kv
  * [0, num_pages) makes its rows count as absent; a sequence without rows gets
  * zeros. The keys are split across workgroups and the partial results merged
  * (flash-decoding style). Supported: B >= 0, H a multiple of 16. Needs
- * workspace: the row lists (B*max_pages*page_size int32) and the split
- * partials (query its size with ws == NULL).
+ * workspace: the split partials, B * nsplit * H * 514 floats (query its size
+ * with ws == NULL).
  */
 int mla_decode_paged(int B, int H, int num_pages, int page_size, int max_pages, const void* q, const void* kv_pages,
                      const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, void* ws,
