@@ -30,6 +30,7 @@ The line also carries:
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
        python bench.py --sweep        context sweep, sparse vs masked dense
        python bench.py --copy-calibration MIB
+       python bench.py --dense-only   the two dense configurations alone
 """
 from __future__ import annotations
 
@@ -55,10 +56,10 @@ FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 # Counter readings (KiB per dispatch, mean of 5 launches of this workload) and a
 # digest of the kernel sources they were taken on.
 COUNTERS = {
-    "indexer_score_filter": {"fetch_kib": 165253.7, "write_kib": 40960.9,
+    "indexer_score_filter": {"fetch_kib": 165228.7, "write_kib": 40957.1,
                              "sources": ("indexer.hip", "common.h"), "sha256_16": "6ff09890993a1c55"},
-    "sparse_attn": {"fetch_kib": 890923.1, "write_kib": 65757.8,
-                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "c5f2a2ed7c647aed"},
+    "sparse_attn": {"fetch_kib": 891033.7, "write_kib": 65941.7,
+                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "ae121a9715755921"},
 }
 METRIC = "prefill tok/s at 128K ctx (sparse MLA); MFMA util %, HBM GB/s % of peak"
 
@@ -176,6 +177,27 @@ def decode_config(dm, torch, B=8, n=131072, page_size=64, reps=10):
             "tflops": B * n * H * 2176 / ms / 1e9}
 
 
+def sparse_cold(dm, torch, q, kv, idx, out, reps=5):
+    """Sparse attention with cold caches: a 512 MB fill (twice the 256 MB last-level cache)
+    runs before each timed call, so the gathered rows come from HBM. Median of reps calls."""
+    ev = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ts = []
+    for r in range(reps + 1):
+        ev.fill_(r & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dm.mla_prefill_sparse(q, kv, idx, out=out, query_block=1024)
+        b.record()
+        torch.cuda.synchronize()
+        if r:
+            ts.append(a.elapsed_time(b))
+    del ev
+    ms = sorted(ts)[len(ts) // 2]
+    by = sparse_attn_bytes(L, TOPK, H)
+    return {"ms": ms, "achieved_GBs": by / (ms * 1e-3) / 1e9, "frac_hbm": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "protocol": f"512 MB fill before each call, median of {reps}"}
+
+
 def masked_baseline(dm, torch, q, kv, idx, t_sparse_ms, step_ms, reps=3):
     """The path the sparse call replaces, on the same chunk: dense absorbed attention over
     every visible key under the same top-k selection ("Sparse prefill for GLM", "The dense
@@ -250,6 +272,8 @@ def main():
                     help="only run the context sweep (sparse vs masked dense, N = 4K..128K, L = 512/1024)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
+    ap.add_argument("--dense-only", action="store_true",
+                    help="only time the two dense MLA configurations (for counter runs) and print them")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -262,6 +286,10 @@ def main():
 
     import torch
     import dsa_sparse_attention_mla_amd as dm
+
+    if args.dense_only:
+        print(json.dumps(dense_configs(dm, torch)), flush=True)
+        return
     from synth import gen_dsa_prefill
     sys.path.insert(0, os.path.join(HERE, "tests"))
     from gpu_util import dev
@@ -317,7 +345,10 @@ def main():
 
     other = None
     baseline = None
+    cold = None
     if not args.no_other_configs:
+        log("bench: sparse attention, cold caches")
+        cold = sparse_cold(dm, torch, q, kv, idx, out)
         log("bench: dense configurations")
         other = dense_configs(dm, torch)
         log("bench: masked dense baseline")
@@ -343,7 +374,8 @@ def main():
                       "sparse_attn": t_att},
         "sparse_attn_roofline": {"achieved_GBs": sparse_attn_bytes(L, TOPK, H) / (t_att * 1e-3) / 1e9 if t_att else None,
                                  "frac_hbm": sparse_attn_bytes(L, TOPK, H) / (t_att * 1e-3) / 1e9 / PEAK_HBM_GBS if t_att else None,
-                                 "tflops": sparse_attn_flops(L, TOPK, H) / (t_att * 1e-3) / 1e12 if t_att else None},
+                                 "tflops": sparse_attn_flops(L, TOPK, H) / (t_att * 1e-3) / 1e12 if t_att else None,
+                                 "caches": "warm (the bench step's own)", "cold": cold},
         "other_configs": other,
         "dense_baseline": baseline,
     }
