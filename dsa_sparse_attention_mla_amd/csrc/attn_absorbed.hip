@@ -52,6 +52,11 @@ constexpr int CPT = CH / FPR;           // 16-byte chunks per fetching thread pe
 constexpr int PF = 2;                   // tiles in flight in the fetching threads' registers
 constexpr int SEG = 2048;               // index entries staged per segment
 constexpr int KST = D / 2 / 16;         // 32x32x16 k-steps per score half (18)
+// Score accumulator row c = 4m + e (m < 8, e < 4) holds tile row krow(c) =
+// m%4 + 4e + 16(m/4): the four rows one transpose read of V^T covers are then four
+// apart, 144 bytes of bank offset each with 1168-byte rows, so a 32-lane read
+// touches every bank once, and the 16 rows of a K fragment read stay distinct.
+__device__ __forceinline__ int krow(int c) { return ((c >> 2) & 3) + 4 * (c & 3) + 16 * (c >> 4); }
 constexpr int NW = 8;                   // waves per workgroup: 4 scoring, 4 producing output
 constexpr int DH = DV / 2;              // value dims per output wave (256)
 constexpr int NDB = DH / 32;            // 32-row value blocks per output wave (8)
@@ -178,7 +183,8 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
 #pragma unroll
       for (int kc = 0; kc < KST; ++kc) asm volatile("" ::"v"(qt[kc]));
     }
-    const int kofs = l32 * ROWB + 576 * half + 16 * up;
+    // lane (up, l32) reads K fragments of tile row krow(l32): accumulator row l32
+    const int kofs = krow(l32) * ROWB + 576 * half + 16 * up;
     auto score_tile = [&](int t) {
       const unsigned char* kp = ring + (size_t)(t % NST) * STAGE + kofs;
       f32x16 sc = {};
@@ -233,14 +239,15 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   float m = -INFINITY, lsum = 0.f;                          // per head (lane column)
-  // V^T operand by transpose reads: lane (G = lane/16, j = lane%16) points at key row
-  // 4 (G/2) + j/4 and value dim 256 half + 16 (G%2) + 4 (j%4); the read returns dims
-  // 256 half + 16 (G%2) + j (= lane % 32) of four consecutive keys. The upper four k
-  // entries come from eight rows further, so k entry 8 up + e of k-step ks is key
-  // 16 ks + 4 up + e (e < 4) or 16 ks + 8 + 4 up + e - 4: the key order of the score
-  // accumulator's rows, and the packed weights serve as the B operand unchanged.
+  // V^T operand by transpose reads: lane (G = lane/16, j = lane%16) points at tile row
+  // G/2 + 4 (j/4) (+16 ks, +2 for the upper four k entries) and value dim 256 half +
+  // 16 (G%2) + 4 (j%4); the read returns dims 256 half + 16 (G%2) + j (= lane % 32) of
+  // the four rows its lane groups point at. Those are tile rows krow(c) of the score
+  // accumulator rows c = 16 ks + 4 up + e and 16 ks + 8 + 4 up + e (e < 4): k entry
+  // 8 up + e of k-step ks follows the accumulator's row order, so the packed weights
+  // serve as the B operand unchanged.
   const int g16 = lane >> 4, j16 = lane & 15;
-  const int voff = (4 * (g16 >> 1) + (j16 >> 2)) * ROWB + (DH * half + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
+  const int voff = ((g16 >> 1) + 4 * (j16 >> 2)) * ROWB + (DH * half + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
   auto output_tile = [&](int t) {
     const int s3 = t % NST;
     // the first batch of V^T fragments does not depend on the scores: read it now,
@@ -252,11 +259,12 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         vf0[d][ks] = join_bf16x8(lds_read_tr16(vb + (16 * ks) * ROWB + 64 * d),
-                                 lds_read_tr16(vb + (16 * ks + 8) * ROWB + 64 * d));
+                                 lds_read_tr16(vb + (16 * ks + 2) * ROWB + 64 * d));
     // S = part0 + part1, in that order in both output waves of the group
     const f32x4* x0 = xch + (size_t)(((t & 1) * 4 + hg) * 4) * 64;         // score wave hg: half 0
     const f32x4* x1 = xch + (size_t)(((t & 1) * 4 + 2 + hg) * 4) * 64;     // score wave 2 + hg: half 1
-    // valid keys of the tile; C row of element j is key 8 (j/4) + 4 up + j%4. With all
+    // valid keys of the tile; element j sits in accumulator row c = 8 (j/4) + 4 up + j%4,
+    // tile row krow(c) = up + 2 ((j/4)%2) + 16 (j/8) + 4 (j%4). With all
     // 32 keys valid and a positive scale (the usual tile) the scale goes into the
     // exponent's fused multiply-add; otherwise scores are scaled and masked first.
     const uint32_t vmask = smask[s3];
@@ -270,9 +278,10 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const bool plain = vmask == 0xFFFFFFFFu && scale_log2 > 0.f;
     float mul = scale_log2;
     if (!plain) {
-      const uint32_t vm = vmask >> (4 * up);
+      const uint32_t vm = vmask >> up;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sv[j] = ((vm >> (8 * (j >> 2) + (j & 3))) & 1u) ? sv[j] * scale_log2 : -INFINITY;
+      for (int j = 0; j < 16; ++j)
+        sv[j] = ((vm >> (2 * ((j >> 2) & 1) + 16 * (j >> 3) + 4 * (j & 3))) & 1u) ? sv[j] * scale_log2 : -INFINITY;
       mul = 1.f;
     }
     float tmax = sv[0];
@@ -326,7 +335,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
         for (int ks = 0; ks < 2; ++ks) {
           const int db = NDB / 2 + d;
           vf[d][ks] = join_bf16x8(lds_read_tr16(vb + (16 * ks) * ROWB + 64 * db),
-                                  lds_read_tr16(vb + (16 * ks + 8) * ROWB + 64 * db));
+                                  lds_read_tr16(vb + (16 * ks + 2) * ROWB + 64 * db));
         }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
