@@ -52,6 +52,15 @@ constexpr int CPT = CH / FPR;           // 16-byte chunks per fetching thread pe
 constexpr int PF = 2;                   // tiles in flight in the fetching threads' registers
 constexpr int SEG = 2048;               // index entries staged per segment
 constexpr int KST = D / 2 / 16;         // 32x32x16 k-steps per score half (18)
+// A wave-uniform pointer, held in scalar registers (direct loads take their base
+// address from there).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Score accumulator row c = 4m + e (m < 8, e < 4) holds tile row krow(c) =
 // m%4 + 4e + 16(m/4): the four rows one transpose read of V^T covers are then four
 // apart, 144 bytes of bank offset each with 1168-byte rows, so a 32-lane read
@@ -212,6 +221,56 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
       if (t + 2 < ntiles) stage_in(t + 2, (t + 2) % NST, slot, seg_base, seg_cnt);
       fetch(t + 2 + PF, slot, seg_base, seg_cnt);
     };
+    if constexpr (!SPARSE) {
+      // Contiguous rows (dense and masked dense): direct global->LDS loads. Stage chunk
+      // c (16 bytes, c < T * ROWC) is chunk c % ROWC of row c / ROWC (ROWC - 1 data
+      // chunks and the padding, which loads the row's last data chunk again); load j
+      // (1 KB) covers chunks 64 j .. 64 j + 63 and score wave w issues loads w, w + 4,
+      // ...; rows past the last key repeat it (their scores are masked).
+      constexpr int ROWC = ROWB / 16, NCH = T * ROWC, NLD = (NCH + 63) / 64, LPW = (NLD + 3) / 4;
+      const uint32_t lds_ring = (uint32_t)(uintptr_t)(DSA_LDS void*)ring;
+      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+      uint32_t doff[LPW];
+      int drow[LPW];
+#pragma unroll
+      for (int s2 = 0; s2 < LPW; ++s2) {
+        const int c = 64 * (4 * s2 + wave_u) + lane;
+        drow[s2] = c / ROWC;
+        doff[s2] = (uint32_t)(drow[s2] * D * 2 + 16 * min(c % ROWC, D * 2 / 16 - 1));
+      }
+      auto dma_tile = [&](int t, int st_i) {
+        const int rmax = count - 1 - t * T;          // last row of the tile that is a key
+        const void* base = uniform_ptr(kvb + (size_t)t * T * D);
+#pragma unroll
+        for (int s2 = 0; s2 < LPW; ++s2) {
+          const int j = 4 * s2 + wave_u;
+          if (j < NLD && 64 * j + lane < NCH) {
+            const uint32_t off = rmax >= T - 1 ? doff[s2] : doff[s2] - (uint32_t)((drow[s2] - min(drow[s2], rmax)) * D * 2);
+            dma16s(base, off, lds_ring + st_i * STAGE + 1024 * j);
+          }
+        }
+        if (wave == 0) {
+          bool v = lane < T && t * T + lane < count;
+          if constexpr (MODE == 2) v = v && ((mrow[t] >> lane) & 1u);
+          const unsigned long long bm = __ballot(v);
+          if (lane == 0) smask[st_i] = (uint32_t)bm;
+        }
+      };
+      const int ntiles = (count + T - 1) / T;
+      segment_indices(0, count);
+      if (ntiles > 0) dma_tile(0, 0);
+      if (ntiles > 1) dma_tile(1, 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      if (ntiles > 0) score_tile(0);
+      for (int t = 0; t < ntiles; ++t) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile t+1 landed
+        lds_barrier();                                       // scores of t, rows of t+1 published
+        if (t + 1 < ntiles) score_tile(t + 1);
+        if (t + 2 < ntiles) dma_tile(t + 2, (t + 2) % NST);
+      }
+      return;
+    }
     for (int seg = 0; seg < nseg; ++seg) {
       const int seg_base = SPARSE ? seg * SEG : 0;
       const int seg_cnt = SPARSE ? min(SEG, count - seg_base) : count;
