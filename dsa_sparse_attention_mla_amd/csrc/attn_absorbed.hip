@@ -52,15 +52,6 @@ constexpr int CPT = CH / FPR;           // 16-byte chunks per fetching thread pe
 constexpr int PF = 2;                   // tiles in flight in the fetching threads' registers
 constexpr int SEG = 2048;               // index entries staged per segment
 constexpr int KST = D / 2 / 16;         // 32x32x16 k-steps per score half (18)
-// A wave-uniform pointer, held in scalar registers (direct loads take their base
-// address from there).
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
 // Score accumulator row c = 4m + e (m < 8, e < 4) holds tile row krow(c) =
 // m%4 + 4e + 16(m/4): the four rows one transpose read of V^T covers are then four
 // apart, 144 bytes of bank offset each with 1168-byte rows, so a 32-lane read

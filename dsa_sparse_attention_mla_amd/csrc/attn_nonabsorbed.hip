@@ -279,15 +279,6 @@ static_assert(NB_KT * NB_NROW % 1024 == 0 && NB_KT * NB_RROW % 1024 == 0 && NB_K
 static_assert(8 * NB_XREC * 64 * 4 <= NB_LDS, "merge area fits the rings");
 }  // namespace
 
-// A wave-uniform pointer, held in scalar registers (the direct loads take their
-// base address from there).
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
 // Combine lanes l and l^32 (the two row halves of a 32x32 accumulator column).
 // Both lanes see the operands in the same order, so they agree bit for bit.
 __device__ __forceinline__ float half_max(float x) {

@@ -75,6 +75,16 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
 }
 
+// A wave-uniform pointer, moved to scalar registers (direct loads take their base
+// address from there). Both halves are read as unsigned 32-bit values, so the low
+// word is zero-extended when the halves are joined.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
