@@ -66,6 +66,17 @@ def test_decode_long_contexts():
     assert_close(got, ref, TOL_BF16, "paged decode 131072 / 70001")
 
 
+def test_decode_one_sequence_many_splits():
+    """B = 1 over 130999 keys: the keys split 512 ways (more than the combine's 256 splits
+    per pass), the last split holds only part of a tile."""
+    lens = [130999]
+    pages, q, table, ln = _paged_case(215, lens, 64, spare_pages=2)
+    got = _run(pages, q, table, ln)
+    ref = oracle.mla_decode_paged(bf16_to_f32(q).astype(np.float64), bf16_to_f32(pages).astype(np.float64), table,
+                                  ln, SCALE)
+    assert_close(got, ref, TOL_BF16, "paged decode, one sequence of 130999 keys")
+
+
 def test_decode_page_outside_pool_counts_as_absent():
     lens = [300]
     pages, q, table, ln = _paged_case(220, lens, 32)
