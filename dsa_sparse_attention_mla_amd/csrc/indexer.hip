@@ -849,16 +849,19 @@ __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     else if (third) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((G_NST - 2) * 3) : "memory");
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"((G_NST - 2) * 2) : "memory");
     lds_barrier();                      // tile t landed; every wave is done with tile t - 1
-    dma_main(min(t + G_NST - 1, ntiles - 1), (t + G_NST - 1) % G_NST);
     // the MFMAs go first when several waves of a SIMD are ready; the VALU work of
     // the others fills in behind them
     __builtin_amdgcn_s_setprio(1);
     const float pb = phase_a(t % G_NST);   // + chain-b sums of tile t - 1
-    const float pa_t = phase_b(t % G_NST); // + chain-a sums of tile t
     __builtin_amdgcn_s_setprio(0);
-    // tile t - 1 (nothing is kept at t = 0, whose previous-tile sums are zeros)
+    // Between the two phases, while the other waves of the SIMD keep its matrix pipe
+    // busy: the survivors of tile t - 1 (nothing is kept at t = 0, whose
+    // previous-tile sums are zeros) and the loads of tile t + G_NST - 1.
     flushed = stage_keep(t - 1, combine(pa, pb), t > 0);
-    pa = pa_t;
+    dma_main(min(t + G_NST - 1, ntiles - 1), (t + G_NST - 1) % G_NST);
+    __builtin_amdgcn_s_setprio(1);
+    pa = phase_b(t % G_NST);               // + chain-a sums of tile t
+    __builtin_amdgcn_s_setprio(0);
   }
   if (ntiles > 0) stage_keep(ntiles - 1, combine(pa, tail_b()), true);
   if (cnt > 0) flush();
