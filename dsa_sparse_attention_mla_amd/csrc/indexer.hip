@@ -11,7 +11,7 @@
 // Pipeline, all on the caller's stream:
 //  1. key_norm_partial:   per-block max of ||k_n||^2 (fp32).
 //  2. query_eps:          eps_i, a rigorous bound on |s_hat - s| for the fp32
-//                         MFMA score s_hat, from sum_h w_h ||q_h|| * max_n ||k_n||.
+//                         MFMA score s_hat, from sum_h |w_h| ||q_h|| * max_n ||k_n||.
 //  3. score_filter:       32x32x16 bf16 MFMA scores for 32 heads; ReLU, weight and
 //                         head sum in registers; every wave owns one query and keeps
 //                         a candidate list in LDS of all keys with
@@ -55,9 +55,9 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Half-width of the uncertainty band around a threshold t (t >= 0): 2*eps plus
-// a few ulps of t for the fp32 evaluation of t +- 2*eps. Increasing in t with
-// slope < 1, so t1 <= t2 implies t1 - band(t1) <= t2 - band(t2).
+// Half-width of the uncertainty band around a threshold t (of either sign): 2*eps
+// plus a few ulps of t for the fp32 evaluation of t +- 2*eps. Its slope in t is
+// below 1 in magnitude, so t1 <= t2 implies t1 - band(t1) <= t2 - band(t2).
 __device__ __forceinline__ float band_halfwidth(float eps, float t) {
   return 2.0f * eps * 1.001f + fabsf(t) * 4.8e-7f;
 }
@@ -101,7 +101,8 @@ __global__ __launch_bounds__(256) void key_norm_partial_kernel(const uint16_t* _
 // ---------------------------------------------------------------- 2. eps per query
 // |fl(q.k) - q.k| <= gamma_128 * sum|q_c k_c| <= gamma_128 ||q|| ||k|| (any order,
 // round-to-nearest or toward zero: u = 2^-23); the ReLU is 1-Lipschitz; the
-// weight product and the 32-term head sum add (u + gamma_32) * sum_h w_h |d_h|.
+// weight product and the 32-term head sum add (u + gamma_32) * sum_h |w_h| |d_h|
+// (weights of either sign).
 // The constant below is that sum (1.92e-5) with a 30% margin for the fp32
 // evaluation of the norms.
 __global__ __launch_bounds__(64) void query_eps_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(64) void query_eps_kernel(const uint16_t* __restric
         acc += a * a;
         acc += b * b;
       }
-    contrib = w[(size_t)i * IH + lane] * sqrtf(acc);
+    contrib = fabsf(w[(size_t)i * IH + lane]) * sqrtf(acc);
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) contrib += __shfl_xor(contrib, off);
@@ -1042,9 +1043,15 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
     for (int j = 0; j < SR_J; ++j)
       if (j < jw && ky[j] >= 0) kept |= 1ull << j;
   } else {
+    // fewer candidates than topk: a sampled start threshold was set too high
+    if (M < topk) {
+      if (tid == 0) fb_flag[i] = 1;
+      return;
+    }
     // ---- 1. tk, the topk-th largest score: a 256-bin histogram linear in the
     // order-preserving integer image of the scores (so a heavy low tail spreads over
-    // many bins), then an exact rank count inside the bin that holds it
+    // many bins), narrowed by further 8-bit digits while the bin that holds it is
+    // too full, then an exact rank count inside that bin
     uint32_t umx = 0u, umn = 0xFFFFFFFFu;
 #pragma unroll
     for (int j = 0; j < SR_J; ++j)
@@ -1073,51 +1080,75 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
       // all scores equal
       tk = __uint_as_float((umx & 0x80000000u) ? (umx & 0x7FFFFFFFu) : ~umx);
     } else {
+      // Radix descent: the entries still in play are those with (d >> hi_sh) == sel,
+      // d = ord_bits - umn; each level histograms the next digit (d >> sh) - (sel <<
+      // (hi_sh - sh)) of those entries and keeps the bin of the need-th largest. The
+      // first level covers the whole span; further levels of 8 bits run only while
+      // the bin holds more entries than the exact rank step takes.
+      int sh = shift, hi_sh = 32, need = topk, cnt = 0;
+      uint64_t sel = 0;
+      for (;;) {
+        const uint64_t base = sel << (hi_sh - sh);
 #pragma unroll
-      for (int j = 0; j < SR_J; ++j)
-        if (j < jw && ky[j] >= 0) atomicAdd(&sm.hist[wave][(ord_bits(sc[j]) - umn) >> shift], 1);
-      __syncthreads();
-      sm.hist[0][tid] += sm.hist[1][tid] + sm.hist[2][tid] + sm.hist[3][tid];
-      __syncthreads();
-      if (wave == 0) {
-        int bin, above;
-        wave_find_bin(sm.hist[0], topk, lane, bin, above);
-        if (lane == 0) {
-          sm.misc[0] = bin;
-          sm.misc[1] = above;
+        for (int j = 0; j < SR_J; ++j)
+          if (j < jw && ky[j] >= 0) {
+            const uint64_t d = ord_bits(sc[j]) - umn;
+            if ((d >> hi_sh) == sel) atomicAdd(&sm.hist[wave][(int)((d >> sh) - base)], 1);
+          }
+        __syncthreads();
+        sm.hist[0][tid] += sm.hist[1][tid] + sm.hist[2][tid] + sm.hist[3][tid];
+        __syncthreads();
+        if (wave == 0) {
+          int bin, above;
+          wave_find_bin(sm.hist[0], need, lane, bin, above);
+          if (lane == 0) {
+            sm.misc[0] = bin;
+            sm.misc[1] = above;
+          }
         }
-      }
-      __syncthreads();
-      const uint32_t bin = (uint32_t)sm.misc[0];
-      const int need = topk - sm.misc[1];
+        __syncthreads();
+        const int bin = sm.misc[0];
+        need -= sm.misc[1];
+        cnt = sm.hist[0][bin];
+        sel = base + (uint64_t)bin;
+        hi_sh = sh;
+        if (cnt <= BIN_CAP || sh == 0) break;
+        sh = sh >= 8 ? sh - 8 : 0;
+        __syncthreads();                  // every thread has read the histogram
 #pragma unroll
-      for (int j = 0; j < SR_J; ++j)
-        if (j < jw && ky[j] >= 0 && ((ord_bits(sc[j]) - umn) >> shift) == bin) {
-          const int slot = atomicAdd(&sm.misc[2], 1);
-          if (slot < BIN_CAP) sm.binv[slot] = sc[j];
-        }
-      __syncthreads();
-      const int nbin = sm.misc[2];
-      if (nbin > BIN_CAP) {
-        if (tid == 0) fb_flag[i] = 1;
-        return;
+        for (int x = 0; x < 4; ++x) sm.hist[x][tid] = 0;
+        __syncthreads();
       }
-      // the need-th largest inside the bin: the largest v with #{u >= v} >= need
-      float best = -INFINITY;
-      for (int e = tid; e < nbin; e += 256) {
-        const float v = sm.binv[e];
-        int c = 0, f = 0;
-        for (; f + 4 <= nbin; f += 4) {
-          const float4 u = *(const float4*)&sm.binv[f];
-          c += (u.x >= v) + (u.y >= v) + (u.z >= v) + (u.w >= v);
+      if (cnt > BIN_CAP) {
+        // sh == 0: every entry of the bin has the same bit pattern
+        const uint32_t ub = umn + (uint32_t)sel;
+        tk = __uint_as_float((ub & 0x80000000u) ? (ub & 0x7FFFFFFFu) : ~ub);
+      } else {
+#pragma unroll
+        for (int j = 0; j < SR_J; ++j)
+          if (j < jw && ky[j] >= 0 && (((uint64_t)(ord_bits(sc[j]) - umn)) >> hi_sh) == sel) {
+            const int slot = atomicAdd(&sm.misc[2], 1);
+            if (slot < BIN_CAP) sm.binv[slot] = sc[j];
+          }
+        __syncthreads();
+        const int nbin = sm.misc[2];
+        // the need-th largest inside the bin: the largest v with #{u >= v} >= need
+        float best = -INFINITY;
+        for (int e = tid; e < nbin; e += 256) {
+          const float v = sm.binv[e];
+          int c = 0, f = 0;
+          for (; f + 4 <= nbin; f += 4) {
+            const float4 u = *(const float4*)&sm.binv[f];
+            c += (u.x >= v) + (u.y >= v) + (u.z >= v) + (u.w >= v);
+          }
+          for (; f < nbin; ++f) c += sm.binv[f] >= v;
+          if (c >= need) best = fmaxf(best, v);
         }
-        for (; f < nbin; ++f) c += sm.binv[f] >= v;
-        if (c >= need) best = fmaxf(best, v);
+        best = wave_max(best);
+        if (lane == 0) sm.red[wave] = best;
+        __syncthreads();
+        tk = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
       }
-      best = wave_max(best);
-      if (lane == 0) sm.red[wave] = best;
-      __syncthreads();
-      tk = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
     }
     const float hw = band_halfwidth(eps, tk);
     const float hi = tk + hw, lo = tk - hw;
@@ -1319,18 +1350,23 @@ __global__ __launch_bounds__(FB_ROWS) void exact_fallback_kernel(
         for (int c = 0; c < ID; ++c) d = __dadd_rn(d, __dmul_rn((double)bf_bits2f(qrow[h * ID + c]), (double)bf_bits2f(kr[c])));
         s = __dadd_rn(s, __dmul_rn((double)wrow[h], d > 0.0 ? d : 0.0));
       }
-      sc[n] = s;
+      sc[n] = s + 0.0;                  // -0 -> +0: one bit pattern per value
     }
     __syncthreads();
     const int kk = min(topk, nv);
-    // exact k-th largest of non-negative doubles by 8-bit digits of the bit pattern
+    // exact k-th largest by 8-bit digits of the order-preserving image of the bit
+    // pattern (weights of either sign give scores of either sign)
+    auto ord64 = [](double d) -> unsigned long long {
+      const unsigned long long u = (unsigned long long)__double_as_longlong(d);
+      return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+    };
     unsigned long long prefix = 0, pmask = 0;
     int need = kk;
     for (int shift = 56; shift >= 0; shift -= 8) {
       hist[tid] = 0;
       __syncthreads();
       for (int n = tid; n < nv; n += FB_ROWS) {
-        const unsigned long long u = (unsigned long long)__double_as_longlong(sc[n]);
+        const unsigned long long u = ord64(sc[n]);
         if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255ull], 1);
       }
       __syncthreads();
@@ -1361,14 +1397,14 @@ __global__ __launch_bounds__(FB_ROWS) void exact_fallback_kernel(
       need -= misc[1];
       __syncthreads();
     }
-    const double kth = __longlong_as_double((long long)prefix);
+    const double kth = __longlong_as_double((long long)((prefix >> 63) ? (prefix & 0x7FFFFFFFFFFFFFFFull) : ~prefix));
     // keys with s > kth are in; of those equal to kth, the `need` lowest indices are in
     int base = 0, eq_taken = 0;
     int32_t* orow = idx_out + (size_t)i * topk;
     float* srow = score_out ? score_out + (size_t)i * topk : nullptr;
     for (int c0 = 0; c0 < nv; c0 += FB_ROWS) {
       const int n = c0 + tid;
-      const double s = n < nv ? sc[n] : -1.0;
+      const double s = n < nv ? sc[n] : -INFINITY;
       const bool gt = n < nv && s > kth;
       const bool eq = n < nv && s == kth;
       const unsigned long long meq = __ballot(eq);

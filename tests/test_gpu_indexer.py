@@ -91,6 +91,29 @@ def test_indexer_sampled_start_adversarial():
     assert np.array_equal(sc, canon)
 
 
+@pytest.mark.parametrize("L,N,topk,shift", [(24, 3000, 64, 0.5), (10, 20000, 2048, 0.5),
+                                            (8, 40000, 512, 0.5), (8, 40000, 512, 0.9)])
+def test_indexer_signed_weights(L, N, topk, shift):
+    """Head weights of either sign (w - shift, w ~ U[0,1)): scores can be negative and,
+    with shift = 0.9, sum_h w_h ||q_h|| < 0, so an error bound that used w_h rather
+    than |w_h| would come out negative. Every row must equal the oracle, on the
+    short-context path and on the sampled-start list path (N = 40000)."""
+    g = gen_indexer(120 + L, L, N)
+    g["w"].data[:] = g["w"].data - np.float32(shift)
+    idx, _, ref, s = _run(g, topk)
+    assert (s[np.isfinite(s)] < 0).any()
+    _check_rows(idx, ref, np.arange(L), f"signed weights L={L} N={N} shift={shift}")
+
+
+def test_indexer_signed_weights_exact_ties():
+    """Exact-input variant with w in [-1, 1) (multiples of 2^-6): negative scores and
+    frequent ties, decided by the lower index."""
+    g = gen_indexer_exact(130, 12, 20000)
+    g["w"].data[:] = np.float32(2.0) * g["w"].data - np.float32(1.0)
+    idx, _, ref, _ = _run(g, 2048)
+    _check_rows(idx, ref, np.arange(12), "signed exact-input indexer")
+
+
 def test_indexer_full_size_small_config():
     """L = 512, N = 65536, top-k 2048 (blocks of 4096): every row against the oracle."""
     g = gen_indexer(1003, 512, 65536)

@@ -31,12 +31,13 @@ def pin_golden(score_fn, topk_fn):
     return True
 
 
-def pin_fraction_brute(score_fn, rng):
-    """Exact rational scores (Fractions) vs the fp64 canonical score on tiny random bf16 inputs."""
+def pin_fraction_brute(score_fn, rng, w_shift=0.0):
+    """Exact rational scores (Fractions) vs the fp64 canonical score on tiny random bf16
+    inputs; w_shift > 0 draws weights of either sign."""
     L, N, H, D = 3, 12, 4, 8
     q = _bf16(rng.standard_normal((L, H, D)))
     k = _bf16(rng.standard_normal((N, D)))
-    w = rng.random((L, H)).astype(np.float32).astype(np.float64)
+    w = (rng.random((L, H)) - w_shift).astype(np.float32).astype(np.float64)
     s = score_fn(q, k, w)
     for i in range(L):
         for n in range(N):
@@ -63,11 +64,11 @@ def pin_exact_inputs(score_fn):
     return True
 
 
-def pin_topk_subsets(topk_fn, rng):
+def pin_topk_subsets(topk_fn, rng, lo=0):
     for trial in range(20):
         N = int(rng.integers(1, 9))
         k = int(rng.integers(1, 6))
-        s = rng.integers(0, 4, size=N).astype(np.float64)        # many ties
+        s = rng.integers(lo, 4, size=N).astype(np.float64)       # many ties
         s[rng.random(N) < 0.2] = -np.inf                          # invisible keys
         got = set(int(x) for x in topk_fn(s[None], k)[0] if x >= 0)
         ref = brute.topk_by_subsets([None if not np.isfinite(x) else x for x in s], k)
@@ -89,12 +90,20 @@ def test_scores_vs_exact_fractions(rng):
     assert pin_fraction_brute(oracle.indexer_scores, rng)
 
 
+def test_scores_vs_exact_fractions_signed_weights(rng):
+    assert pin_fraction_brute(oracle.indexer_scores, rng, w_shift=0.5)
+
+
 def test_exact_inputs_are_exact():
     assert pin_exact_inputs(oracle.indexer_scores)
 
 
 def test_topk_brute_force_subsets(rng):
     assert pin_topk_subsets(oracle.topk_full, rng)
+
+
+def test_topk_brute_force_subsets_negative_scores(rng):
+    assert pin_topk_subsets(oracle.topk_full, rng, lo=-3)
 
 
 def test_topk_blocked_brute_force_subsets(rng):
