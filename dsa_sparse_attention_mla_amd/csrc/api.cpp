@@ -194,8 +194,9 @@ int mla_decode_paged(int B, int H, int num_pages, int page_size, int max_pages, 
     return DSA_MLA_INVALID_ARG;
   if (H % 16 != 0) return DSA_MLA_UNSUPPORTED;
   const int maxlen = max_pages * page_size;
-  // split length: a multiple of 32 keys, 256 .. 4096, aiming at about 512 workgroups
-  long long spl = ((long long)B * maxlen + 511) / 512;
+  // split length: a multiple of 32 keys, 256 .. 4096, aiming at one workgroup per
+  // compute unit (256; one round of workgroups, since one fills a CU's LDS)
+  long long spl = ((long long)B * maxlen + 255) / 256;
   spl = (spl + 31) / 32 * 32;
   spl = spl < 256 ? 256 : (spl > 4096 ? 4096 : spl);
   const int nsplit = (int)((maxlen + spl - 1) / spl);

@@ -67,14 +67,30 @@ def test_decode_long_contexts():
 
 
 def test_decode_one_sequence_many_splits():
-    """B = 1 over 130999 keys: the keys split 512 ways (more than the combine's 256 splits
-    per pass), the last split holds only part of a tile."""
+    """B = 1 over 130999 keys: the keys split 256 ways, the last split holds only part of
+    a tile."""
     lens = [130999]
     pages, q, table, ln = _paged_case(215, lens, 64, spare_pages=2)
     got = _run(pages, q, table, ln)
     ref = oracle.mla_decode_paged(bf16_to_f32(q).astype(np.float64), bf16_to_f32(pages).astype(np.float64), table,
                                   ln, SCALE)
     assert_close(got, ref, TOL_BF16, "paged decode, one sequence of 130999 keys")
+
+
+def test_decode_more_splits_than_one_combine_pass():
+    """B = 1 over 1060001 keys (splits of 4096 keys, the longest): 259 splits, more than
+    the combine's 256 per pass. The table maps the 4141 logical pages onto 40 physical
+    ones in random order (a page may serve several positions), so the pool stays small."""
+    n, ps, P, H = 1_060_001, 256, 40, 16
+    rng = np.random.default_rng(216)
+    pages = bf16_bits(rng.standard_normal((P, ps, 576), dtype=np.float32))
+    q = bf16_bits(rng.standard_normal((1, H, 576), dtype=np.float32))
+    table = rng.integers(0, P, size=(1, (n + ps - 1) // ps)).astype(np.int32)
+    ln = np.array([n], dtype=np.int32)
+    got = _run(pages, q, table, ln)
+    ref = oracle.mla_decode_paged(bf16_to_f32(q).astype(np.float64), bf16_to_f32(pages).astype(np.float64), table,
+                                  ln, SCALE)
+    assert_close(got, ref, TOL_BF16, "paged decode, one sequence of 1060001 keys")
 
 
 def test_decode_page_outside_pool_counts_as_absent():
