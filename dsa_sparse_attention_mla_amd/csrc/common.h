@@ -37,6 +37,11 @@ __device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
 __device__ __forceinline__ short4v lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS short4v*)(p));
 }
+// Same read from a pointer already in the LDS address space: a base plus a constant
+// then folds into the instruction's offset field, one address register per base.
+__device__ __forceinline__ short4v lds_read_tr16(DSA_LDS const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS short4v*)(p));
+}
 
 __device__ __forceinline__ bf16x8 join_bf16x8(short4v lo, short4v hi) {
   typedef short short8v __attribute__((ext_vector_type(8)));
