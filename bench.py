@@ -56,10 +56,10 @@ FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 # Counter readings (KiB per dispatch, mean of 5 launches of this workload) and a
 # digest of the kernel sources they were taken on.
 COUNTERS = {
-    "indexer_score_filter": {"fetch_kib": 165135.4, "write_kib": 40700.6,
-                             "sources": ("indexer.hip", "common.h"), "sha256_16": "79f43d00f5f26ac4"},
-    "sparse_attn": {"fetch_kib": 891226.6, "write_kib": 65692.3,
-                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "1ab30d5bc2c34604"},
+    "indexer_score_filter": {"fetch_kib": 165145.7, "write_kib": 40691.8,
+                             "sources": ("indexer.hip", "common.h"), "sha256_16": "3886fed0804de42c"},
+    "sparse_attn": {"fetch_kib": 891183.0, "write_kib": 65982.5,
+                    "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "a91e5c5542fc443a"},
 }
 METRIC = "prefill tok/s at 128K ctx (sparse MLA); MFMA util %, HBM GB/s % of peak"
 
