@@ -35,7 +35,8 @@ def _check_rows(idx, ref, rows, what):
         assert np.all(np.diff(v) > 0) and np.all(row[len(v):] == -1)
 
 
-@pytest.mark.parametrize("L,N,topk", [(8, 300, 16), (37, 1000, 64), (5, 5000, 2048), (64, 64, 16), (3, 70000, 100)])
+@pytest.mark.parametrize("L,N,topk", [(8, 300, 16), (37, 1000, 64), (5, 5000, 2048), (64, 64, 16), (3, 70000, 100),
+                                    (1, 1, 1), (1, 7, 2048), (3, 3, 2)])
 def test_indexer_small(L, N, topk):
     g = gen_indexer(80 + L, L, N)
     idx, _, ref, _ = _run(g, topk)
