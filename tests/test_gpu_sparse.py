@@ -104,6 +104,20 @@ def test_sparse_invalid_entries_skipped_and_empty_rows_zero():
     assert_close(out, ref, TOL_BF16, "invalid entries")
 
 
+def test_sparse_repeated_indices_count_per_occurrence():
+    """A row listed twice gets two weights, as in a gather (the selection never lists a
+    key twice; the masked dense path, a bitmap, would count it once)."""
+    L, N, topk = 5, 300, 96
+    q, kv, _, qf, kvf, _ = _case(74, L, N, topk)
+    rng = np.random.default_rng(75)
+    idxn = rng.integers(0, 40, size=(L, topk)).astype(np.int32)   # many repeats
+    idxn[4, :] = 17                                                   # one row, 96 times
+    out = host_f64(dm.mla_prefill_sparse(q, kv, dev(idxn)))
+    ref = oracle.mla_sparse_gather(qf, kvf, idxn, SCALE)
+    assert_close(out, ref, TOL_BF16, "repeated indices")
+    assert np.allclose(out[4], kvf[17, :512][None, :].repeat(64, axis=0), atol=1e-2)
+
+
 def test_sparse_inputs_unchanged_outputs_overwritten_repeatable():
     """Inputs are read-only (decode after prefill sees the same cache), every output element is
     written, and repeated runs are bit-identical."""
