@@ -909,40 +909,42 @@ struct RefineLds {
   int misc[16];
   float red[8];
 };
-static_assert(64 * ID * 2 <= RANK_WORDS * 4, "a band batch of key rows fits the bitmap");
+// a band batch of 64 fp32 key rows spans the bitmap and the union after it
+static_assert(offsetof(RefineLds, u) == sizeof(uint32_t) * RANK_WORDS, "the union follows the bitmap");
+static_assert(64 * ID * 4 <= sizeof(uint32_t) * RANK_WORDS + sizeof(RefineLds::u), "a band batch fits");
 static_assert(BAND_CAP <= 256, "one thread per band slot in the emit");
 static_assert(sizeof(RefineLds) <= 80 * 1024, "two refine workgroups per compute unit");
 }  // namespace
 
-// Canonical fp64 scores of up to 64 band keys whose rows are staged in LDS
-// (krows, 256 B each): lane l32 of 32-lane group g owns head l32 and keys
+// Canonical fp64 scores of up to 64 band keys whose rows are staged in LDS as
+// fp32 (krows, 512 B each; bf16 -> fp32 is exact, so each key value is widened once
+// when staged instead of once per head): lane l32 of 32-lane group g owns head l32 and keys
 // g, g+8, ..., g+56 (eight independent chains). d_h is summed over dims in
 // ascending order; the head terms are then added in ascending head order by one
 // lane per key. A bf16 x bf16 product is exact in fp64, so the fused multiply-add
 // rounds exactly as a product followed by a sum; the weight products are rounded
 // separately.
-__device__ void canonical_scores_batch(const uint16_t* qrow_lds, const uint16_t* krows, int nkeys,
+__device__ void canonical_scores_batch(const uint16_t* qrow_lds, const float* krows, int nkeys,
                                        const float* __restrict__ wrow, double* dh, double* out) {
   const int tid = threadIdx.x, g = tid >> 5, l32 = tid & 31;
   const uint16_t* qh = qrow_lds + l32 * Q_ROW;
   double d[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) d[j] = 0.0;
-  for (int c = 0; c < ID / 8; ++c) {
-    const u32x4 qv = *(const u32x4*)(qh + 8 * c);
-    u32x4 kv[8];
+  for (int c = 0; c < ID / 4; ++c) {
+    const uint2 qv = *(const uint2*)(qh + 4 * c);
+    f32x4 kv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kv[j] = *(const u32x4*)(krows + (size_t)(g + 8 * j) * ID + 8 * c);
+    for (int j = 0; j < 8; ++j) kv[j] = *(const f32x4*)(krows + (size_t)(g + 8 * j) * ID + 4 * c);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double qd = (double)bf_bits2f((uint16_t)((qv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t qw = (e >> 1) ? qv.y : qv.x;
+      const double qd = (double)bf_bits2f((uint16_t)((qw >> (16 * (e & 1))) & 0xFFFFu));
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double kd = (double)bf_bits2f((uint16_t)((kv[j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
-        d[j] = __fma_rn(qd, kd, d[j]);
-      }
+      for (int j = 0; j < 8; ++j) d[j] = __fma_rn(qd, (double)kv[j][e], d[j]);
     }
   }
+  __syncthreads();                      // the head dots overwrite the tail of the key rows
 #pragma unroll
   for (int j = 0; j < 8; ++j) dh[(g + 8 * j) * DH_ROW + l32] = d[j];
   __syncthreads();
@@ -1201,13 +1203,23 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
         *(u32x4*)(sm.qrow + h * Q_ROW + 8 * c) = *(const u32x4*)(q + (size_t)i * IH * ID + 8 * e);
       }
       const float* wrow = w + (size_t)i * IH;
-      uint16_t* krows = (uint16_t*)sm.bitmap;           // 64 rows x 256 B
+      float* krows = (float*)sm.bitmap;                 // 64 rows x 512 B, over the bitmap and the union
       for (int b0 = 0; b0 < nb; b0 += 64) {
         const int nk = min(64, nb - b0);
         for (int x = tid; x < 64 * (ID / 8); x += 256) {  // row r, chunk c; missing rows repeat row 0
           const int r = x >> 4, c = x & 15;
           const int n = sm.bkey[b0 + (r < nk ? r : 0)];
-          *(u32x4*)(krows + r * ID + 8 * c) = *(const u32x4*)(k + (size_t)n * ID + 8 * c);
+          const u32x4 v = *(const u32x4*)(k + (size_t)n * ID + 8 * c);
+          f32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            lo[2 * e] = __uint_as_float(v[e] << 16);
+            lo[2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+            hi[2 * e] = __uint_as_float(v[2 + e] << 16);
+            hi[2 * e + 1] = __uint_as_float(v[2 + e] & 0xFFFF0000u);
+          }
+          *(f32x4*)(krows + r * ID + 8 * c) = lo;
+          *(f32x4*)(krows + r * ID + 8 * c + 4) = hi;
         }
         __syncthreads();
         canonical_scores_batch(sm.qrow, krows, nk, wrow, sm.u.dh, sm.bscore + b0);
