@@ -91,3 +91,21 @@ def topk_by_subsets(scores, k):
             found.append(set(sub))
     assert len(found) == 1, "strict total order must give exactly one closed subset"
     return found[0]
+
+
+def gathered(q_row, kv, idx_row, scale, dv):
+    """Attention of one query over an explicitly gathered list of rows.
+
+    The rows named by idx_row are copied out one entry at a time (a repeated
+    index appears as often as it is listed; entries outside [0, len(kv)) are
+    dropped), every head scores each copy and softmax runs over the copies.
+    q_row [H][D] and kv [N][D] are nested lists; returns [H][dv].
+    """
+    rows = [kv[j] for j in idx_row if 0 <= j < len(kv)]
+    if not rows:
+        return [[0.0] * dv for _ in q_row]
+    out = []
+    for qh in q_row:
+        scores = [[scale * math.fsum(a * b for a, b in zip(qh, r)) for r in rows]]
+        out.append(attention_rows(scores, [r[:dv] for r in rows], [[True] * len(rows)])[0])
+    return out

@@ -120,6 +120,29 @@ def test_absorbed_value_slice_mutant_caught(pin, rng):
     assert not pin(abs_value_tail, rng)
 
 
+def masked_no_causal(q, kv, idx, scale, dv=512, causal=True, rows=None):
+    """Drops the causal term: selected keys past the query's limit get weight."""
+    return oracle.mla_masked_dense(q, kv, idx, scale, dv, causal=False, rows=rows)
+
+
+def sparse_dedup(q, kv, idx, scale, dv=512, rows=None):
+    """Treats each index row as a set: a repeated index weighs once."""
+    idx = np.asarray(idx)
+    out = np.full(idx.shape, -1, dtype=np.int64)
+    for r in range(idx.shape[0]):
+        u = np.unique(idx[r][idx[r] >= 0])
+        out[r, :len(u)] = u
+    return oracle.mla_sparse_gather(q, kv, out, scale, dv, rows)
+
+
+def test_masked_causal_mutant_caught(rng):
+    assert not S.pin_masked_causal_clause(masked_no_causal, rng)
+
+
+def test_gather_dedup_mutant_caught(rng):
+    assert not S.pin_gather_repeats_per_occurrence(sparse_dedup, rng)
+
+
 def test_sparse_minus_one_mutant_caught(rng):
     assert not S.pin_sparse_equals_masked_dense(sparse_minus_one_wraps, rng, pad=0.3)
 
@@ -169,6 +192,8 @@ def test_real_oracle_passes_every_pin(rng):
     assert A.pin_nonabs_rope_only(oracle.mla_nonabsorbed, rng)
     assert A.pin_absorption_identity(oracle.mla_absorbed, rng)
     assert S.pin_sparse_equals_masked_dense(oracle.mla_sparse_gather, rng, pad=0.3)
+    assert S.pin_masked_causal_clause(oracle.mla_masked_dense, rng)
+    assert S.pin_gather_repeats_per_occurrence(oracle.mla_sparse_gather, rng)
     assert I.pin_topk_subsets(oracle.topk_full, rng)
     assert I.pin_golden(oracle.indexer_scores, oracle.topk_full)
     assert DEC.pin_paged_rows_hand(oracle.paged_rows)

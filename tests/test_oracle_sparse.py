@@ -33,6 +33,54 @@ def pin_sparse_brute(fn_sparse, rng):
     return np.allclose(fn_sparse(q, kv, idx, 0.7, dv=3), ref, rtol=0, atol=1e-12)
 
 
+def pin_masked_causal_clause(fn_masked, rng):
+    """Selected keys past a query's causal limit stay masked ("Sparse prefill for GLM",
+    section "The dense mask": the selection mask is combined with the causal mask).
+
+    Queries sit at positions 5..8 of N = 9; every row selects keys past its limit.
+    Reference: the pure-Python brute force over the explicit set of keys that are
+    both selected and visible, and the closed form of query 0, whose only selected
+    visible key is key 0, so its output is that key's value row exactly.
+    """
+    L, N, H, D, dv = 4, 9, 2, 5, 3
+    q, kv = rng.standard_normal((L, H, D)), rng.standard_normal((N, D))
+    idx = np.array([[0, 7, 8, -1], [2, 6, 8, 3], [1, 8, 4, 7], [0, 1, 2, 8]])
+    sel = [{int(x) for x in r if 0 <= x <= N - L + i} for i, r in enumerate(idx)]
+    assert sel[0] == {0} and sel[1] == {2, 3, 6} and sel[2] == {1, 4, 7}   # the limit cuts every row but the last
+    got = fn_masked(q, kv, idx, 0.5, dv=dv)
+    ref = np.array(brute.absorbed(q.tolist(), kv.tolist(), 0.5, dv, sel=sel))
+    first = np.broadcast_to(kv[0, :dv], (H, dv))
+    return bool(np.allclose(got, ref, rtol=0, atol=1e-12) and np.array_equal(got[0], first))
+
+
+def pin_gather_repeats_per_occurrence(fn_sparse, rng):
+    """A repeated index weighs once per occurrence in the gather form ("Sparse prefill
+    for GLM", section "Sparse attention": the chosen rows are gathered, so a key listed
+    twice is two rows of the gathered block).
+
+    Closed form: with a zero query every copy has score 0, so the output is the plain
+    mean over the copies: a key listed twice and one listed once give (2 v_a + v_b) / 3
+    (a set would give (v_a + v_b) / 2). Brute force: the explicitly gathered list of
+    copies for random queries.
+    """
+    L, N, H, D, dv = 3, 8, 2, 6, 4
+    q, kv = rng.standard_normal((L, H, D)), rng.standard_normal((N, D))
+    q[0] = 0.0
+    idx = np.array([[3, 5, 3, -1], [1, 1, 1, 6], [2, 7, 7, 0]])
+    got = fn_sparse(q, kv, idx, 0.4, dv=dv)
+    closed = np.broadcast_to((2 * kv[3, :dv] + kv[5, :dv]) / 3, (H, dv))
+    ref = np.array([brute.gathered(q[i].tolist(), kv.tolist(), idx[i].tolist(), 0.4, dv) for i in range(L)])
+    return bool(np.allclose(got[0], closed, rtol=0, atol=1e-14) and np.allclose(got, ref, rtol=0, atol=1e-12))
+
+
+def test_masked_dense_causal_clause(rng):
+    assert pin_masked_causal_clause(oracle.mla_masked_dense, rng)
+
+
+def test_gather_repeats_count_per_occurrence(rng):
+    assert pin_gather_repeats_per_occurrence(oracle.mla_sparse_gather, rng)
+
+
 def test_sparse_matches_dense_under_mask(rng):
     assert pin_sparse_equals_masked_dense(oracle.mla_sparse_gather, rng)
 
