@@ -140,8 +140,7 @@ def cpu_baseline(g, sample):
 def dense_configs(dm, torch, reps=10):
     """Time the dense MLA prefill configurations (not part of the step)."""
     from synth import gen_absorbed, gen_nonabsorbed
-    sys.path.insert(0, os.path.join(HERE, "tests"))
-    from gpu_util import dev
+    from synth import to_torch as dev
     res = {}
     g = gen_nonabsorbed(1001, 4096, 4096, H=16, dtype="bf16", scale=0.5)
     t = {k: dev(v)[None] for k, v in g.items()}
@@ -291,8 +290,7 @@ def main():
         print(json.dumps(dense_configs(dm, torch)), flush=True)
         return
     from synth import gen_dsa_prefill
-    sys.path.insert(0, os.path.join(HERE, "tests"))
-    from gpu_util import dev
+    from synth import to_torch as dev
 
     if args.sweep:
         print(json.dumps(sweep(dm, torch, dev)), flush=True)

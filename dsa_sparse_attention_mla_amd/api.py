@@ -34,6 +34,32 @@ def _need(t, name, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need_out(t, name, dtype, shape, device):
+    """A caller-supplied output buffer: exact dtype, shape and device, contiguous. The
+    kernels write every element of the expected shape, so a smaller or differently laid
+    out buffer would be written past its end; it is refused before anything launches."""
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _need_workspace(t, nbytes, device):
+    """A caller-supplied workspace: a contiguous 1-D uint8 device tensor of at least nbytes."""
+    _need(t, "workspace", torch.uint8, 1)
+    if t.device != device:
+        raise ValueError(f"workspace must be on {device}, got {t.device}")
+    if t.numel() < nbytes:
+        raise ValueError(f"workspace holds {t.numel()} bytes, {nbytes} needed")
+
+
+def _same_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def _workspace(query, device):
     size = ctypes.c_size_t(0)
     check(query(None, ctypes.byref(size)), "workspace query")
@@ -76,10 +102,11 @@ def mla_prefill_dense(q, k, *, q_rope=None, k_rope=None, v=None, scale=None, cau
         dv = 128
         if scale is None:
             scale = 1.0 / math.sqrt(192)
+    _same_device(q.device, k=k, q_rope=q_rope, k_rope=k_rope, v=v)
     if out is None:
         out = torch.empty((B, L, H, dv), dtype=dtype, device=q.device)
     else:
-        _need(out, "out", dtype, 4)
+        _need_out(out, "out", dtype, (B, L, H, dv), q.device)
     st = lib().mla_prefill_dense(
         _lib.MODE_ABSORBED if absorbed else _lib.MODE_NONABSORBED,
         _lib.BF16 if dtype == torch.bfloat16 else _lib.F32,
@@ -118,7 +145,9 @@ def dsa_indexer_topk(q_idx, k_idx, w, topk, *, block=4096, return_scores=False, 
     if k_idx.shape[0] != B or k_idx.shape[2] != Di or w.shape != (B, L, Hi):
         raise ValueError("shapes must be q_idx [B,L,Hi,Di], k_idx [B,N,Di], w [B,L,Hi]")
     dev = q_idx.device
+    _same_device(dev, k_idx=k_idx, w=w)
     if out is not None:
+        _need_out(out, "out", torch.int32, (B, L, topk) if batched else (L, topk), dev)
         idx = out if batched else out[None]
     else:
         idx = torch.empty((B, L, topk), dtype=torch.int32, device=dev)
@@ -129,7 +158,7 @@ def dsa_indexer_topk(q_idx, k_idx, w, topk, *, block=4096, return_scores=False, 
                                       _ptr(idx), _ptr(scores), ws, ws_bytes, _stream(dev))
 
     if workspace is not None:
-        _need(workspace, "workspace", torch.uint8, 1)
+        _need_workspace(workspace, indexer_workspace_bytes(L, N, topk, block, Hi, Di), dev)
         ws, size = workspace, ctypes.c_size_t(workspace.numel())
     else:
         ws, size = _workspace(call, dev)
@@ -155,11 +184,12 @@ def mla_prefill_sparse(q, kv, idx, *, scale=None, query_block=1024, out=None):
         raise ValueError("shapes must be q [B,L,H,576], kv [B,N,576], idx [B,L,topk]")
     if scale is None:
         scale = 1.0 / math.sqrt(576)
+    _same_device(q.device, kv=kv, idx=idx)
     if out is None:
         out = torch.empty((B, L, H, 512), dtype=torch.bfloat16, device=q.device)
     else:
+        _need_out(out, "out", torch.bfloat16, (B, L, H, 512) if batched else (L, H, 512), q.device)
         out = out if batched else out[None]
-        _need(out, "out", torch.bfloat16, 4)
     st = lib().mla_prefill_sparse(B, L, N, H, _ptr(q), _ptr(kv), _ptr(idx), idx.shape[2], float(scale),
                                   int(query_block), _ptr(out), None, None, _stream(q.device))
     check(st, "mla_prefill_sparse")
@@ -193,15 +223,18 @@ def mla_prefill_masked(q, kv, idx, *, scale=None, out=None, workspace=None):
         raise ValueError("shapes must be q [B,L,H,576], kv [B,N,576], idx [B,L,topk]")
     if scale is None:
         scale = 1.0 / math.sqrt(576)
+    _same_device(q.device, kv=kv, idx=idx)
     if out is None:
         out = torch.empty((B, L, H, 512), dtype=torch.bfloat16, device=q.device)
     else:
+        _need_out(out, "out", torch.bfloat16, (B, L, H, 512) if batched else (L, H, 512), q.device)
         if not batched:
             out = out[None]
-        _need(out, "out", torch.bfloat16, 4)
     nbytes = masked_workspace_bytes(B, L, N)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _need_workspace(workspace, nbytes, q.device)
     n = ctypes.c_size_t(workspace.numel())
     st = lib().mla_prefill_masked(B, L, N, H, _ptr(q), _ptr(kv), _ptr(idx), idx.shape[2], float(scale), _ptr(out),
                                   _ptr(workspace), ctypes.byref(n), _stream(q.device))
@@ -236,13 +269,16 @@ def mla_decode_paged(q, kv_pages, page_table, seq_lens, *, scale=None, out=None,
     maxp = page_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(576)
+    _same_device(q.device, kv_pages=kv_pages, page_table=page_table, seq_lens=seq_lens)
     if out is None:
         out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
     else:
-        _need(out, "out", torch.bfloat16, 3)
+        _need_out(out, "out", torch.bfloat16, (B, H, 512), q.device)
     nbytes = decode_workspace_bytes(B, H, P, ps, maxp)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _need_workspace(workspace, nbytes, q.device)
     n = ctypes.c_size_t(workspace.numel())
     st = lib().mla_decode_paged(B, H, P, ps, maxp, _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
                                 float(scale), _ptr(out), _ptr(workspace), ctypes.byref(n), _stream(q.device))

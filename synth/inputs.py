@@ -14,7 +14,7 @@ import numpy as np
 __all__ = [
     "bf16_bits", "bf16_to_f32", "to_f64", "Tensor",
     "gen_nonabsorbed", "gen_absorbed", "gen_indexer", "gen_indexer_exact",
-    "gen_topk_indices", "gen_dsa_prefill", "CONFIG_SEED",
+    "gen_topk_indices", "gen_dsa_prefill", "CONFIG_SEED", "to_torch",
 ]
 
 # seed used for the workload shapes listed in the design doc (seed = 1000 + config number)
@@ -23,9 +23,12 @@ CONFIG_SEED = {i: 1000 + i for i in range(5)}
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 by round-to-nearest-even, returned as uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    # uint32 arithmetic: a carry past bit 31 wraps, and (a mod 2^32) >> 16 equals
+    # (a >> 16) mod 2^16, so the result is the same as with wider integers
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = u + np.uint32(0x7FFF)
+    r += (u >> 16) & np.uint32(1)
+    return (r >> 16).astype(np.uint16)
 
 
 def bf16_to_f32(b: np.ndarray) -> np.ndarray:
@@ -152,3 +155,14 @@ def gen_topk_indices(seed, L, N, topk, causal=True, pad_frac=0.0):
             m = rng.random(topk) < pad_frac
             out[i, m] = -1
     return out
+
+
+def to_torch(t, device="cuda:0"):
+    """A generated tensor (or numpy array) as a torch tensor on `device` with the same
+    storage bits (bf16 tensors become torch.bfloat16)."""
+    import torch
+    if isinstance(t, Tensor):
+        if t.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(t.data)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(t)).to(device)

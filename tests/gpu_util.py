@@ -2,16 +2,12 @@
 import numpy as np
 import torch
 
-from synth import Tensor
+from synth import to_torch
 
 
 def dev(t, device="cuda:0"):
     """synth Tensor (or numpy array) -> torch device tensor with the same storage bits."""
-    if isinstance(t, Tensor):
-        if t.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).view(torch.bfloat16).to(device)
-        return torch.from_numpy(np.ascontiguousarray(t.data)).to(device)
-    return torch.from_numpy(np.ascontiguousarray(t)).to(device)
+    return to_torch(t, device)
 
 
 def host_f64(x: torch.Tensor) -> np.ndarray:
@@ -24,10 +20,15 @@ def err_report(got, ref):
                 rel=float(d.max() / max(np.abs(ref).max(), 1e-30)) if d.size else 0.0)
 
 
-def assert_close(got, ref, atol, what=""):
+def assert_close(got, ref, atol, what="", rel_guard=None):
+    """max-abs within atol (the stated tolerance); with rel_guard, also max-abs / max|ref|
+    within rel_guard, a regression guard a few bf16 ulps above what the kernels reach,
+    so that an error well inside the loose absolute bound still fails."""
     r = err_report(got, ref)
     print(f"[{what}] max_abs={r['max_abs']:.3e} mean_abs={r['mean_abs']:.3e} max_abs/max|ref|={r['rel']:.3e}", flush=True)
     assert r["max_abs"] <= atol, f"{what}: max_abs {r['max_abs']} > {atol}"
+    if rel_guard is not None:
+        assert r["rel"] <= rel_guard, f"{what}: max_abs/max|ref| {r['rel']} > {rel_guard}"
     return r
 
 

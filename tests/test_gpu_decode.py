@@ -8,7 +8,7 @@ import torch
 import oracle
 import dsa_sparse_attention_mla_amd as dm
 from synth import bf16_bits, bf16_to_f32, gen_dsa_prefill, to_f64
-from gpu_util import assert_close, dev, host_f64
+from gpu_util import assert_close, dev, host_f64, sorted_rows
 
 pytestmark = pytest.mark.gpu
 TOL_BF16 = 2e-2
@@ -113,8 +113,11 @@ def test_decode_after_sparse_prefill():
     t = {k: dev(v) for k, v in g.items()}
     out, idx = dm.dsa_prefill(t["q"], t["kv"], t["q_idx"], t["k_idx"], t["w"], topk, min_context=16384)
     f = {k: to_f64(v) for k, v in g.items()}
-    ref_p = oracle.mla_sparse_gather(f["q"], f["kv"], idx.cpu().numpy(), SCALE, rows=[0, L - 1])
-    assert_close(host_f64(out)[[0, L - 1]], ref_p, TOL_BF16, "sparse prefill rows")
+    rows = [0, L // 2, L - 1]
+    ref_p, ref_idx = oracle.dsa_prefill(f["q"], f["kv"], f["q_idx"], f["k_idx"], f["w"], topk, SCALE,
+                                        min_context=16384, rows=rows)
+    assert sorted_rows(idx.cpu().numpy()[rows]) == sorted_rows(ref_idx[rows])   # the selection itself
+    assert_close(host_f64(out)[rows], ref_p, TOL_BF16, "sparse prefill rows")
     # next token: its key row is appended at position N; the cache goes into shuffled pages
     rng = np.random.default_rng(231)
     new_row = bf16_bits(rng.standard_normal((1, 576), dtype=np.float32))

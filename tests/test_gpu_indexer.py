@@ -141,24 +141,6 @@ def test_indexer_full_size_small_config():
     _check_score_error(g, idx, sc, s, np.arange(512), "score error 512 x 65536")
 
 
-def test_indexer_full_size_sampled():
-    """L = 1024, N = 131072, top-k 2048: sampled rows against the oracle."""
-    g = gen_indexer(1004, 1024, 131072)
-    rows = np.array([0, 1, 2, 100, 511, 512, 777, 1021, 1022, 1023])
-    idx, sc, ref, s = _run(g, 2048, rows=rows)
-    got = sorted_rows(idx[rows])
-    exp = sorted_rows(ref)
-    assert got == exp
-    assert (idx >= 0).all()
-    # s holds the sampled rows only: index it by position
-    got_s = np.take_along_axis(s, idx[rows].astype(np.int64), axis=1)
-    err = np.abs(sc[rows] - got_s).max(axis=1)
-    eps = _eps_rows(g, rows)
-    print(f"[score error 1024 x 131072] max |s_hat - s| = {err.max():.3e}, max ratio to eps = {(err / eps).max():.4f}",
-          flush=True)
-    assert np.all(err <= eps / 8)
-
-
 def test_indexer_block_argument_has_no_effect():
     g = gen_indexer(96, 20, 9000)
     q, k, w = dev(g["q_idx"]), dev(g["k_idx"]), dev(g["w"])
