@@ -9,12 +9,13 @@ a workspace buffer) -- all arithmetic runs in the library's HIP kernels.
     mla_prefill_sparse(...)   absorbed attention over gathered top-k rows
     mla_prefill_masked(...)   dense absorbed attention under the top-k mask (gated path)
     mla_decode_paged(...)     one decode step over a paged joined cache
+    mla_decode_paged_noalloc(...)  the same step without a workspace (fixed device scratch)
     use_sparse(...)           the dense/sparse gate ("Sparse prefill for GLM", "When it runs")
     dsa_prefill(...)          indexer + gated attention for one chunk
 """
 from .api import (  # noqa: F401
     mla_prefill_dense, dsa_indexer_topk, mla_prefill_sparse, mla_prefill_masked, masked_workspace_bytes,
-    mla_decode_paged, decode_workspace_bytes,
+    mla_decode_paged, decode_workspace_bytes, mla_decode_paged_noalloc,
     use_sparse, dsa_prefill,
     SPARSE_PREFILL_DEFAULT, SPARSE_PREFILL_MIN_CONTEXT_DEFAULT, kernel_trace, indexer_workspace_bytes,
 )

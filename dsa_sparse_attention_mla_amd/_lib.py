@@ -22,6 +22,8 @@ SIGNATURES = {
     "mla_prefill_sparse": (_i, [_i, _i, _i, _i, _p, _p, _p, _i, _f, _i, _p, _p, _sz, _p]),
     "mla_prefill_masked": (_i, [_i, _i, _i, _i, _p, _p, _p, _i, _f, _p, _p, _sz, _p]),
     "mla_decode_paged": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _f, _p, _p, _sz, _p]),
+    "mla_decode_paged_noalloc": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _f, _p, _p]),
+    "mla_decode_paged_noalloc_capacity": (ctypes.c_size_t, []),
     "dsa_mla_trace_enable": (_i, [_i]),
     "dsa_mla_trace_collect": (_i, [_i, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]),
     "dsa_mla_status_string": (ctypes.c_char_p, [_i]),

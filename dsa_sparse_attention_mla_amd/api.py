@@ -286,6 +286,29 @@ def mla_decode_paged(q, kv_pages, page_table, seq_lens, *, scale=None, out=None,
     return out
 
 
+def mla_decode_paged_noalloc(q, kv_pages, page_table, seq_lens, *, scale=None, out):
+    """mla_decode_paged without a workspace: the split partials go to the library's fixed
+    device scratch (for callers that cannot allocate). `out` [B,H,512] bf16 is required.
+    Calls on one device must not overlap in time (they share the scratch)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_pages, "kv_pages", torch.bfloat16, 3)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, H, D = q.shape
+    P, ps, D2 = kv_pages.shape
+    if D != 576 or D2 != 576 or page_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("shapes must be q [B,H,576], kv_pages [P,page_size,576], page_table [B,max_pages], "
+                         "seq_lens [B]")
+    _same_device(q.device, kv_pages=kv_pages, page_table=page_table, seq_lens=seq_lens)
+    _need_out(out, "out", torch.bfloat16, (B, H, 512), q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(576)
+    st = lib().mla_decode_paged_noalloc(B, H, P, ps, page_table.shape[1], _ptr(q), _ptr(kv_pages), _ptr(page_table),
+                                        _ptr(seq_lens), float(scale), _ptr(out), _stream(q.device))
+    check(st, "mla_decode_paged_noalloc")
+    return out
+
+
 def use_sparse(sparse_prefill: bool, B: int, L: int, N: int,
                min_context: int = SPARSE_PREFILL_MIN_CONTEXT_DEFAULT, batched: bool = False) -> bool:
     """The gate ("Sparse prefill for GLM", section "When it runs"): sparse only when switched

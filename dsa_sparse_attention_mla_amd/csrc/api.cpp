@@ -60,6 +60,39 @@ int workspace_step(size_t need, void* ws, size_t* ws_bytes) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DSA_MLA_OK : DSA_MLA_HIP; }
 
+// Argument checks shared by both decode entry points.
+int decode_check(int B, int H, int num_pages, int page_size, int max_pages, const void* q, const void* kv_pages,
+                 const int32_t* page_table, const int32_t* seq_lens, float scale, const void* out) {
+  if (B < 0 || H < 1 || num_pages < 1 || page_size < 1 || max_pages < 1) return DSA_MLA_INVALID_ARG;
+  if ((long long)num_pages * page_size > INT32_MAX || (long long)max_pages * page_size > INT32_MAX)
+    return DSA_MLA_INVALID_ARG;
+  if (!std::isfinite(scale)) return DSA_MLA_INVALID_ARG;
+  if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
+    return DSA_MLA_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_pages) || !aligned4(page_table) || !aligned4(seq_lens) || !aligned16(out))
+    return DSA_MLA_INVALID_ARG;
+  if (H % 16 != 0) return DSA_MLA_UNSUPPORTED;
+  return DSA_MLA_OK;
+}
+
+// Split of the decode keys: a multiple of 32 keys, 256 .. 4096, aiming at one workgroup
+// per compute unit (256; one round of workgroups, since one fills a CU's LDS).
+struct DecodePlan {
+  int spl, nsplit;
+  size_t part_bytes;   // split partials: B * nsplit * H records of 512 outputs + max + sum
+};
+DecodePlan decode_plan(int B, int H, int max_pages, int page_size) {
+  const int maxlen = max_pages * page_size;
+  long long spl = ((long long)B * maxlen + 255) / 256;
+  spl = (spl + 31) / 32 * 32;
+  spl = spl < 256 ? 256 : (spl > 4096 ? 4096 : spl);
+  DecodePlan p;
+  p.spl = (int)spl;
+  p.nsplit = (int)((maxlen + spl - 1) / spl);
+  p.part_bytes = (size_t)B * p.nsplit * H * (512 + 2) * 4;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,32 +217,39 @@ int mla_prefill_masked(int B, int L, int N, int H, const void* q, const void* kv
 int mla_decode_paged(int B, int H, int num_pages, int page_size, int max_pages, const void* q, const void* kv_pages,
                      const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, void* ws,
                      size_t* ws_bytes, void* stream) {
-  if (B < 0 || H < 1 || num_pages < 1 || page_size < 1 || max_pages < 1) return DSA_MLA_INVALID_ARG;
-  if ((long long)num_pages * page_size > INT32_MAX || (long long)max_pages * page_size > INT32_MAX)
-    return DSA_MLA_INVALID_ARG;
-  if (!std::isfinite(scale)) return DSA_MLA_INVALID_ARG;
-  if (q == nullptr || kv_pages == nullptr || page_table == nullptr || seq_lens == nullptr || out == nullptr)
-    return DSA_MLA_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(kv_pages) || !aligned4(page_table) || !aligned4(seq_lens) || !aligned16(out))
-    return DSA_MLA_INVALID_ARG;
-  if (H % 16 != 0) return DSA_MLA_UNSUPPORTED;
-  const int maxlen = max_pages * page_size;
-  // split length: a multiple of 32 keys, 256 .. 4096, aiming at one workgroup per
-  // compute unit (256; one round of workgroups, since one fills a CU's LDS)
-  long long spl = ((long long)B * maxlen + 255) / 256;
-  spl = (spl + 31) / 32 * 32;
-  spl = spl < 256 ? 256 : (spl > 4096 ? 4096 : spl);
-  const int nsplit = (int)((maxlen + spl - 1) / spl);
-  const size_t part_bytes = (size_t)B * nsplit * H * (512 + 2) * 4;
-  const int wsr = workspace_step(part_bytes, ws, ws_bytes);
+  const int v = decode_check(B, H, num_pages, page_size, max_pages, q, kv_pages, page_table, seq_lens, scale, out);
+  if (v != DSA_MLA_OK) return v;
+  const DecodePlan dp = decode_plan(B, H, max_pages, page_size);
+  const int wsr = workspace_step(dp.part_bytes, ws, ws_bytes);
   if (wsr >= 0) return wsr;
   if (B == 0) return DSA_MLA_OK;
   const int a = check_arch();
   if (a != DSA_MLA_OK) return a;
-  float* part = (float*)ws;
   return hip_status(dsa::launch_paged_decode((const uint16_t*)q, (const uint16_t*)kv_pages, page_table, seq_lens, B,
-                                             H, num_pages, page_size, max_pages, (int)spl, nsplit, part,
+                                             H, num_pages, page_size, max_pages, dp.spl, dp.nsplit, (float*)ws,
                                              (uint16_t*)out, scale, (hipStream_t)stream));
 }
+
+int mla_decode_paged_noalloc(int B, int H, int num_pages, int page_size, int max_pages, const void* q,
+                             const void* kv_pages, const int32_t* page_table, const int32_t* seq_lens, float scale,
+                             void* out, void* stream) {
+  const int v = decode_check(B, H, num_pages, page_size, max_pages, q, kv_pages, page_table, seq_lens, scale, out);
+  if (v != DSA_MLA_OK) return v;
+  const DecodePlan dp = decode_plan(B, H, max_pages, page_size);
+  if (dp.part_bytes > dsa::kDecodeScratchBytes) return DSA_MLA_WORKSPACE;
+  if (B == 0) return DSA_MLA_OK;
+  const int a = check_arch();
+  if (a != DSA_MLA_OK) return a;
+  void* part = nullptr;
+  if (dsa::decode_scratch(&part) != hipSuccess || part == nullptr) {
+    (void)hipGetLastError();
+    return DSA_MLA_HIP;
+  }
+  return hip_status(dsa::launch_paged_decode((const uint16_t*)q, (const uint16_t*)kv_pages, page_table, seq_lens, B,
+                                             H, num_pages, page_size, max_pages, dp.spl, dp.nsplit, (float*)part,
+                                             (uint16_t*)out, scale, (hipStream_t)stream));
+}
+
+size_t mla_decode_paged_noalloc_capacity(void) { return dsa::kDecodeScratchBytes; }
 
 }  // extern "C"

@@ -33,6 +33,8 @@
 // 16-byte loads per thread, eight threads per row) and written to their LDS stage;
 // the index list of a segment of up to 2048 keys is staged in LDS first, so a row
 // address never waits on an index load.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -546,6 +548,31 @@ hipError_t launch_paged_decode(const uint16_t* q, const uint16_t* kv_pages, cons
   KernelTrace kt("decode_combine", stream);
   hipLaunchKernelGGL(decode_combine_kernel, dim3(H, B), dim3(DV / 2), 0, stream, part, nsplit, H, out);
   return hipGetLastError();
+}
+
+// Fixed device scratch for the decode entry point that allocates nothing: the split
+// partials live here instead of in a caller workspace. Each device that loads the
+// library holds its own copy until the process ends. In host code the name is only a
+// stand-in for the symbol: the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to kernels.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_mask_rows(const int32_t* idx, int B, int L, int N, int topk, uint32_t* mask, hipStream_t stream) {

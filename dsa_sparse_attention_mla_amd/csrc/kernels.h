@@ -28,6 +28,10 @@ hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv,
 hipError_t launch_paged_decode(const uint16_t* q, const uint16_t* kv_pages, const int32_t* page_table,
                                const int32_t* seqlens, int B, int H, int num_pages, int page_size, int max_pages,
                                int spl, int nsplit, float* part, uint16_t* out, float scale, hipStream_t stream);
+// Size of the fixed decode scratch (split partials of the no-allocation decode call).
+constexpr size_t kDecodeScratchBytes = (size_t)40 << 20;
+// Device address of that scratch on the current device (looked up once per device).
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_mask_rows(const int32_t* idx, int B, int L, int N, int topk, uint32_t* mask, hipStream_t stream);
 
 hipError_t launch_nonabsorbed_attn(bool bf16, const void* qn, const void* qr, const void* kn, const void* kr,

@@ -10,6 +10,8 @@
  *                       (the path the sparse call replaces; the gated case)
  *   mla_decode_paged    one decode step (L = 1) of absorbed attention over a
  *                       paged joined cache
+ *   mla_decode_paged_noalloc  the same step with the library's fixed scratch
+ *                       instead of a workspace (for callers that cannot allocate)
  *
  * Conventions shared by all calls
  * -------------------------------
@@ -17,6 +19,11 @@
  * Validation: every argument check runs on the host before anything is
  *   launched; a call that returns an error has launched nothing and left every
  *   output untouched. No call prints, throws or allocates device memory.
+ * Process-wide state: the library keeps a per-device record of the device
+ *   check, the tracing switch and its pending event records (diagnostics, see
+ *   dsa_mla_trace_enable), and, per device, the fixed scratch array of
+ *   mla_decode_paged_noalloc with its looked-up device address. All of it is
+ *   guarded by locks; nothing else persists between calls.
  * Memory: every tensor argument is a DEVICE pointer owned by the caller,
  *   contiguous row-major in the layout stated per call, with a 16-byte aligned
  *   base. Inputs are only read; outputs are fully overwritten.
@@ -180,6 +187,27 @@ int mla_prefill_masked(int B, int L, int N, int H, const void* q, const void* kv
 int mla_decode_paged(int B, int H, int num_pages, int page_size, int max_pages, const void* q, const void* kv_pages,
                      const int32_t* page_table, const int32_t* seq_lens, float scale, void* out, void* ws,
                      size_t* ws_bytes, void* stream);
+
+/*
+ * mla_decode_paged_noalloc -- mla_decode_paged for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. It takes no workspace: the split partials go to a fixed scratch
+ * array of mla_decode_paged_noalloc_capacity() bytes (40 MiB) that the library holds
+ * on every device it runs on until the process ends. Same arguments, layouts,
+ * kernels and result as mla_decode_paged; a call whose partials,
+ * B * nsplit * H * 514 * 4 bytes (nsplit as in mla_decode_paged: about 256 / B
+ * splits per sequence, fewer for short caches), would not fit returns
+ * DSA_MLA_WORKSPACE and launches nothing. At H = 64 this admits, e.g., 8 sequences
+ * of 131072 keys or up to about 1.3M cached keys in all. Every record the combine
+ * reads is written by the same call, so nothing needs clearing between calls. All
+ * calls on one device share its scratch: calls that overlap in time on one device
+ * (different streams, or different threads without ordering) race and must not be
+ * issued.
+ */
+int mla_decode_paged_noalloc(int B, int H, int num_pages, int page_size, int max_pages, const void* q,
+                             const void* kv_pages, const int32_t* page_table, const int32_t* seq_lens, float scale,
+                             void* out, void* stream);
+size_t mla_decode_paged_noalloc_capacity(void);
 
 /*
  * Per-kernel timing (diagnostics). dsa_mla_trace_enable(1) makes every later
