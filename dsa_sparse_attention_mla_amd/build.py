@@ -19,8 +19,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # packed fp32 ops are disabled: the compiler would otherwise form v_pk_*_f32 from scalar code.
-# MFMA accumulators are kept in ordinary VGPRs (not AGPRs): the online-softmax rescale of the
-# output accumulators then needs no AGPR<->VGPR copies.
+# MFMA accumulators are kept in ordinary VGPRs (not AGPRs) unless a source is listed in
+# AGPR_FORM: the online-softmax rescale of the output accumulators then needs no
+# AGPR<->VGPR copies.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-mllvm", "-amdgpu-mfma-vgpr-form",
@@ -31,9 +32,22 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
+# Sources whose MFMA accumulators go to the accumulation registers (AGPRs): kernels that
+# run one wave per SIMD and need more than 256 registers per lane.
+AGPR_FORM = {"attn_absorbed_dense.hip"}
+
+
+def flags(src):
+    f = list(COMMON)
+    if os.path.basename(src) in AGPR_FORM:
+        i = f.index("-amdgpu-mfma-vgpr-form")
+        del f[i - 1:i + 1]
+    return f
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *flags(src), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops' is not a recognized feature" not in l)
     if r.returncode != 0:

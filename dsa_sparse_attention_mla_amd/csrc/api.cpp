@@ -139,8 +139,8 @@ int mla_prefill_dense(int mode, int dtype, int B, int L, int N, int H, const voi
   if (mode == DSA_MLA_MODE_NONABSORBED)
     return hip_status(dsa::launch_nonabsorbed_attn(dtype == DSA_MLA_BF16, q, q_rope, k, k_rope, v, out, B, L, N, H,
                                                    causal, scale, st));
-  return hip_status(dsa::launch_absorbed_attn(0, (const uint16_t*)q, (const uint16_t*)k, nullptr, nullptr, (uint16_t*)out,
-                                              B, L, N, H, 0, 0, L, causal, scale, st));
+  return hip_status(dsa::launch_absorbed_dense((const uint16_t*)q, (const uint16_t*)k, nullptr, (uint16_t*)out, B, L, N,
+                                               H, causal, scale, st));
 }
 
 int dsa_indexer_topk(int B, int L, int N, int Hi, int Di, const void* q_idx, const void* k_idx, const float* w,
@@ -209,8 +209,8 @@ int mla_prefill_masked(int B, int L, int N, int H, const void* q, const void* kv
   uint32_t* mask = (uint32_t*)ws;
   hipError_t e = dsa::launch_mask_rows(idx, B, L, N, topk, mask, (hipStream_t)stream);
   if (e != hipSuccess) return DSA_MLA_HIP;
-  e = dsa::launch_absorbed_attn(2, (const uint16_t*)q, (const uint16_t*)kv, idx, mask, (uint16_t*)out, B, L, N, H,
-                                topk, 0, L, 1, scale, (hipStream_t)stream);
+  e = dsa::launch_absorbed_dense((const uint16_t*)q, (const uint16_t*)kv, mask, (uint16_t*)out, B, L, N, H, 1, scale,
+                                 (hipStream_t)stream);
   return hip_status(e);
 }
 

@@ -25,6 +25,8 @@ hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv,
                                 const uint32_t* mask, uint16_t* out, int B, int L, int N, int H, int topk, int q0,
                                 int nq, int causal, float scale, hipStream_t stream, const int32_t* seqlens = nullptr,
                                 float* part = nullptr, int spl = 0, int psz = 1);
+hipError_t launch_absorbed_dense(const uint16_t* q, const uint16_t* kv, const uint32_t* mask, uint16_t* out, int B,
+                                 int L, int N, int H, int causal, float scale, hipStream_t stream);
 hipError_t launch_paged_decode(const uint16_t* q, const uint16_t* kv_pages, const int32_t* page_table,
                                const int32_t* seqlens, int B, int H, int num_pages, int page_size, int max_pages,
                                int spl, int nsplit, float* part, uint16_t* out, float scale, hipStream_t stream);

@@ -158,6 +158,18 @@ def test_absorbed_nonpositive_scale(scale):
     assert_close(host_f64(out[0]), ref, TOL_BF16, f"absorbed scale={scale}")
 
 
+@pytest.mark.parametrize("scale", [40 / math.sqrt(576), -40 / math.sqrt(576)])
+def test_absorbed_wide_score_range(scale):
+    """Scores spread over hundreds of log2 units: the first tile's maximum is far below
+    (or above) the row's true maximum, so the kernel's second pass against the true
+    maximum has to run for these rows."""
+    q, kv, qf, kvf = _abs(43, 20, 700, 64)
+    out = dm.mla_prefill_dense(q[None], kv[None], scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.mla_absorbed(qf, kvf, scale)
+    assert_close(host_f64(out[0]), ref, TOL_BF16, f"absorbed wide range scale={scale:.3f}")
+
+
 def test_dense_batch():
     """B = 2 (batches take the dense path): each batch entry equals its own single-sequence call."""
     L, N, H = 20, 60, 16

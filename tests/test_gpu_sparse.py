@@ -169,6 +169,19 @@ def test_masked_dense_selection_rules():
     assert_close(out, ref, TOL_BF16, "masked selection rules")
 
 
+def test_masked_dense_wide_score_range():
+    """A sharp scale with selections that skip the first key tile for some queries: the
+    reference taken from the first tile is empty or far off, so the second pass runs."""
+    L, N, topk = 16, 900, 40
+    g, idxn = _masked_case(125, L, N, topk)
+    idxn[::2] = np.where(idxn[::2] < 64, 64 + (idxn[::2] % 200), idxn[::2])   # nothing in tile 0 or 1
+    q, kv, qf, kvf = dev(g["q"]), dev(g["kv"]), to_f64(g["q"]), to_f64(g["kv"])
+    scale = 30 / math.sqrt(576)
+    out = host_f64(dm.mla_prefill_masked(q, kv, dev(idxn), scale=scale))
+    ref = oracle.mla_masked_dense(qf, kvf, idxn, scale)
+    assert_close(out, ref, TOL_BF16, "masked dense wide range")
+
+
 def test_masked_dense_batch():
     L, N, topk, H = 12, 200, 32, 64
     cases = [_masked_case(130 + b, L, N, topk, H) for b in range(2)]
