@@ -14,9 +14,14 @@ The line also carries:
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                 workload on this host;
   kernels_ms    per-kernel average duration (HIP events);
-  other_configs the dense MLA prefill configurations (non-absorbed bf16 at
-                L = N = 4096, absorbed at L = 512 / N = 16384) with their MFMA
-                fractions.
+  other_configs the other configurations, each with its roofline fraction:
+                non-absorbed fp32 at L = N = 256 and bf16 at L = N = 4096,
+                absorbed bf16 at L = 512 / N = 16384, the indexer alone at
+                L = 512 / N = 65536, and a paged decode step.
+  measured_ceilings  what this GPU sustains, measured in the same run by the
+                library's probes: bf16 MFMA on register operands (with the
+                shader clock under that load) and HBM copy / read streams;
+                the fractions above are also given against these.
 
   traffic       HBM bytes per launch of the dominant kernel from rocprofv3's
                 FETCH_SIZE / WRITE_SIZE counters, scaled by what the same
@@ -26,6 +31,8 @@ The line also carries:
 
   dense_baseline the path the sparse call replaces (masked dense attention) on
                 the same chunk, with the speed-ups of the sparse path.
+
+Kernel and configuration times are medians of per-launch HIP-event timings.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
        python bench.py --sweep        context sweep, sparse vs masked dense
@@ -44,6 +51,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
 L, N, TOPK, BLOCK, H = 1024, 131072, 2048, 4096, 64
@@ -137,25 +145,73 @@ def cpu_baseline(g, sample):
                       f"{dt:.1f} s"}
 
 
-def dense_configs(dm, torch, reps=10):
+def dense_configs(dm, torch, reps=10, ceil=None):
     """Time the dense MLA prefill configurations (not part of the step)."""
     from synth import gen_absorbed, gen_nonabsorbed
     from synth import to_torch as dev
     res = {}
-    g = gen_nonabsorbed(1001, 4096, 4096, H=16, dtype="bf16", scale=0.5)
+
+    def entry(ms, fl, peak, measured=None):
+        e = {"ms": ms, "tflops": fl / ms / 1e9, "mfma_frac": fl / ms / 1e9 / peak}
+        if measured:
+            e["frac_of_measured_mfma"] = fl / ms / 1e9 / measured
+        return e
+    meas = ceil["mfma_bf16"]["tflops"] if ceil else None
+    g = gen_nonabsorbed(1000, 256, 256, H=16, dtype="f32")
     t = {k: dev(v)[None] for k, v in g.items()}
     fn = lambda: dm.mla_prefill_dense(t["qn"], t["kn"], q_rope=t["qr"], k_rope=t["kr"], v=t["v"])  # noqa: E731
     ms = _time(fn, torch, reps)
-    fl = 640 * 16 * 4096 * 4097 // 2
-    res["nonabsorbed_bf16_L4096_N4096_H16"] = {"ms": ms, "tflops": fl / ms / 1e9,
-                                               "mfma_frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+    res["nonabsorbed_fp32_L256_N256_H16"] = dict(entry(ms, 640 * 16 * 256 * 257 // 2, PEAK_FP32_MFMA_TFLOPS),
+                                                 peak="fp32 MFMA 157.3 TFLOP/s",
+                                                 note="one 64-query tile per workgroup: 64 workgroups, launch-bound")
+    g = gen_nonabsorbed(1001, 4096, 4096, H=16, dtype="bf16", scale=0.5)
+    t = {k: dev(v)[None] for k, v in g.items()}
+    ms = _time(fn, torch, reps)
+    res["nonabsorbed_bf16_L4096_N4096_H16"] = entry(ms, 640 * 16 * 4096 * 4097 // 2, PEAK_BF16_TFLOPS, meas)
     g = gen_absorbed(1002, 512, 16384, H=64)
     q, kv = dev(g["q"])[None], dev(g["kv"])[None]
     ms = _time(lambda: dm.mla_prefill_dense(q, kv), torch, reps)
     fl = 2176 * 64 * sum(16384 - 512 + i + 1 for i in range(512))
-    res["absorbed_bf16_L512_N16384_H64"] = {"ms": ms, "tflops": fl / ms / 1e9,
-                                            "mfma_frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS}
+    res["absorbed_bf16_L512_N16384_H64"] = entry(ms, fl, PEAK_BF16_TFLOPS, meas)
     return res
+
+
+def indexer_config(dm, torch, Li=512, Ni=65536, reps=10, ceil=None):
+    """The indexer alone at L = 512, N = 65536 (top-2048, blocks of 4096): the phase
+    (every indexer kernel) and its score kernel, against bf16 MFMA peak."""
+    from synth import gen_indexer
+    from synth import to_torch as dev
+    g = gen_indexer(1003, Li, Ni)
+    q_idx, k_idx, w = dev(g["q_idx"]), dev(g["k_idx"]), dev(g["w"])
+    ws = torch.empty(dm.indexer_workspace_bytes(Li, Ni, TOPK, BLOCK), dtype=torch.uint8, device="cuda:0")
+    idx = torch.empty((Li, TOPK), dtype=torch.int32, device="cuda:0")
+    fn = lambda: dm.dsa_indexer_topk(q_idx, k_idx, w, TOPK, block=BLOCK, out=idx, workspace=ws)  # noqa: E731
+    ms = _time(fn, torch, reps)
+    with dm.kernel_trace() as tr:
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+    kms = {k: tot / max(cnt, 1) for k, (cnt, tot) in tr.stats.items()}
+    fl = indexer_flops(Li, Ni)
+    t_sc = max(kms.values()) if kms else ms
+    sc_name = max(kms, key=kms.get) if kms else None
+    e = {"workload": f"indexer, L={Li}, N={Ni}, 32 heads x 128, top-{TOPK}, blocks of {BLOCK}",
+         "ms": ms, "tflops": fl / ms / 1e9, "mfma_frac": fl / ms / 1e9 / PEAK_BF16_TFLOPS,
+         "score_kernel": sc_name, "score_kernel_ms": t_sc, "score_kernel_mfma_frac": fl / t_sc / 1e9 / PEAK_BF16_TFLOPS,
+         "kernels_ms": kms}
+    if ceil:
+        e["score_kernel_frac_of_measured_mfma"] = fl / t_sc / 1e9 / ceil["mfma_bf16"]["tflops"]
+    return e
+
+
+def measured_ceilings(dm):
+    """The library's probes: sustained bf16 MFMA (and the shader clock under it), HBM streams."""
+    mf = dm.probe_mfma(grid=1024, iters=4096)
+    cp = dm.probe_stream(2 << 30, mode="copy")
+    rd = dm.probe_stream(2 << 30, mode="read")
+    return {"mfma_bf16": mf, "hbm_copy": cp, "hbm_read": rd,
+            "mfma_frac_of_datasheet": mf["tflops"] / PEAK_BF16_TFLOPS,
+            "hbm_read_frac_of_datasheet": rd["GB_s"] / PEAK_HBM_GBS}
 
 
 def decode_config(dm, torch, B=8, n=131072, page_size=64, reps=10):
@@ -247,16 +303,19 @@ def sweep(dm, torch, dev):
 
 
 def _time(fn, torch, reps):
+    """Median over reps of one call's HIP-event time, after two untimed calls."""
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
+    ts = []
     for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
         fn()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return sorted(ts)[len(ts) // 2]
 
 
 def main():
@@ -266,11 +325,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=96)
+    ap.add_argument("--cpu-sample", type=int, default=384)
     ap.add_argument("--sweep", action="store_true",
                     help="only run the context sweep (sparse vs masked dense, N = 4K..128K, L = 512/1024)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
+    ap.add_argument("--ceilings-only", action="store_true",
+                    help="only run the measurement probes (MFMA, HBM copy / read) and print them")
     ap.add_argument("--dense-only", action="store_true",
                     help="only time the two dense MLA configurations (for counter runs) and print them")
     args = ap.parse_args()
@@ -288,6 +349,9 @@ def main():
 
     if args.dense_only:
         print(json.dumps(dense_configs(dm, torch)), flush=True)
+        return
+    if args.ceilings_only:
+        print(json.dumps(measured_ceilings(dm)), flush=True)
         return
     from synth import gen_dsa_prefill
     from synth import to_torch as dev
@@ -319,27 +383,35 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / args.steps
+    step_median_ms = _time(step, torch, args.steps)
 
     log("bench: per-kernel event timing")
-    with dm.kernel_trace() as tr:
-        for _ in range(args.steps):
+    per_kernel = {}
+    for _ in range(args.steps):
+        with dm.kernel_trace() as tr:
             step()
-        torch.cuda.synchronize()
-    kernels_ms = {k: tot / max(cnt, 1) for k, (cnt, tot) in tr.stats.items()}
+            torch.cuda.synchronize()
+        for k, (cnt, tot) in tr.stats.items():
+            per_kernel.setdefault(k, []).append(tot / max(cnt, 1))
+    kernels_ms = {k: sorted(v)[len(v) // 2] for k, v in per_kernel.items()}   # median over steps
     t_idx = kernels_ms.get("indexer_score_filter", 0.0)
     t_att = kernels_ms.get("sparse_attn", 0.0)
+    log("bench: measured ceilings")
+    ceil = measured_ceilings(dm)
     if t_idx >= t_att:
         fl = indexer_flops(L, N)
         ach = fl / (t_idx * 1e-3) / 1e12
         roof = {"kernel": "indexer_score_filter", "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic_bytes("indexer_score_filter"),
-                "per_launch": f"{fl:.4e} FLOP (8192 per visible query-key pair)", "ms": t_idx}
+                "per_launch": f"{fl:.4e} FLOP (8192 per visible query-key pair)", "ms": t_idx,
+                "frac_of_measured": ach / ceil["mfma_bf16"]["tflops"]}
     else:
         by = sparse_attn_bytes(L, TOPK, H)
         ach = by / (t_att * 1e-3) / 1e9
         roof = {"kernel": "sparse_attn", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": ach / PEAK_HBM_GBS, "traffic": traffic_bytes("sparse_attn"),
-                "per_launch": f"{by:.4e} B (gathered rows, q, out, idx)", "ms": t_att}
+                "per_launch": f"{by:.4e} B (gathered rows, q, out, idx)", "ms": t_att,
+                "frac_of_measured": ach / ceil["hbm_read"]["GB_s"]}
 
     other = None
     baseline = None
@@ -348,7 +420,9 @@ def main():
         log("bench: sparse attention, cold caches")
         cold = sparse_cold(dm, torch, q, kv, idx, out)
         log("bench: dense configurations")
-        other = dense_configs(dm, torch)
+        other = dense_configs(dm, torch, ceil=ceil)
+        log("bench: indexer alone (L=512, N=65536)")
+        other["indexer_L512_N65536"] = indexer_config(dm, torch, ceil=ceil)
         log("bench: masked dense baseline")
         baseline = masked_baseline(dm, torch, q, kv, idx, t_att, ms_per_step)
         log("bench: paged decode")
@@ -361,7 +435,7 @@ def main():
     line = {
         "metric": METRIC, "value": L / (ms_per_step * 1e-3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "step_median_ms": step_median_ms,
         "config": {"workload": "DSA sparse MLA prefill, one 1024-query chunk at the end of a 131072-position "
                                "context: indexer 32 heads x 128 (top-2048, blocks of 4096) + absorbed attention "
                                "64 heads over gathered 576-wide latent+rope rows (value = first 512)",
@@ -370,11 +444,18 @@ def main():
         "roofline": roof, "cpu_baseline": cpu, "kernels_ms": kernels_ms,
         "phases_ms": {"indexer_total": sum(v for k, v in kernels_ms.items() if k.startswith(("indexer", "key_norm", "query_eps"))),
                       "sparse_attn": t_att},
-        "sparse_attn_roofline": {"achieved_GBs": sparse_attn_bytes(L, TOPK, H) / (t_att * 1e-3) / 1e9 if t_att else None,
-                                 "frac_hbm": sparse_attn_bytes(L, TOPK, H) / (t_att * 1e-3) / 1e9 / PEAK_HBM_GBS if t_att else None,
+        "sparse_attn_roofline": {"effective_GBs_at_algorithmic_bytes": sparse_attn_bytes(L, TOPK, H) / (t_att * 1e-3) / 1e9 if t_att else None,
+                                 "effective_frac_hbm": sparse_attn_bytes(L, TOPK, H) / (t_att * 1e-3) / 1e9 / PEAK_HBM_GBS if t_att else None,
+                                 "algorithmic_bytes": sparse_attn_bytes(L, TOPK, H),
+                                 "counter_bytes": traffic_bytes("sparse_attn"),
+                                 "note": "algorithmic bytes count every gathered row once per query; rows shared by "
+                                         "queries of the chunk are served from the 256 MB last-level cache, so this "
+                                         "is an effective rate, not DRAM bandwidth (counter_bytes: HBM bytes read "
+                                         "and written, from rocprofv3, or null if the kernel changed since)",
                                  "tflops": sparse_attn_flops(L, TOPK, H) / (t_att * 1e-3) / 1e12 if t_att else None,
                                  "caches": "warm (the bench step's own)", "cold": cold},
         "other_configs": other,
+        "measured_ceilings": ceil,
         "dense_baseline": baseline,
     }
     print(json.dumps(line), flush=True)

@@ -26,6 +26,8 @@ SIGNATURES = {
     "mla_decode_paged_noalloc_capacity": (ctypes.c_size_t, []),
     "dsa_mla_trace_enable": (_i, [_i]),
     "dsa_mla_trace_collect": (_i, [_i, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)]),
+    "dsa_mla_probe_mfma": (_i, [_i, _i, _p, _p, _p, ctypes.POINTER(ctypes.c_int), _p]),
+    "dsa_mla_probe_stream": (_i, [_i, _p, _p, ctypes.c_size_t, _i, _p]),
     "dsa_mla_status_string": (ctypes.c_char_p, [_i]),
     "dsa_mla_abi_version": (_i, []),
 }

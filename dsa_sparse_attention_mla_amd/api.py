@@ -360,3 +360,56 @@ class kernel_trace:
             nm = names.raw[32 * j:32 * j + 32].split(b"\0", 1)[0].decode()
             self.stats[nm] = (counts[j], tot[j])
         return False
+
+
+def _event_ms(launch, device, reps):
+    """Median over reps of one launch's HIP-event time (one untimed launch first)."""
+    ts = []
+    for r in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch()
+        b.record()
+        torch.cuda.synchronize(device)
+        if r:
+            ts.append(a.elapsed_time(b))
+    return sorted(ts)[len(ts) // 2]
+
+
+def probe_mfma(grid=1024, iters=4096, reps=3, device="cuda"):
+    """Sustained bf16 MFMA rate on register operands and the shader clock it runs at
+    (diagnostic: the measured ceiling of the matrix-bound kernels). Returns TFLOP/s
+    (median launch), the mean shader clock under the load and cycles per MFMA."""
+    dev = torch.device(device)
+    cyc = torch.empty(4 * grid, dtype=torch.int64, device=dev)
+    wall = torch.empty(4 * grid, dtype=torch.int64, device=dev)
+    sink = torch.empty(256 * grid, dtype=torch.float32, device=dev)
+    khz = ctypes.c_int(0)
+
+    def launch():
+        check(lib().dsa_mla_probe_mfma(grid, iters, _ptr(cyc), _ptr(wall), _ptr(sink), ctypes.byref(khz),
+                                       _stream(dev)), "dsa_mla_probe_mfma")
+
+    ms = _event_ms(launch, dev, reps)
+    c, w = cyc.double().mean().item(), wall.double().mean().item()
+    flop = grid * 4 * iters * 8 * 32768
+    return {"tflops": flop / ms / 1e9, "sclk_ghz": c / (w / (khz.value * 1e3)) / 1e9,
+            "cycles_per_mfma": c / (iters * 8), "ms": ms,
+            "what": f"{grid} workgroups x 4 waves, {iters} rounds of 8 independent 32x32x16 bf16 MFMAs"}
+
+
+def probe_stream(nbytes=2 << 30, mode="copy", grid=4096, reps=3, device="cuda"):
+    """HBM stream rate (diagnostic: the measured ceiling of the bandwidth-bound kernels).
+    mode "copy" reads and writes nbytes (2 nbytes moved), "read" reads nbytes."""
+    dev = torch.device(device)
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty(nbytes // 4 if mode == "copy" else 256 * grid, dtype=torch.int32, device=dev)
+    m = {"copy": 0, "read": 1}[mode]
+
+    def launch():
+        check(lib().dsa_mla_probe_stream(m, _ptr(src), _ptr(dst), nbytes, grid, _stream(dev)), "dsa_mla_probe_stream")
+
+    ms = _event_ms(launch, dev, reps)
+    moved = nbytes * (2 if m == 0 else 1)
+    del src, dst
+    return {"GB_s": moved / ms / 1e6, "ms": ms, "what": f"{mode} of {nbytes >> 20} MiB, {grid} workgroups"}

@@ -252,4 +252,28 @@ int mla_decode_paged_noalloc(int B, int H, int num_pages, int page_size, int max
 
 size_t mla_decode_paged_noalloc_capacity(void) { return dsa::kDecodeScratchBytes; }
 
+int dsa_mla_probe_mfma(int grid, int iters, long long* cycles, long long* wall, float* sink, int* wall_khz,
+                       void* stream) {
+  if (grid < 1 || grid > 65535 || iters < 1 || cycles == nullptr || wall == nullptr || sink == nullptr)
+    return DSA_MLA_INVALID_ARG;
+  const int a = check_arch();
+  if (a != DSA_MLA_OK) return a;
+  if (wall_khz != nullptr) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+      return DSA_MLA_HIP;
+    *wall_khz = khz;
+  }
+  return hip_status(dsa::launch_mfma_burn(grid, iters, cycles, wall, sink, (hipStream_t)stream));
+}
+
+int dsa_mla_probe_stream(int mode, const void* src, void* dst, size_t bytes, int grid, void* stream) {
+  if ((mode != 0 && mode != 1) || grid < 1 || grid > 65535 || bytes % 64 != 0) return DSA_MLA_INVALID_ARG;
+  if (src == nullptr || dst == nullptr || !aligned16(src) || !aligned16(dst)) return DSA_MLA_INVALID_ARG;
+  if (bytes == 0) return DSA_MLA_OK;
+  const int a = check_arch();
+  if (a != DSA_MLA_OK) return a;
+  return hip_status(dsa::launch_stream(mode, src, dst, bytes, grid, (hipStream_t)stream));
+}
+
 }  // extern "C"

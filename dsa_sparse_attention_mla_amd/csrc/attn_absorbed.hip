@@ -1,15 +1,13 @@
 // Absorbed (latent-space) MLA attention over joined 576-wide latent+rope rows.
 //
-// One kernel serves three calls:
-//  * dense absorbed prefill (keys 0..p_i of a contiguous cache, bottom-right
-//    causal),
+// One kernel serves two calls:
 //  * sparse prefill: each query attends only to the rows its index list names,
 //    gathered from the cache ("Sparse prefill for GLM", section "Sparse
 //    attention": joined latent+rope rows, all heads share the gathered block,
 //    absorbed attention whose value is the latent part of the row), and
-//  * masked dense prefill, the path the sparse one replaces (same page, section
-//    "The dense mask"): every visible key is visited and only the keys the
-//    query's top-k selection marks in a bitmap get weight.
+//  * one split of a paged decode step (the rows of a sequence's page list).
+// Dense and masked dense absorbed prefill, where a cache tile is shared by many
+// queries, have a kernel of their own (attn_absorbed_dense.hip).
 //
 // Work decomposition (gfx950): one workgroup per query and 64-head group, 8
 // waves, with the 32x32x16 bf16 MFMA so that every operand fragment read from LDS
@@ -69,9 +67,7 @@ static_assert(T * FPR == 256 && CPT * FPR == CH, "the score waves fetch whole ti
 static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
 }  // namespace
 
-// MODE: 0 dense (every visible key), 1 sparse (gathered index lists), 2 masked
-// dense (every visible key, weighted only where the query's selection bitmap has
-// its bit set), 3 paged decode split (one query per sequence; workgroup x gathers
+// MODE: 1 sparse (gathered index lists), 3 paged decode split (one query per sequence; workgroup x gathers
 // keys [x*spl, x*spl + spl) of the sequence's row list and writes its unnormalised
 // partial output with the running max and sum, merged afterwards).
 template <int MODE>
@@ -79,7 +75,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const uint32_t* __restrict__ mask, uint16_t* __restrict__ out, int L, int N, int H, int topk, int q0, int causal,
     float scale_log2, const int32_t* __restrict__ seqlens, float* __restrict__ part, int spl, int psz) {
-  constexpr bool SPARSE = MODE == 1 || MODE == 3;   // rows come from an index list
+  static_assert(MODE == 1 || MODE == 3, "rows come from an index list");
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   unsigned char* ring = dyn;                                // [NST][STAGE]
   int* sidx = (int*)(dyn + NST * (size_t)STAGE);            // [SEG]
@@ -95,18 +91,14 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   const int half = (wave >> 1) & 1;                         // score half, or value half of an output wave
   const int head = blockIdx.z * 64 + 32 * hg + l32;
   const bool head_ok = head < H;
-  const int p = N - L + i;
-  int count = MODE == 1 ? topk : (causal ? p + 1 : N);
+  int count = topk;
   // (topk is the row-list length here; a sequence length past it is clamped to it)
   if constexpr (MODE == 3) count = max(0, min(spl, min(seqlens[b], topk) - (int)blockIdx.x * spl));
   // paged decode: rows are physical rows of the page pool (N of them), shared by all sequences
   const uint16_t* kvb = kv + (MODE == 3 ? (size_t)0 : (size_t)b * N * D);
   // sparse: the query's index list; paged decode: the sequence's page table row
   // (topk = max_pages * page_size there)
-  const int32_t* irow = MODE == 1   ? idx + ((size_t)b * L + i) * topk
-                        : MODE == 3 ? idx + (size_t)b * (topk / psz)
-                                    : nullptr;
-  const uint32_t* mrow = MODE == 2 ? mask + ((size_t)b * L + i) * ((N + 31) / 32) : nullptr;
+  const int32_t* irow = MODE == 1 ? idx + ((size_t)b * L + i) * topk : idx + (size_t)b * (topk / psz);
 
   // Tile rows (score waves, tid < 256): thread tid handles row tid / 8 of the tile and
   // its 16-byte columns tid % 8 + 8 u, so a thread looks up one key per tile and its
@@ -115,7 +107,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   auto key_of = [&](int t, int r, int seg_base, int seg_cnt) -> int {
     const int slot = t * T + r;
     if (slot >= seg_cnt) return -1;
-    return SPARSE ? sidx[slot] : seg_base + slot;
+    return sidx[slot];
   };
   // Every fetching thread issues CPT loads for every fetch, also past the last tile
   // (those read row 0 and are never staged), so the number of outstanding loads is the
@@ -131,8 +123,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
 #pragma unroll
     for (int u = 0; u < CPT; ++u) *(u32x4*)(st + 128 * u) = src[u];
     if (wave == 0) {
-      bool v = lane < T && key_of(t, lane, seg_base, seg_cnt) >= 0;
-      if constexpr (MODE == 2) v = v && ((mrow[(seg_base + t * T) / 32] >> lane) & 1u);
+      const bool v = lane < T && key_of(t, lane, seg_base, seg_cnt) >= 0;
       const unsigned long long bm = __ballot(v);
       if (lane == 0) smask[st_i] = (uint32_t)bm;
     }
@@ -141,7 +132,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
   // before any is used).
   auto segment_indices = [&](int seg_base, int seg_cnt) {
     lds_barrier();                                 // the previous segment's indices and stages are no longer read
-    if (SPARSE) {
+    {
       constexpr int PER = SEG / (64 * NW);
       int xs[PER];
 #pragma unroll
@@ -165,7 +156,7 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     }
   };
 
-  const int nseg = count > 0 ? (SPARSE ? (count + SEG - 1) / SEG : 1) : 0;
+  const int nseg = count > 0 ? (count + SEG - 1) / SEG : 0;
 
   if (score_wave) {
     // ---------------------------------------------------------------- scoring
@@ -214,59 +205,9 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
       if (t + 2 < ntiles) stage_in(t + 2, (t + 2) % NST, slot, seg_base, seg_cnt);
       fetch(t + 2 + PF, slot, seg_base, seg_cnt);
     };
-    if constexpr (!SPARSE) {
-      // Contiguous rows (dense and masked dense): direct global->LDS loads. Stage chunk
-      // c (16 bytes, c < T * ROWC) is chunk c % ROWC of row c / ROWC (ROWC - 1 data
-      // chunks and the padding, which loads the row's last data chunk again); load j
-      // (1 KB) covers chunks 64 j .. 64 j + 63 and score wave w issues loads w, w + 4,
-      // ...; rows past the last key repeat it (their scores are masked).
-      constexpr int ROWC = ROWB / 16, NCH = T * ROWC, NLD = (NCH + 63) / 64, LPW = (NLD + 3) / 4;
-      const uint32_t lds_ring = (uint32_t)(uintptr_t)(DSA_LDS void*)ring;
-      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-      uint32_t doff[LPW];
-      int drow[LPW];
-#pragma unroll
-      for (int s2 = 0; s2 < LPW; ++s2) {
-        const int c = 64 * (4 * s2 + wave_u) + lane;
-        drow[s2] = c / ROWC;
-        doff[s2] = (uint32_t)(drow[s2] * D * 2 + 16 * min(c % ROWC, D * 2 / 16 - 1));
-      }
-      auto dma_tile = [&](int t, int st_i) {
-        const int rmax = count - 1 - t * T;          // last row of the tile that is a key
-        const void* base = uniform_ptr(kvb + (size_t)t * T * D);
-#pragma unroll
-        for (int s2 = 0; s2 < LPW; ++s2) {
-          const int j = 4 * s2 + wave_u;
-          if (j < NLD && 64 * j + lane < NCH) {
-            const uint32_t off = rmax >= T - 1 ? doff[s2] : doff[s2] - (uint32_t)((drow[s2] - min(drow[s2], rmax)) * D * 2);
-            dma16s(base, off, lds_ring + st_i * STAGE + 1024 * j);
-          }
-        }
-        if (wave == 0) {
-          bool v = lane < T && t * T + lane < count;
-          if constexpr (MODE == 2) v = v && ((mrow[t] >> lane) & 1u);
-          const unsigned long long bm = __ballot(v);
-          if (lane == 0) smask[st_i] = (uint32_t)bm;
-        }
-      };
-      const int ntiles = (count + T - 1) / T;
-      segment_indices(0, count);
-      if (ntiles > 0) dma_tile(0, 0);
-      if (ntiles > 1) dma_tile(1, 1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      lds_barrier();
-      if (ntiles > 0) score_tile(0);
-      for (int t = 0; t < ntiles; ++t) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile t+1 landed
-        lds_barrier();                                       // scores of t, rows of t+1 published
-        if (t + 1 < ntiles) score_tile(t + 1);
-        if (t + 2 < ntiles) dma_tile(t + 2, (t + 2) % NST);
-      }
-      return;
-    }
     for (int seg = 0; seg < nseg; ++seg) {
-      const int seg_base = SPARSE ? seg * SEG : 0;
-      const int seg_cnt = SPARSE ? min(SEG, count - seg_base) : count;
+      const int seg_base = seg * SEG;
+      const int seg_cnt = min(SEG, count - seg_base);
       const int ntiles = (seg_cnt + T - 1) / T;
       segment_indices(seg_base, seg_cnt);
       // tiles 0 and 1 staged, 2 and 3 in registers, scores of 0
@@ -304,13 +245,13 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     const int s3 = t % NST;
     // the first batch of V^T fragments does not depend on the scores: read it now,
     // under the softmax
-    // (the stage offset is made opaque, so the compiler keeps one address register and
-    // folds every read's constant into the instruction instead of strength-reducing
-    // sixteen addresses across the loop: 2.5% on the dense path; the gather path was
-    // measured no faster, even slower with uncorrelated index lists, and keeps the
-    // compiler's form)
+    // (decode: the stage offset is made opaque, so the compiler keeps one address
+    // register and folds every read's constant into the instruction instead of
+    // strength-reducing sixteen addresses across the loop; the prefill gather was
+    // measured no faster that way, even slower with uncorrelated index lists, and
+    // keeps the compiler's form)
     int sofs = s3 * STAGE;
-    if constexpr (MODE != 1) asm volatile("" : "+s"(sofs));
+    if constexpr (MODE == 3) asm volatile("" : "+s"(sofs));
     DSA_LDS const unsigned char* vb = (DSA_LDS const unsigned char*)dyn + sofs + voff;
     bf16x8 vf0[NDB / 2][2];
 #pragma unroll
@@ -404,8 +345,8 @@ __global__ __launch_bounds__(64 * NW) void absorbed_attn_kernel(
     }
   };
   for (int seg = 0; seg < nseg; ++seg) {
-    const int seg_base = SPARSE ? seg * SEG : 0;
-    const int seg_cnt = SPARSE ? min(SEG, count - seg_base) : count;
+    const int seg_base = seg * SEG;
+    const int seg_cnt = min(SEG, count - seg_base);
     const int ntiles = (seg_cnt + T - 1) / T;
     segment_indices(seg_base, seg_cnt);
     lds_barrier();                                 // tiles 0 and 1 staged, scores of 0 under way
@@ -589,8 +530,7 @@ hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv,
                                 float* part, int spl, int psz) {
   static bool attr_set = false;
   if (!attr_set) {
-    const void* fns[4] = {(const void*)absorbed_attn_kernel<0>, (const void*)absorbed_attn_kernel<1>,
-                          (const void*)absorbed_attn_kernel<2>, (const void*)absorbed_attn_kernel<3>};
+    const void* fns[2] = {(const void*)absorbed_attn_kernel<1>, (const void*)absorbed_attn_kernel<3>};
     for (const void* f : fns) {
       const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
       if (e != hipSuccess) return e;
@@ -599,17 +539,13 @@ hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv,
   }
   const float scale_log2 = scale * 1.4426950408889634f;
   dim3 grid(nq, B, (H + 63) / 64), block(64 * NW);
-  static const char* names[4] = {"absorbed_dense_attn", "sparse_attn", "masked_dense_attn", "paged_decode_attn"};
-  KernelTrace kt(names[mode], stream);
+  if (mode != 1 && mode != 3) return hipErrorInvalidValue;
+  KernelTrace kt(mode == 1 ? "sparse_attn" : "paged_decode_attn", stream);
 #define DSA_LAUNCH_ABS(M)                                                                                    \
   hipLaunchKernelGGL((absorbed_attn_kernel<M>), grid, block, LDS_BYTES, stream, q, kv, idx, mask, out, L, N, H, \
                      topk, q0, causal, scale_log2, seqlens, part, spl, psz)
-  switch (mode) {
-    case 1: DSA_LAUNCH_ABS(1); break;
-    case 2: DSA_LAUNCH_ABS(2); break;
-    case 3: DSA_LAUNCH_ABS(3); break;
-    default: DSA_LAUNCH_ABS(0); break;
-  }
+  if (mode == 1) DSA_LAUNCH_ABS(1);
+  else DSA_LAUNCH_ABS(3);
 #undef DSA_LAUNCH_ABS
   return hipGetLastError();
 }

@@ -87,7 +87,7 @@ __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
 // Score MFMAs with the accumulator in vector registers. The leading s_nop covers a
 // vector instruction that may have written an A/B operand just before.
 __device__ __forceinline__ void score_mfma_first(f32x16& s, bf16x8 a, bf16x8 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(b));
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void score_mfma(f32x16& s, bf16x8 a, bf16x8 b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));

@@ -21,6 +21,7 @@ class KernelTrace {
   void* a_;
 };
 
+// mode 1: sparse prefill over index lists; mode 3: one split of a paged decode step
 hipError_t launch_absorbed_attn(int mode, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                                 const uint32_t* mask, uint16_t* out, int B, int L, int N, int H, int topk, int q0,
                                 int nq, int causal, float scale, hipStream_t stream, const int32_t* seqlens = nullptr,
@@ -34,6 +35,9 @@ hipError_t launch_paged_decode(const uint16_t* q, const uint16_t* kv_pages, cons
 constexpr size_t kDecodeScratchBytes = (size_t)40 << 20;
 // Device address of that scratch on the current device (looked up once per device).
 hipError_t decode_scratch(void** ptr);
+hipError_t launch_mfma_burn(int grid, int iters, long long* cycles, long long* wall, float* sink,
+                            hipStream_t stream);
+hipError_t launch_stream(int mode, const void* src, void* dst, size_t bytes, int grid, hipStream_t stream);
 hipError_t launch_mask_rows(const int32_t* idx, int B, int L, int N, int topk, uint32_t* mask, hipStream_t stream);
 
 hipError_t launch_nonabsorbed_attn(bool bf16, const void* qn, const void* qr, const void* kn, const void* kr,

@@ -222,6 +222,34 @@ size_t mla_decode_paged_noalloc_capacity(void);
 int dsa_mla_trace_enable(int on);
 int dsa_mla_trace_collect(int max_kernels, char* names, int* counts, double* total_ms);
 
+/*
+ * Measurement probes (diagnostics, not part of the attention path): the ceilings
+ * the kernels above are measured against on the running GPU, next to the data
+ * sheet's peaks.
+ *
+ * dsa_mla_probe_mfma launches `grid` workgroups of four waves (one per SIMD when
+ * grid is a multiple of the compute-unit count); every wave runs `iters` rounds
+ * of eight independent 32x32x16 bf16 MFMAs (32768 FLOP each) on register
+ * operands. Per wave w of workgroup g, cycles[4g + w] receives the shader-clock
+ * cycles of its loop and wall[4g + w] the ticks of the constant-rate wall clock
+ * over the same loop; sink[256 g + thread] receives a sum of the results.
+ * cycles, wall and sink are device buffers of 4 grid, 4 grid and 256 grid
+ * elements, owned by the caller. *wall_khz (host, may be NULL) receives the
+ * wall clock's rate in kHz. Total work: grid * 4 * iters * 8 * 32768 FLOP; the
+ * ratio cycles / wall gives the shader clock under full matrix load.
+ *
+ * dsa_mla_probe_stream moves `bytes` (a multiple of 64) through HBM with
+ * 16-byte-per-lane loads over a grid of `grid` workgroups of 256 threads:
+ * mode 0 copies src to dst (bytes read and bytes written), mode 1 only reads src
+ * and writes one 32-bit word per thread (dst: 1024 grid bytes). src and dst are
+ * 16-byte-aligned device buffers owned by the caller.
+ *
+ * Both return DSA_MLA_INVALID_ARG for out-of-range arguments before launching.
+ */
+int dsa_mla_probe_mfma(int grid, int iters, long long* cycles, long long* wall, float* sink, int* wall_khz,
+                       void* stream);
+int dsa_mla_probe_stream(int mode, const void* src, void* dst, size_t bytes, int grid, void* stream);
+
 /* Short English name of a status code (static storage). */
 const char* dsa_mla_status_string(int status);
 

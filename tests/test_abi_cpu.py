@@ -172,3 +172,24 @@ def test_decode_workspace_query():
     ok = ctypes.c_size_t(sz.value)
     assert _decode(ws=P, ws_bytes=ctypes.byref(ok)) == _lib.ARCH
     assert _decode(B=0, ws=P, ws_bytes=ctypes.byref(ok)) == _lib.OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(grid=0), _lib.INVALID_ARG), (dict(iters=0), _lib.INVALID_ARG), (dict(cyc=None), _lib.INVALID_ARG),
+    (dict(sink=None), _lib.INVALID_ARG), (dict(), _lib.ARCH),
+])
+def test_probe_mfma_validation(kw, code):
+    a = dict(grid=256, iters=16, cyc=P, wall=P, sink=P, khz=None, stream=None)
+    a.update(kw)
+    assert dm.lib().dsa_mla_probe_mfma(*a.values()) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=2), _lib.INVALID_ARG), (dict(nbytes=100), _lib.INVALID_ARG), (dict(src=MIS), _lib.INVALID_ARG),
+    (dict(dst=None), _lib.INVALID_ARG), (dict(grid=0), _lib.INVALID_ARG), (dict(nbytes=0), _lib.OK),
+    (dict(), _lib.ARCH),
+])
+def test_probe_stream_validation(kw, code):
+    a = dict(mode=0, src=P, dst=P, nbytes=1 << 20, grid=64, stream=None)
+    a.update(kw)
+    assert dm.lib().dsa_mla_probe_stream(*a.values()) == code
