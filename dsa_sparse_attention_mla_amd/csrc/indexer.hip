@@ -12,18 +12,28 @@
 //  1. key_norm_partial:   per-block max of ||k_n||^2 (fp32).
 //  2. query_eps:          eps_i, a rigorous bound on |s_hat - s| for the fp32
 //                         MFMA score s_hat, from sum_h |w_h| ||q_h|| * max_n ||k_n||.
-//  3. score_filter:       32x32x16 bf16 MFMA scores for 32 heads; ReLU, weight and
-//                         head sum in registers; every wave owns one query and keeps
-//                         a candidate list in LDS of all keys with
+//  3. one score kernel, both with 32x32x16 bf16 MFMA scores for 32 heads and the
+//     ReLU, weight and head sum in registers; only candidates leave the chip:
+//     score_list (long contexts: every query of a group sees at least 8 * SAMPLE
+//                         keys): the workgroup scores SAMPLE keys spread over the
+//                         visible range, fixes each query's threshold just below
+//                         the sample's expected k-th largest, streams its key split
+//                         and appends every key at or above the threshold to the
+//                         query's list in memory (no list on chip, no compaction).
+//     score_filter (short contexts): every wave owns one query and keeps a
+//                         candidate list in LDS of all keys with
 //                         s_hat >= tau - band(tau), tau = the running k-th largest
 //                         s_hat (found by an in-LDS radix select whenever the list
-//                         fills up). Only candidates leave the chip.
-//  4. select_refine:      per query, T = k-th largest s_hat among candidates.
+//                         fills up), i.e. a running top-k folded tile by tile.
+//  4. select_refine:      per query, T = k-th largest s_hat among candidates, after
+//                         a coverage check (every split's threshold at most
+//                         T - band: the lists then hold the whole top-k).
 //                         s_hat > T + band: in. s_hat < T - band: out. The keys in
 //                         between are re-scored canonically in fp64 and ranked by
 //                         (s desc, index asc) to fill the rest.
-//  5. exact_fallback:     rows whose candidates overflowed (huge ties) are solved
-//                         from the canonical fp64 score of every visible key.
+//  5. exact_fallback:     rows that failed the coverage check or whose lists
+//                         overflowed (huge ties, a sampled threshold set badly) are
+//                         solved from the canonical fp64 score of every visible key.
 // Output rows are in ascending key order, padded with -1.
 #include <cmath>
 
