@@ -58,6 +58,7 @@ constexpr int SR_J = 48;                // candidates per thread (in registers) 
 constexpr int SR_MAX = SR_J * 256;      // candidates per query select_refine holds
 constexpr int NORM_BLOCKS = 1024;
 constexpr int FB_ROWS = 256;            // block size of the fallback kernel
+constexpr int FB_BLOCKS = 256;          // fallback workgroups: one per compute unit
 }  // namespace
 
 __device__ __forceinline__ void wave_sync() {
@@ -934,6 +935,15 @@ static_assert(sizeof(RefineLds) <= 80 * 1024, "two refine workgroups per compute
 // lane per key. A bf16 x bf16 product is exact in fp64, so the fused multiply-add
 // rounds exactly as a product followed by a sum; the weight products are rounded
 // separately.
+// fp64 product rounded on its own: the weight products of the canonical score are
+// not exact, and a fused multiply-add formed from a product and the following sum
+// would round once instead of twice.
+__device__ __forceinline__ double dmul_rounded(double a, double b) {
+  double p;
+  asm volatile("v_mul_f64 %0, %1, %2" : "=v"(p) : "v"(a), "v"(b));
+  return p;
+}
+
 __device__ void canonical_scores_batch(const uint16_t* qrow_lds, const float* krows, int nkeys,
                                        const float* __restrict__ wrow, double* dh, double* out) {
   const int tid = threadIdx.x, g = tid >> 5, l32 = tid & 31;
@@ -962,7 +972,7 @@ __device__ void canonical_scores_batch(const uint16_t* qrow_lds, const float* kr
     double sc = 0.0;
     for (int h = 0; h < IH; ++h) {
       const double v = dh[tid * DH_ROW + h];
-      sc = __dadd_rn(sc, __dmul_rn((double)wrow[h], v > 0.0 ? v : 0.0));
+      sc = sc + dmul_rounded((double)wrow[h], v > 0.0 ? v : 0.0);
     }
     out[tid] = sc;
   }
@@ -1338,14 +1348,21 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
 }
 
 // ---------------------------------------------------------------- 5. exact fallback
-// One workgroup per flagged row at a time; the canonical fp64 score of every
-// visible key goes to a per-workgroup scratch row, then an exact 64-bit radix
-// select finds the k-th largest value and a stable scan emits the set.
+// One workgroup per flagged row at a time (one workgroup per compute unit); the
+// canonical fp64 score of every visible key goes to a per-workgroup scratch row,
+// then an exact 64-bit radix select finds the k-th largest value and a stable scan
+// emits the set. A thread scores one key at a time: the 32 head dots advance
+// together over 32-dim chunks of the key (converted to fp64 once per chunk), with
+// the query in LDS as fp64 and read by all lanes at once. A product of two bf16
+// values is exact in fp64, so each fused multiply-add rounds exactly as the
+// canonical product-then-sum; dims are added in ascending order per head, and the
+// weighted head terms (products of an fp32 weight and an fp64 dot, not exact) are
+// rounded separately and added in ascending head order.
 __global__ __launch_bounds__(FB_ROWS) void exact_fallback_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w, int L, int N,
     int topk, const int* __restrict__ fb_flag, double* __restrict__ scratch, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
-  __shared__ uint16_t qrow[IH * ID];
+  __shared__ double qd[IH * ID];
   __shared__ float wrow[IH];
   __shared__ int hist[256];
   __shared__ int misc[4];
@@ -1361,18 +1378,52 @@ __global__ __launch_bounds__(FB_ROWS) void exact_fallback_kernel(
     if (fb_flag[i] == 0) continue;
     const int nv = min(N, N - L + i + 1);
     __syncthreads();
-    for (int e = tid; e < IH * ID; e += FB_ROWS) qrow[e] = q[(size_t)i * IH * ID + e];
+    for (int e = tid; e < IH * ID; e += FB_ROWS) qd[e] = (double)bf_bits2f(q[(size_t)i * IH * ID + e]);
     if (tid < IH) wrow[tid] = w[(size_t)i * IH + tid];
     __syncthreads();
-    for (int n = tid; n < nv; n += FB_ROWS) {
-      const uint16_t* kr = k + (size_t)n * ID;
-      double s = 0.0;
-      for (int h = 0; h < IH; ++h) {
-        double d = 0.0;
-        for (int c = 0; c < ID; ++c) d = __dadd_rn(d, __dmul_rn((double)bf_bits2f(qrow[h * ID + c]), (double)bf_bits2f(kr[c])));
-        s = __dadd_rn(s, __dmul_rn((double)wrow[h], d > 0.0 ? d : 0.0));
+    // two keys per thread (n and n + FB_ROWS): every query value read from LDS feeds
+    // four multiply-adds
+    for (int n = tid; n < nv; n += 2 * FB_ROWS) {
+      const int n2 = n + FB_ROWS < nv ? n + FB_ROWS : n;     // past the end: key n again, not stored
+      const u32x4* kr0 = (const u32x4*)(k + (size_t)n * ID);
+      const u32x4* kr1 = (const u32x4*)(k + (size_t)n2 * ID);
+      double d0[IH], d1[IH];
+#pragma unroll
+      for (int h = 0; h < IH; ++h) d0[h] = d1[h] = 0.0;
+      for (int c0 = 0; c0 < ID; c0 += 32) {
+        u32x4 kw0[4], kw1[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          kw0[x] = kr0[c0 / 8 + x];
+          kw1[x] = kr1[c0 / 8 + x];
+        }
+        double kd0[32], kd1[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const uint32_t w0 = kw0[e / 8][(e % 8) / 2], w1 = kw1[e / 8][(e % 8) / 2];
+          kd0[e] = (double)bf_bits2f((uint16_t)((e & 1) ? (w0 >> 16) : (w0 & 0xFFFFu)));
+          kd1[e] = (double)bf_bits2f((uint16_t)((e & 1) ? (w1 >> 16) : (w1 & 0xFFFFu)));
+        }
+        const double* qc = qd + c0;
+#pragma unroll
+        for (int h = 0; h < IH; ++h)
+#pragma unroll
+          for (int e = 0; e < 32; e += 2) {
+            const double2 qq = *(const double2*)(qc + h * ID + e);
+            d0[h] = __builtin_fma(qq.x, kd0[e], d0[h]);
+            d1[h] = __builtin_fma(qq.x, kd1[e], d1[h]);
+            d0[h] = __builtin_fma(qq.y, kd0[e + 1], d0[h]);
+            d1[h] = __builtin_fma(qq.y, kd1[e + 1], d1[h]);
+          }
       }
-      sc[n] = s + 0.0;                  // -0 -> +0: one bit pattern per value
+      double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+      for (int h = 0; h < IH; ++h) {
+        s0 = s0 + dmul_rounded((double)wrow[h], d0[h] > 0.0 ? d0[h] : 0.0);
+        s1 = s1 + dmul_rounded((double)wrow[h], d1[h] > 0.0 ? d1[h] : 0.0);
+      }
+      sc[n] = s0 + 0.0;                 // -0 -> +0: one bit pattern per value
+      if (n + FB_ROWS < nv) sc[n + FB_ROWS] = s1 + 0.0;
     }
     __syncthreads();
     const int kk = min(topk, nv);
@@ -1387,9 +1438,21 @@ __global__ __launch_bounds__(FB_ROWS) void exact_fallback_kernel(
     for (int shift = 56; shift >= 0; shift -= 8) {
       hist[tid] = 0;
       __syncthreads();
-      for (int n = tid; n < nv; n += FB_ROWS) {
-        const unsigned long long u = ord64(sc[n]);
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255ull], 1);
+      // lanes of a wave that share the first active lane's digit add once (a row of
+      // equal scores would otherwise put every lane's atomic on one bin)
+      for (int n0 = 0; n0 < nv; n0 += FB_ROWS) {
+        const int n = n0 + tid;
+        const unsigned long long u = n < nv ? ord64(sc[n]) : 0ull;
+        const bool act = n < nv && (u & pmask) == prefix;
+        const int dig = (int)((u >> shift) & 255ull);
+        const unsigned long long am = __ballot(act);
+        if (am) {
+          const int first = __ffsll((long long)am) - 1;
+          const int d0 = __shfl(dig, first);
+          const unsigned long long same = __ballot(act && dig == d0);
+          if (lane == first) atomicAdd(&hist[d0], (int)__popcll(same));
+          if (act && dig != d0) atomicAdd(&hist[dig], 1);
+        }
       }
       __syncthreads();
       if (tid < 64) {
@@ -1500,7 +1563,7 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
                       expect <= 0.6 * (double)ns * cap_sel;
     if (pl.global_lists) pl.cap = cap_sel;
   }
-  pl.fb_blocks = L < 32 ? L : 32;
+  pl.fb_blocks = L < FB_BLOCKS ? L : FB_BLOCKS;
   if (pl.fb_blocks < 1) pl.fb_blocks = 1;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += (bytes + 255) / 256 * 256; return o; };
@@ -1511,7 +1574,13 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
   pl.off_fb = take(sizeof(int) * (size_t)L);
   pl.off_cand_s = take(sizeof(float) * (size_t)L * ns * pl.cap);
   pl.off_cand_i = take(sizeof(int) * (size_t)L * ns * pl.cap);
-  pl.off_scratch = take(sizeof(double) * (size_t)pl.fb_blocks * N);
+  // the fallback's scratch rows reuse the candidate lists, which select_refine has
+  // consumed by the time the fallback runs (same stream)
+  pl.off_scratch = pl.off_cand_s;
+  {
+    const size_t scratch_end = pl.off_scratch + (sizeof(double) * (size_t)pl.fb_blocks * N + 255) / 256 * 256;
+    if (scratch_end > off) off = scratch_end;
+  }
   pl.ws_bytes = off;
   pl.filter_lds = 0;                    // all LDS of the score and refine kernels is static
   pl.select_lds = 0;

@@ -126,3 +126,28 @@ def test_sparse_chunk_longer_than_query_block():
         assert torch.equal(o, outs[0])
     ref = oracle.mla_sparse_gather(to_f64(g["q"]), to_f64(g["kv"]), idxn, SCALE_ABS)
     assert_close(host_f64(outs[0]), ref, TOL_BF16, "sparse L=1500, two query blocks", rel_guard=REL_GUARD)
+
+
+def test_dsa_prefill_mid_sweep_point_32k():
+    """A point of the context sweep (N = 32768, L = 512, top-2048, 64 heads), through both
+    attention paths the sweep compares: every row's index set equals the oracle's, and
+    on 17 stratified rows both the sparse and the masked dense output equal dense
+    attention under the oracle's selection."""
+    L, N = 512, 32768
+    g = gen_dsa_prefill(1040, L, N, H=64)
+    t = {k: dev(v) for k, v in g.items()}
+    idx_d = dm.dsa_indexer_topk(t["q_idx"], t["k_idx"], t["w"], TOPK4)
+    sp = dm.mla_prefill_sparse(t["q"], t["kv"], idx_d)
+    md = dm.mla_prefill_masked(t["q"], t["kv"], idx_d)
+    torch.cuda.synchronize()
+    idx = idx_d.cpu().numpy()
+    qf, kf, wf = to_f64(g["q_idx"]), to_f64(g["k_idx"]), to_f64(g["w"])
+    ref = oracle.topk_full(oracle.indexer_scores(qf, kf, wf), TOPK4)
+    bad = [r for r, a, b in zip(range(L), sorted_rows(idx), sorted_rows(ref)) if a != b]
+    print(f"[indexer 512 x 32768] mismatching rows {len(bad)}", flush=True)
+    assert not bad, f"rows {bad[:5]} differ"
+    rows = np.unique(np.concatenate([np.arange(0, L, 32), [L - 1]]))
+    want = oracle.mla_masked_dense(to_f64(g["q"]), to_f64(g["kv"]), ref, SCALE_ABS, rows=rows)
+    assert_close(host_f64(sp)[rows], want, TOL_BF16, "sparse 32768 vs dense under the oracle's mask",
+                 rel_guard=REL_GUARD)
+    assert_close(host_f64(md)[rows], want, TOL_BF16, "masked dense 32768 vs the oracle", rel_guard=REL_GUARD)

@@ -176,3 +176,27 @@ def test_indexer_batched_equals_per_entry():
     for b, g in enumerate(gs):
         s = oracle.indexer_scores(to_f64(g["q_idx"]), to_f64(g["k_idx"]), to_f64(g["w"]))
         _check_rows(idx[b].cpu().numpy(), oracle.topk_full(s, 256), np.arange(12), f"batched indexer entry {b}")
+
+
+def test_indexer_fallback_every_row_full_size():
+    """Worst case of the exact fallback at the full workload size: with q = 0 every visible
+    score is 0 for all 1024 queries over 131072 keys, so every row fails the coverage
+    check and is solved by the fallback from canonical fp64 scores of all its keys; the
+    set is the lowest 2048 indices of every row. The call's time is printed (it is the
+    cliff a badly placed sampled start costs)."""
+    L, N, topk = 1024, 131072, 2048
+    g = gen_indexer(1005, L, N)
+    g["q_idx"].data[:] = 0
+    q, k, w = dev(g["q_idx"]), dev(g["k_idx"]), dev(g["w"])
+    ws = torch.empty(dm.indexer_workspace_bytes(L, N, topk), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((L, topk), dtype=torch.int32, device="cuda")
+    dm.dsa_indexer_topk(q, k, w, topk, out=idx, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    dm.dsa_indexer_topk(q, k, w, topk, out=idx, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    print(f"[indexer fallback, all {L} rows of {N} keys] {a.elapsed_time(b):.2f} ms", flush=True)
+    want = torch.arange(topk, dtype=torch.int32, device="cuda").expand(L, topk)
+    assert torch.equal(idx, want)
