@@ -32,7 +32,8 @@ The line also carries:
   dense_baseline the path the sparse call replaces (masked dense attention) on
                 the same chunk, with the speed-ups of the sparse path.
 
-Kernel and configuration times are medians of per-launch HIP-event timings.
+Kernel and configuration times are medians of per-launch HIP-event timings
+(launches queued back to back).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
        python bench.py --sweep        context sweep, sparse vs masked dense
@@ -304,19 +305,20 @@ def sweep(dm, torch, dev):
 
 
 def _time(fn, torch, reps):
-    """Median over reps of one call's HIP-event time, after two untimed calls."""
+    """Median over reps of one call's HIP-event time. The calls are queued back to back
+    (no synchronisation between them), so each event pair brackets the call's own GPU
+    work rather than the host's launch latency; two untimed calls come first."""
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
-    ts = []
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
         a.record()
         fn()
         b.record()
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
-    return sorted(ts)[len(ts) // 2]
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return ts[len(ts) // 2]
 
 
 def main():
