@@ -1559,9 +1559,28 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
     const int nv0 = L > 0 ? std::min(N, N - L + 1) : N;
     const double mean = (double)topk * SAMPLE / std::max(nv0, 1);
     const double expect = topk + 6.0 * std::sqrt((double)topk * nv0 / SAMPLE) + 8.0 * nv0 / SAMPLE;
-    pl.global_lists = L > 0 && nv0 >= 8 * SAMPLE && mean <= SAMPLE / 8 && SAMPLE <= cap_sel &&
-                      expect <= 0.6 * (double)ns * cap_sel;
-    if (pl.global_lists) pl.cap = cap_sel;
+    auto fits = [&](int n_s, int c_sel) {
+      return L > 0 && nv0 >= 8 * SAMPLE && mean <= SAMPLE / 8 && SAMPLE <= c_sel &&
+             expect <= 0.6 * (double)n_s * c_sel;
+    };
+    pl.global_lists = fits(ns, cap_sel);
+    if (pl.global_lists) {
+      pl.cap = cap_sel;
+      // The list kernel takes GQ queries per workgroup: more splits (up to the four
+      // the refine kernel merges) until the launch has a workgroup per compute unit.
+      const int lgroups = (L + GQ - 1) / GQ;
+      int ns_l = (256 + lgroups - 1) / lgroups;
+      ns_l = std::min(std::min(ns_l, 4), max_by_n);
+      const int cap_l = SR_MAX / std::max(ns_l, 1) / 64 * 64;
+      if (ns_l > ns && fits(ns_l, cap_l)) {
+        ns = ns_l;
+        span = ((N + ns - 1) / ns + TK - 1) / TK * TK;
+        pl.nsplit = ns;
+        pl.span = span;
+        pl.small_off = span <= 65536;
+        pl.cap = cap_l;
+      }
+    }
   }
   pl.fb_blocks = L < FB_BLOCKS ? L : FB_BLOCKS;
   if (pl.fb_blocks < 1) pl.fb_blocks = 1;
