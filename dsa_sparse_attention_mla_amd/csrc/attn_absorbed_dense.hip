@@ -161,26 +161,34 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int qw1 = min(r0 + 32 * wave + 31, nrows - 1) / H;
   const int W = (N + 31) / 32;
   const uint32_t* mrow = MASKED ? mask + ((size_t)b * L + (lane == 0 ? qw0 : qw1)) * W : nullptr;
-  auto load_part = [&](int t, int s) {
-    const int st = t % NST;
-    const int rmax = count - 1 - t * T;                     // last row of the tile that is a key
+  // Byte offset of this lane's chunk of load slot s within a whole tile, fixed for the
+  // kernel; a tile with fewer key rows clamps it to the last chunk of its last key row.
+  uint32_t soff[LPW];
+#pragma unroll
+  for (int s = 0; s < LPW; ++s) {
+    const int c = 64 * (NWV * s + wave_u) + lane, r = c / ROWCH;
+    soff[s] = (uint32_t)(min(r, T - 1) * D * 2 + 16 * min(c - r * ROWCH, D * 2 / 16 - 1));
+  }
+  // Tile t's loads go to stage st. Every step issues one tile's loads, also past the
+  // last tile (then the last tile again, into a stage nobody reads), so the number of
+  // loads in flight is the same on every path; no branch, no per-load arithmetic but a
+  // minimum.
+  auto load_part = [&](int t, int st, int s) {
+    const int rlim = min(count - 1 - t * T, T - 1);         // last row of the tile that is a key
     const void* base = uniform_ptr(kvb + (size_t)t * T * D);
     const int j = NWV * s + wave_u;
-    const int c = 64 * j + lane;
-    const int r = c / ROWCH;                                // row and chunk, recomputed (few registers)
-    const uint32_t off = (uint32_t)(min(r, min(rmax, T - 1)) * D * 2 + 16 * min(c - r * ROWCH, D * 2 / 16 - 1));
     const uint32_t dst = j < NLD ? lds0 + st * STAGE + 1024 * j : lds0 + (uint32_t)DUMP_OFF;
-    dma16s(base, off, dst);
+    dma16s(base, min(soff[s], (uint32_t)(rlim * D * 2 + 16 * (D * 2 / 16 - 1))), dst);
   };
-  auto load_mask = [&](int t) {
+  auto load_mask = [&](int t, int st) {
     if constexpr (MASKED) {
-      if (lane < 2) dma4(mrow + t, lds0 + (uint32_t)(MASK_OFF + ((t % NST) * NWV + wave_u) * 8));
+      if (lane < 2) dma4(mrow + t, lds0 + (uint32_t)(MASK_OFF + (st * NWV + wave_u) * 8));
     }
   };
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t, int st) {
 #pragma unroll
-    for (int s = 0; s < LPW; ++s) load_part(t, s);
-    load_mask(t);
+    for (int s = 0; s < LPW; ++s) load_part(t, st, s);
+    load_mask(t, st);
   };
   constexpr int LPT = LPW + (MASKED ? 1 : 0);              // loads per wave per tile
   // wait until at most n tiles' loads of this wave are in flight
@@ -280,10 +288,10 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(1, 1))
   float lsum = 0.f;                                         // this lane's share of the row's sum
   if (ntiles > 0) {
     // reference for the first pass: the maximum of the first tile (0 if it has no key)
-    load_tile(0);
-    if (ntiles > 1) load_tile(1);
-    if (ntiles > 2) load_tile(2);
-    wait_tiles(min(ntiles - 1, 2));
+    load_tile(0, 0);
+    load_tile(min(1, ntiles - 1), 1);
+    load_tile(min(2, ntiles - 1), 2);
+    wait_tiles(2);
     lds_barrier();
     float mref;
     {
@@ -305,10 +313,10 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
         lsum = 0.f;
         lds_barrier();
-        load_tile(0);
-        if (ntiles > 1) load_tile(1);
-        if (ntiles > 2) load_tile(2);
-        wait_tiles(min(ntiles - 1, 2));
+        load_tile(0, 0);
+        load_tile(min(1, ntiles - 1), 1);
+        load_tile(min(2, ntiles - 1), 2);
+        wait_tiles(2);
         lds_barrier();
       }
       f32x16 c;
@@ -321,7 +329,7 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(1, 1))
       // blocks are fenced, so the reads stay ahead and the vector work stays spread.
       auto step = [&](int t, auto edge_t, auto last_t) {
         constexpr bool LAST = decltype(last_t)::value;
-        wait_tiles(t + 2 < ntiles ? 1 : 0);                 // tile t+1 landed (t+2 may be in flight)
+        wait_tiles(1);                                      // tile t+1 landed (t+2 may be in flight)
         lds_barrier();                                      // ... for every wave; stage t-1 is free
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 pk0, pk1;
@@ -363,13 +371,13 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(1, 1))
         __builtin_amdgcn_sched_barrier(0);
         // value MFMAs of tile t; the loads of tile t+3 (stage t-1, free since the
         // barrier) and the exponent arguments of tile t+1 ride between them
-        const bool load_next = t + 3 < ntiles;
+        const int tl = min(t + 3, ntiles - 1), sl = (t + 3) % NST;
 #pragma unroll
         for (int i = 0; i < 2 * NDB; ++i) {
           o[i >> 1] = mfma32x32x16(vf[i % PDV], (i & 1) ? pk1 : pk0, o[i >> 1]);
           if (i + PDV < 2 * NDB) vf[i % PDV] = vfrag(vb, i + PDV);
-          if (i % 2 == 1 && i / 2 < LPW && load_next) load_part(t + 3, i / 2);
-          if (i == 2 * LPW + 1 && load_next) load_mask(t + 3);
+          if (i % 2 == 1 && i / 2 < LPW) load_part(tl, sl, i / 2);
+          if (i == 2 * LPW + 1) load_mask(tl, sl);
           if constexpr (!LAST) {
             if (i == 3) exponents(t + 1, n, mref, mx, edge_t);
           }
@@ -381,6 +389,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (; t < min(nfull, ntiles - 1); ++t) step(t, no_edge(), more());
       for (; t < ntiles - 1; ++t) step(t, edge(), more());
       step(t, edge(), last());
+      // the spare loads of the last steps land before a second pass reloads the
+      // stages, or the workgroup ends
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       // the row's largest exponent argument: within SPAN of the reference, or a second
       // pass against the row's true maximum
       mx = pair_max(mx);
