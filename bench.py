@@ -13,6 +13,8 @@ The line also carries:
                 its bound, timed with HIP events on its launch stream;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                 workload on this host;
+  graph_ms_per_step  the same step captured once into a HIP graph and replayed
+                (value itself is the eagerly launched step);
   kernels_ms    per-kernel average duration (HIP events);
   other_configs the other configurations, each with its roofline fraction:
                 non-absorbed fp32 at L = N = 256 and bf16 at L = N = 4096,
@@ -388,6 +390,27 @@ def main():
     ms_per_step = dt * 1e3 / args.steps
     step_median_ms = _time(step, torch, args.steps)
 
+    # the same step captured once into a HIP graph and replayed (no per-launch host work)
+    log("bench: graph replay")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    del graph
+
     log("bench: per-kernel event timing")
     per_kernel = {}
     for _ in range(args.steps):
@@ -439,6 +462,7 @@ def main():
         "metric": METRIC, "value": L / (ms_per_step * 1e-3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "step_median_ms": step_median_ms,
+        "graph_ms_per_step": graph_ms_per_step, "graph_tok_s": L / (graph_ms_per_step * 1e-3),
         "config": {"workload": "DSA sparse MLA prefill, one 1024-query chunk at the end of a 131072-position "
                                "context: indexer 32 heads x 128 (top-2048, blocks of 4096) + absorbed attention "
                                "64 heads over gathered 576-wide latent+rope rows (value = first 512)",
