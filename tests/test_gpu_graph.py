@@ -46,3 +46,39 @@ def test_dsa_step_replays_as_hip_graph(L, N):
         torch.cuda.synchronize()
         assert torch.equal(idx, idx_ref), f"replay {r}: index sets differ"
         assert torch.equal(out, out_ref), f"replay {r}: attention output differs"
+
+
+def test_noalloc_decode_replays_as_hip_graph():
+    """The decode entry point that allocates nothing is what a caller under graph capture
+    uses: a captured step replays to the eager result, with eager decode calls (the
+    workspace form and the scratch form on other inputs) run between the replays."""
+    import numpy as np
+    rng = np.random.default_rng(1060)
+    B, H, ps, n = 4, 64, 64, 20000
+    npg = (n + ps - 1) // ps
+    pages = torch.randn((B * npg + 3, ps, 576), generator=torch.Generator().manual_seed(1061)).to(torch.bfloat16).cuda()
+    q = torch.randn((B, H, 576), generator=torch.Generator().manual_seed(1062)).to(torch.bfloat16).cuda()
+    table = torch.from_numpy(rng.permutation(B * npg + 3)[: B * npg].astype(np.int32).reshape(B, npg)).cuda()
+    lens = torch.tensor([n, 1, 12345, 64], dtype=torch.int32, device="cuda")
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+    dm.mla_decode_paged_noalloc(q, pages, table, lens, out=out)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dm.mla_decode_paged_noalloc(q, pages, table, lens, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dm.mla_decode_paged_noalloc(q, pages, table, lens, out=out)
+    other = torch.empty_like(out)
+    for r in range(3):
+        out.zero_()
+        dm.mla_decode_paged(q[:2], pages, table[:2], lens[:2].flip(0).contiguous())
+        dm.mla_decode_paged_noalloc(q[1:], pages, table[1:], lens[1:], out=other[1:])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r} differs"
