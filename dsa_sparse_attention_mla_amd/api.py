@@ -398,7 +398,7 @@ def probe_mfma(grid=1024, iters=4096, reps=3, device="cuda"):
             "what": f"{grid} workgroups x 4 waves, {iters} rounds of 8 independent 32x32x16 bf16 MFMAs"}
 
 
-def probe_stream(nbytes=2 << 30, mode="copy", grid=4096, reps=3, device="cuda"):
+def probe_stream(nbytes=2 << 30, mode="copy", grid=2048, reps=3, device="cuda"):
     """HBM stream rate (diagnostic: the measured ceiling of the bandwidth-bound kernels).
     mode "copy" reads and writes nbytes (2 nbytes moved), "read" reads nbytes."""
     dev = torch.device(device)

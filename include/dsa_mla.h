@@ -241,7 +241,8 @@ int dsa_mla_trace_collect(int max_kernels, char* names, int* counts, double* tot
  * dsa_mla_probe_stream moves `bytes` (a multiple of 64) through HBM with
  * 16-byte-per-lane loads over a grid of `grid` workgroups of 256 threads:
  * mode 0 copies src to dst (bytes read and bytes written), mode 1 only reads src
- * and writes one 32-bit word per thread (dst: 1024 grid bytes). src and dst are
+ * (non-temporal loads, eight per thread in flight) and writes one 32-bit word per
+ * thread (dst: 1024 grid bytes). src and dst are
  * 16-byte-aligned device buffers owned by the caller.
  *
  * Both return DSA_MLA_INVALID_ARG for out-of-range arguments before launching.
