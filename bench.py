@@ -329,7 +329,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=384)
+    ap.add_argument("--cpu-sample", type=int, default=512)
     ap.add_argument("--sweep", action="store_true",
                     help="only run the context sweep (sparse vs masked dense, N = 4K..128K, L = 512/1024)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
