@@ -200,3 +200,41 @@ def test_indexer_fallback_every_row_full_size():
     print(f"[indexer fallback, all {L} rows of {N} keys] {a.elapsed_time(b):.2f} ms", flush=True)
     want = torch.arange(topk, dtype=torch.int32, device="cuda").expand(L, topk)
     assert torch.equal(idx, want)
+
+
+def test_indexer_sampled_start_adversarial_full_size():
+    """The ×4 sampled-key construction at the full workload (1024 queries, 131072 keys):
+    keys at the sampled positions of the first query group are scaled by 4, so its
+    sampled start lands far above its true k-th score; the affected rows must come back
+    exact through the fallback. The call's time and the number of rows the fallback
+    solved (their returned scores are the canonical ones) are printed."""
+    L, N, topk, sample, gq = 1024, 131072, 2048, 2048, 8
+    g = gen_indexer(1070, L, N)
+    nv_min = N - L + 1                       # keys every query of the first group sees
+    pos = (np.arange(sample, dtype=np.int64) * nv_min) // sample
+    kb = g["k_idx"].data
+    rows = kb[pos]
+    nz = (rows & 0x7F80) != 0
+    rows[nz] += 0x0100                        # bf16 exponent + 2: exact multiplication by 4
+    kb[pos] = rows
+    q, k, w = dev(g["q_idx"]), dev(g["k_idx"]), dev(g["w"])
+    ws = torch.empty(dm.indexer_workspace_bytes(L, N, topk), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((L, topk), dtype=torch.int32, device="cuda")
+    dm.dsa_indexer_topk(q, k, w, topk, out=idx, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    idx_d, sc_d = dm.dsa_indexer_topk(q, k, w, topk, return_scores=True, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    check = np.unique(np.concatenate([np.arange(2 * gq), [100, 511, 1023]]))
+    qf, kf, wf = to_f64(g["q_idx"]), to_f64(g["k_idx"]), to_f64(g["w"])
+    s = oracle.indexer_scores(qf, kf, wf, rows=check)
+    ref = oracle.topk_full(s, topk)
+    got = idx_d.cpu().numpy()
+    _check_rows(got, ref, check, "sampled start adversarial, full size")
+    canon = np.take_along_axis(s, got[check].astype(np.int64), axis=1).astype(np.float32)
+    fb_rows = int((sc_d.cpu().numpy()[check] == canon).all(axis=1).sum())
+    print(f"[indexer adversarial 1024 x 131072] {a.elapsed_time(b):.2f} ms; of the {len(check)} checked rows, "
+          f"{fb_rows} came back through the fallback", flush=True)
+    assert fb_rows >= gq                      # the first group's rows all needed the fallback
