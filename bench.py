@@ -40,7 +40,8 @@ Kernel and configuration times are medians of per-launch HIP-event timings
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--no-cpu-baseline]
        python bench.py --sweep        context sweep, sparse vs masked dense
        python bench.py --copy-calibration MIB
-       python bench.py --dense-only   the two dense configurations alone
+       python bench.py --dense-only   the dense configurations alone
+       python bench.py --ceilings-only  the measurement probes alone
 """
 from __future__ import annotations
 
@@ -337,7 +338,7 @@ def main():
     ap.add_argument("--ceilings-only", action="store_true",
                     help="only run the measurement probes (MFMA, HBM copy / read) and print them")
     ap.add_argument("--dense-only", action="store_true",
-                    help="only time the two dense MLA configurations (for counter runs) and print them")
+                    help="only time the dense MLA configurations (fp32 and bf16 non-absorbed, absorbed; for counter runs) and print them")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
