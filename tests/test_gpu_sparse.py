@@ -152,6 +152,20 @@ def test_masked_dense_matches_oracle_and_gather(L, N, topk):
     assert_close(out, gathered, TOL_BF16, "masked dense vs gather")
 
 
+@pytest.mark.parametrize("L,N,topk,H", [(37, 900, 64, 16), (23, 700, 50, 80), (9, 300, 40, 128)])
+def test_masked_dense_other_head_counts(L, N, topk, H):
+    """Head counts other than 64: a workgroup's 128 (query, head) rows then span up to
+    eight queries (H = 16), or a query's heads span two workgroups (H = 80, 128), so the
+    per-wave selection words and causal limits come from different queries."""
+    g, idxn = _masked_case(170 + H, L, N, topk, H=H)
+    q, kv, qf, kvf = dev(g["q"]), dev(g["kv"]), to_f64(g["q"]), to_f64(g["kv"])
+    out = host_f64(dm.mla_prefill_masked(q, kv, dev(idxn)))
+    ref = oracle.mla_masked_dense(qf, kvf, idxn, SCALE)
+    assert_close(out, ref, TOL_BF16, f"masked dense L={L} N={N} topk={topk} H={H}")
+    sparse = host_f64(dm.mla_prefill_sparse(q, kv, dev(idxn)))
+    assert_close(sparse, ref, TOL_BF16, f"sparse L={L} N={N} topk={topk} H={H}")
+
+
 def test_masked_dense_selection_rules():
     """-1 and out-of-range entries ignored, a repeated index selects its key once, a
     selected key past the causal limit stays masked, an empty selection gives zeros."""
