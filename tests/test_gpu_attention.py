@@ -139,6 +139,17 @@ def test_absorbed_small(L, N, H):
     assert_close(host_f64(out[0]), ref, TOL_BF16, f"absorbed L={L} N={N} H={H}")
 
 
+@pytest.mark.parametrize("L,N,H", [(50, 300, 64), (300, 100, 16), (7, 1, 80), (130, 33, 64)])
+def test_absorbed_noncausal(L, N, H):
+    """Non-causal absorbed attention: every query sees all N keys, also with more
+    queries than keys (allowed without the causal mask) and a single key."""
+    q, kv, qf, kvf = _abs(44 + L, L, N, H)
+    out = dm.mla_prefill_dense(q[None], kv[None], causal=False)
+    torch.cuda.synchronize()
+    ref = oracle.mla_absorbed(qf, kvf, 1 / math.sqrt(576), causal=False)
+    assert_close(host_f64(out[0]), ref, TOL_BF16, f"absorbed non-causal L={L} N={N} H={H}")
+
+
 def test_absorbed_sharpened():
     q, kv, qf, kvf = _abs(41, 24, 90, 64)
     scale = 8 / math.sqrt(576)
