@@ -309,9 +309,16 @@ def sweep(dm, torch, dev):
 def _time(fn, torch, reps):
     """Median over reps of one call's HIP-event time. The calls are queued back to back
     (no synchronisation between them), so each event pair brackets the call's own GPU
-    work rather than the host's launch latency; two untimed calls come first."""
-    for _ in range(2):
+    work rather than the host's launch latency. Untimed calls come first, for at least
+    30 ms of GPU time: a configuration's first calls after other work run up to 15%
+    slower until the GPU settles (measured on the 0.1 ms non-absorbed configuration)."""
+    t0 = time.perf_counter()
+    for i in range(400):
         fn()
+        if i >= 4 and i % 4 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 > 0.03:
+                break
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
