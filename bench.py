@@ -12,9 +12,13 @@ The line also carries:
   roofline      the dominant kernel's achieved rate against the MI355X peak of
                 its bound, timed with HIP events on its launch stream;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
-                workload on this host;
+                workload on this host (per stage, with the CPU model and BLAS
+                library), and the oracle of the two dense configurations on a
+                few rows each;
   graph_ms_per_step  the same step captured once into a HIP graph and replayed
                 (value itself is the eagerly launched step);
+  pages_protocol_ms  the step timed as the pages time theirs: the mean of
+                three runs after one warm-up run;
   kernels_ms    per-kernel average duration (HIP events);
   other_configs the other configurations, each with its roofline fraction:
                 non-absorbed fp32 at L = N = 256 and bf16 at L = N = 4096,
@@ -138,15 +142,63 @@ def cpu_baseline(g, sample):
     kv64 = to_f64(g["kv"])
     t0 = time.perf_counter()
     s = oracle.indexer_scores(qf, kf, wf, rows=rows)
+    t1 = time.perf_counter()
     sel = oracle.topk_full(s, TOPK)
     idx = np.full((L, TOPK), -1, dtype=np.int64)
     idx[rows] = sel
+    t2 = time.perf_counter()
     oracle.mla_sparse_gather(q64, kv64, idx, 1.0 / np.sqrt(576.0), rows=rows)
-    dt = time.perf_counter() - t0
+    t3 = time.perf_counter()
+    dt = t3 - t0
     return {"value": sample / dt, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{sample} of the {L} query rows (evenly spaced) of the same workload: canonical fp64 indexer "
                       f"scores over all {N} keys, full stable-sort top-{TOPK}, fp64 gather attention over {H} heads; "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s",
+            "stages_s": {"indexer_scores": t1 - t0, "topk_full_sort": t2 - t1, "sparse_gather_attention": t3 - t2},
+            "host": host_info()}
+
+
+def host_info():
+    """CPU model and the BLAS library NumPy uses, for the oracle timings."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{k: i.get(k) for k in ("internal_api", "version", "num_threads")}
+                for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "blas": blas}
+
+
+def cpu_dense_stages(rows1=256, rows2=16):
+    """The fp64 oracle of the two dense configurations on a few query rows each (the
+    last rows, which see the most keys): seconds per row, beside the GPU kernels."""
+    import numpy as np
+    import oracle
+    from synth import gen_absorbed, gen_nonabsorbed, to_f64
+    out = {}
+    g = gen_nonabsorbed(1001, 4096, 4096, H=16, dtype="bf16", scale=0.5)
+    a = {k: to_f64(v) for k, v in g.items()}
+    r = np.arange(4096 - rows1, 4096)
+    t0 = time.perf_counter()
+    oracle.mla_nonabsorbed(a["qn"], a["qr"], a["kn"], a["kr"], a["v"], 1.0 / np.sqrt(192.0), rows=r)
+    out["nonabsorbed_bf16_L4096_N4096_H16"] = {"rows": rows1, "s_per_row": (time.perf_counter() - t0) / rows1}
+    g = gen_absorbed(1002, 512, 16384, H=64)
+    q64, kv64 = to_f64(g["q"]), to_f64(g["kv"])
+    r = np.arange(512 - rows2, 512)
+    t0 = time.perf_counter()
+    oracle.mla_absorbed(q64, kv64, 1.0 / np.sqrt(576.0), rows=r)
+    out["absorbed_bf16_L512_N16384_H64"] = {"rows": rows2, "s_per_row": (time.perf_counter() - t0) / rows2}
+    return out
 
 
 def dense_configs(dm, torch, reps=10, ceil=None):
@@ -395,6 +447,14 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / args.steps
+    # the pages' own protocol: the mean of three runs after one warm-up run
+    step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    pages_protocol_ms = (time.perf_counter() - t0) * 1e3 / 3
     step_median_ms = _time(step, torch, args.steps)
 
     # the same step captured once into a HIP graph and replayed (no per-launch host work)
@@ -464,12 +524,14 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         cpu = cpu_baseline(g, args.cpu_sample)
+        cpu["dense_configs"] = cpu_dense_stages()
 
     line = {
         "metric": METRIC, "value": L / (ms_per_step * 1e-3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "step_median_ms": step_median_ms,
         "graph_ms_per_step": graph_ms_per_step, "graph_tok_s": L / (graph_ms_per_step * 1e-3),
+        "pages_protocol_ms": pages_protocol_ms,
         "config": {"workload": "DSA sparse MLA prefill, one 1024-query chunk at the end of a 131072-position "
                                "context: indexer 32 heads x 128 (top-2048, blocks of 4096) + absorbed attention "
                                "64 heads over gathered 576-wide latent+rope rows (value = first 512)",
