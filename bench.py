@@ -69,12 +69,12 @@ SEED = 1004
 # 524302 KiB fetched and 1048576 KiB written per dispatch: fetch counts half the
 # bytes a copy moves on this chip, write counts all of them.
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
-# Counter readings (KiB per dispatch, mean of the 13 launches of this workload in a
+# Counter readings (KiB per dispatch, mean of the 32 launches of this workload in a
 # 2-step bench run) and a digest of the kernel sources they were taken on.
 COUNTERS = {
-    "indexer_score_filter": {"fetch_kib": 165037.3, "write_kib": 40693.9,
-                             "sources": ("indexer.hip", "common.h"), "sha256_16": "ebe5c359f394b33e"},
-    "sparse_attn": {"fetch_kib": 891323.5, "write_kib": 65951.5,
+    "indexer_score_filter": {"fetch_kib": 165036.7, "write_kib": 40684.9,
+                             "sources": ("indexer.hip", "common.h"), "sha256_16": "93f2773cf2bf1737"},
+    "sparse_attn": {"fetch_kib": 891426.7, "write_kib": 66028.6,
                     "sources": ("attn_absorbed.hip", "common.h"), "sha256_16": "22423f6382a19b7c"},
 }
 METRIC = "prefill tok/s at 128K ctx (sparse MLA); MFMA util %, HBM GB/s % of peak"

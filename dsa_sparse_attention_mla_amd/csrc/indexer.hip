@@ -9,7 +9,8 @@
 // fused multiply-add), ties to the lower key index.
 //
 // Pipeline, all on the caller's stream:
-//  1. key_norm_partial:   per-block max of ||k_n||^2 (fp32).
+//  1. key_norm_partial:   per-block max of ||k_n|| (squares summed in fp64, so no
+//                         bf16 key overflows or underflows it).
 //  2. query_eps:          eps_i, a rigorous bound on |s_hat - s| for the fp32
 //                         MFMA score s_hat, from sum_h |w_h| ||q_h|| * max_n ||k_n||.
 //  3. one score kernel, both with 32x32x16 bf16 MFMA scores for 32 heads and the
@@ -32,8 +33,10 @@
 //                         between are re-scored canonically in fp64 and ranked by
 //                         (s desc, index asc) to fill the rest.
 //  5. exact_fallback:     rows that failed the coverage check or whose lists
-//                         overflowed (huge ties, a sampled threshold set badly) are
-//                         solved from the canonical fp64 score of every visible key.
+//                         overflowed (huge ties, a sampled threshold set badly), and
+//                         rows whose magnitudes could overflow the fp32 scores (eps
+//                         = +inf), are solved from the canonical fp64 score of every
+//                         visible key.
 // Output rows are in ascending key order, padded with -1.
 #include <cmath>
 
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(256) void key_norm_partial_kernel(const uint16_t* _
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = tid >> 4, l16 = tid & 15;   // 16 keys per pass, 16 lanes per key
   constexpr int U = 8;                        // passes in flight per thread
-  float mx = 0.f;
+  double mx = 0.0;                            // largest squared norm of this thread's keys
   const int stride = gridDim.x * 16;
   for (int n0 = blockIdx.x * 16 + sub; n0 < N; n0 += U * stride) {
     u32x4 v[U];
@@ -91,20 +94,22 @@ __global__ __launch_bounds__(256) void key_norm_partial_kernel(const uint16_t* _
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float acc = 0.f;
+      double acc = 0.0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float a = bf_bits2f((uint16_t)(v[u][e] & 0xFFFFu)), b = bf_bits2f((uint16_t)(v[u][e] >> 16));
-        acc += a * a + b * b;
+        const double a = bf_bits2f((uint16_t)(v[u][e] & 0xFFFFu)), b = bf_bits2f((uint16_t)(v[u][e] >> 16));
+        acc = __fma_rn(a, a, acc);
+        acc = __fma_rn(b, b, acc);
       }
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
-      mx = fmaxf(mx, acc);
+      mx = fmax(mx, acc);
     }
   }
 #pragma unroll
-  for (int off = 16; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) red[wave] = mx;
+  for (int off = 16; off < 64; off <<= 1) mx = fmax(mx, __shfl_xor(mx, off));
+  // the norm, rounded up into fp32 (+inf past its range)
+  if (lane == 0) red[wave] = (float)(sqrt(mx) * (1.0 + 0x1p-20));
   __syncthreads();
   if (tid == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
@@ -114,13 +119,19 @@ __global__ __launch_bounds__(256) void key_norm_partial_kernel(const uint16_t* _
 // round-to-nearest or toward zero: u = 2^-23); the ReLU is 1-Lipschitz; the
 // weight product and the 32-term head sum add (u + gamma_32) * sum_h |w_h| |d_h|
 // (weights of either sign).
-// The constant below is that sum (1.92e-5) with a 30% margin for the fp32
-// evaluation of the norms.
+// The constant below is that sum (1.92e-5) with a 30% margin. The norms are
+// summed in fp64, so they neither overflow nor underflow for any bf16 input; an
+// absolute term covers fp32 results below the normal range, which the matrix unit
+// may flush (at most 2^-126 per product, partial sum or weighted head term:
+// below 2^-117 * (sum_h |w_h| + 1) per score).
+// Inputs whose fp32 score could overflow (max_h ||q_h|| max ||k|| or
+// sum_h |w_h| ||q_h|| max ||k|| at or past 2^120, or non-finite) get eps = +inf,
+// which sends the query to the exact fallback.
 __global__ __launch_bounds__(64) void query_eps_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                                                        const float* __restrict__ partial, int nparts, int L,
                                                        float* __restrict__ eps) {
   const int i = blockIdx.x, lane = threadIdx.x;
-  float km = 0.f;
+  float km = 0.f;                                 // max_n ||k_n|| (rounded up)
   {
     // all of this lane's partial maxima in flight at once (nparts = NORM_BLOCKS)
     constexpr int PPL = NORM_BLOCKS / 64;
@@ -132,26 +143,38 @@ __global__ __launch_bounds__(64) void query_eps_kernel(const uint16_t* __restric
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) km = fmaxf(km, __shfl_xor(km, off));
-  float contrib = 0.f;
+  if (km != km) km = INFINITY;                    // (a NaN partial cannot occur; be safe)
+  double contrib = 0.0, qn = 0.0, aw = 0.0;      // |w_h| ||q_h||, ||q_h||, |w_h|
   if (lane < IH) {
     const uint16_t* qh = q + ((size_t)i * IH + lane) * ID;
     u32x4 v[ID / 8];
 #pragma unroll
     for (int c = 0; c < ID / 8; ++c) v[c] = *(const u32x4*)(qh + 8 * c);
-    float acc = 0.f;
+    double acc = 0.0;
 #pragma unroll
     for (int c = 0; c < ID / 8; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float a = bf_bits2f((uint16_t)(v[c][e] & 0xFFFFu)), b = bf_bits2f((uint16_t)(v[c][e] >> 16));
-        acc += a * a;
-        acc += b * b;
+        const double a = bf_bits2f((uint16_t)(v[c][e] & 0xFFFFu)), b = bf_bits2f((uint16_t)(v[c][e] >> 16));
+        acc = __fma_rn(a, a, acc);
+        acc = __fma_rn(b, b, acc);
       }
-    contrib = fabsf(w[(size_t)i * IH + lane]) * sqrtf(acc);
+    qn = sqrt(acc) * (1.0 + 0x1p-20);
+    aw = fabs((double)w[(size_t)i * IH + lane]);
+    contrib = aw * qn;
   }
+  double qmax = qn;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) contrib += __shfl_xor(contrib, off);
-  if (lane == 0) eps[i] = 2.5e-5f * contrib * sqrtf(km * 1.0001f) * 1.0001f + 1e-30f;
+  for (int off = 1; off < 64; off <<= 1) {
+    contrib += __shfl_xor(contrib, off);
+    aw += __shfl_xor(aw, off);
+    qmax = fmax(qmax, __shfl_xor(qmax, off));
+  }
+  if (lane == 0) {
+    const double kmd = km, bound = contrib * kmd;
+    const bool safe = bound < 0x1p120 && qmax * kmd < 0x1p120;   // false for +inf and NaN too
+    eps[i] = safe ? (float)(2.5e-5 * bound * 1.0002) + (float)((aw + 1.0) * 0x1p-117) + 1e-30f : INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------- 3. score + running candidates
@@ -999,6 +1022,11 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
   const int nv = min(N, p + 1);
   int32_t* orow = idx_out + (size_t)i * topk;
   float* srow = score_out ? score_out + (size_t)i * topk : nullptr;
+  // magnitudes past the range the fp32 scores are safe in (eps = +inf): exact fallback
+  if (!(eps_in[i] < INFINITY)) {
+    if (tid == 0) fb_flag[i] = 1;
+    return;
+  }
 
   // ---- candidates into registers. Split sp's list fills slots [pre4[sp], pre4[sp] +
   // cnt rounded up to 4); thread t loads slot groups t + 256 u (4 slots each, one

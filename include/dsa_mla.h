@@ -108,6 +108,9 @@ int mla_prefill_dense(int mode, int dtype, int B, int L, int N, int H,
  * The result is the EXACT top-k set of the canonical score (dot products in
  * fp64 summed over dims in ascending order, head terms added in ascending head
  * order, every operation separately rounded), ties to the lower key index.
+ * This holds for any finite inputs: queries whose magnitudes could overflow the
+ * fp32 filter scores are resolved by the exact fp64 path. (NaN or infinite inputs
+ * have no canonical score; their result is unspecified.)
  * Rows are written in ascending key order; a row with fewer than topk visible
  * keys holds all of them followed by -1. score_out (nullable) [B,L,topk] fp32
  * receives the fp32 MFMA score of each returned key (-inf on padding).

@@ -115,6 +115,43 @@ def test_indexer_signed_weights_exact_ties():
     _check_rows(idx, ref, np.arange(12), "signed exact-input indexer")
 
 
+def _scale_pow2(t, e):
+    """Multiply every nonzero bf16 value of t by 2^e exactly (a shift of the exponent field)."""
+    b = t.data
+    ex = (b.astype(np.int32) >> 7) & 0xFF
+    nz = ex != 0
+    assert np.all(ex[nz] + e >= 1) and np.all(ex[nz] + e <= 254), "scaled values leave the bf16 normal range"
+    b[nz] = (b[nz].astype(np.int32) + (e << 7)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("N,eq,ek,ew,what", [
+    (9000, 20, 110, 0, "dot products past the fp32 range"),
+    (40000, 20, 110, 0, "dot products past the fp32 range, sampled start"),
+    (9000, -66, 60, 0, "query squares below the fp32 range, products normal"),
+    (9000, -60, -60, 0, "products near and below the fp32 normal range"),
+    (9000, 0, 0, 100, "weights of 2^100 (scores still in fp32 range)"),
+    (9000, 0, 0, 120, "weights of 2^120 (scores may overflow fp32)"),
+])
+def test_indexer_extreme_magnitudes(N, eq, ek, ew, what):
+    """q, k (and w) scaled by powers of two far outside the range the fp32 filter is
+    comfortable in. The canonical fp64 scores only scale, so the set cannot change,
+    while the fp32 scores overflow to inf / NaN, or their norms underflow, or products
+    flush to zero: the error bound must still hold (norms taken in fp64, an absolute
+    term for flushed results) or send the query to the exact fallback. Every row must
+    equal the oracle's set and the unscaled inputs' set."""
+    L, topk = 6 if N < 16384 else 4, 512
+    g = gen_indexer(140, L, N)
+    idx0, _, ref0, _ = _run(g, topk)
+    _check_rows(idx0, ref0, np.arange(L), f"unscaled, N={N}")
+    _scale_pow2(g["q_idx"], eq)
+    _scale_pow2(g["k_idx"], ek)
+    if ew:
+        g["w"].data[:] = g["w"].data * np.float32(2.0 ** ew)
+    idx, _, ref, _ = _run(g, topk)
+    _check_rows(idx, ref, np.arange(L), f"indexer, {what}")
+    assert sorted_rows(idx) == sorted_rows(idx0)
+
+
 def _eps_rows(g, rows):
     """The per-query error bound the filter's band is built on, recomputed in fp64:
     2.5e-5 * sum_h |w_h| ||q_h|| * max_n ||k_n||."""
