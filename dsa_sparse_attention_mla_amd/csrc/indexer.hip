@@ -62,6 +62,10 @@ constexpr int SR_MAX = SR_J * 256;      // candidates per query select_refine ho
 constexpr int NORM_BLOCKS = 1024;
 constexpr int FB_ROWS = 256;            // block size of the fallback kernel
 constexpr int FB_BLOCKS = 256;          // fallback workgroups: one per compute unit
+#ifndef FB_CHUNK
+#define FB_CHUNK 16                     // key dims converted to fp64 at a time in the fallback
+#endif
+static_assert(FB_CHUNK % 8 == 0 && ID % FB_CHUNK == 0, "whole 16-byte key loads per chunk");
 }  // namespace
 
 __device__ __forceinline__ void wave_sync() {
@@ -1418,16 +1422,33 @@ __global__ __launch_bounds__(FB_ROWS) void exact_fallback_kernel(
       double d0[IH], d1[IH];
 #pragma unroll
       for (int h = 0; h < IH; ++h) d0[h] = d1[h] = 0.0;
-      for (int c0 = 0; c0 < ID; c0 += 32) {
-        u32x4 kw0[4], kw1[4];
+      // 16-dim chunks: the 64 head dots, the chunk of both keys in fp64 and the query
+      // reads stay within the vector registers (32-dim chunks spilled); the next
+      // chunk's key loads are in flight while this one is multiplied
+      u32x4 kn0[FB_CHUNK / 8], kn1[FB_CHUNK / 8];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          kw0[x] = kr0[c0 / 8 + x];
-          kw1[x] = kr1[c0 / 8 + x];
+      for (int x = 0; x < FB_CHUNK / 8; ++x) {
+        kn0[x] = kr0[x];
+        kn1[x] = kr1[x];
+      }
+#pragma unroll
+      for (int c0 = 0; c0 < ID; c0 += FB_CHUNK) {
+        u32x4 kw0[FB_CHUNK / 8], kw1[FB_CHUNK / 8];
+#pragma unroll
+        for (int x = 0; x < FB_CHUNK / 8; ++x) {
+          kw0[x] = kn0[x];
+          kw1[x] = kn1[x];
         }
-        double kd0[32], kd1[32];
+        if (c0 + FB_CHUNK < ID) {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
+          for (int x = 0; x < FB_CHUNK / 8; ++x) {
+            kn0[x] = kr0[(c0 + FB_CHUNK) / 8 + x];
+            kn1[x] = kr1[(c0 + FB_CHUNK) / 8 + x];
+          }
+        }
+        double kd0[FB_CHUNK], kd1[FB_CHUNK];
+#pragma unroll
+        for (int e = 0; e < FB_CHUNK; ++e) {
           const uint32_t w0 = kw0[e / 8][(e % 8) / 2], w1 = kw1[e / 8][(e % 8) / 2];
           kd0[e] = (double)bf_bits2f((uint16_t)((e & 1) ? (w0 >> 16) : (w0 & 0xFFFFu)));
           kd1[e] = (double)bf_bits2f((uint16_t)((e & 1) ? (w1 >> 16) : (w1 & 0xFFFFu)));
@@ -1436,7 +1457,7 @@ __global__ __launch_bounds__(FB_ROWS) void exact_fallback_kernel(
 #pragma unroll
         for (int h = 0; h < IH; ++h)
 #pragma unroll
-          for (int e = 0; e < 32; e += 2) {
+          for (int e = 0; e < FB_CHUNK; e += 2) {
             const double2 qq = *(const double2*)(qc + h * ID + e);
             d0[h] = __builtin_fma(qq.x, kd0[e], d0[h]);
             d1[h] = __builtin_fma(qq.x, kd1[e], d1[h]);
