@@ -21,6 +21,12 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _on(device):
+    """The library launches on the current HIP device: make it the tensors' device
+    for the call (on a host with several GPUs the current one may be another)."""
+    return torch.cuda.device(device)
+
+
 def _need(t, name, dtype, ndim):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -107,11 +113,12 @@ def mla_prefill_dense(q, k, *, q_rope=None, k_rope=None, v=None, scale=None, cau
         out = torch.empty((B, L, H, dv), dtype=dtype, device=q.device)
     else:
         _need_out(out, "out", dtype, (B, L, H, dv), q.device)
-    st = lib().mla_prefill_dense(
-        _lib.MODE_ABSORBED if absorbed else _lib.MODE_NONABSORBED,
-        _lib.BF16 if dtype == torch.bfloat16 else _lib.F32,
-        B, L, N, H, _ptr(q), _ptr(q_rope), _ptr(k), _ptr(k_rope), _ptr(v), _ptr(out),
-        float(scale), 1 if causal else 0, None, None, _stream(q.device))
+    with _on(q.device):
+        st = lib().mla_prefill_dense(
+            _lib.MODE_ABSORBED if absorbed else _lib.MODE_NONABSORBED,
+            _lib.BF16 if dtype == torch.bfloat16 else _lib.F32,
+            B, L, N, H, _ptr(q), _ptr(q_rope), _ptr(k), _ptr(k_rope), _ptr(v), _ptr(out),
+            float(scale), 1 if causal else 0, None, None, _stream(q.device))
     check(st, "mla_prefill_dense")
     return out
 
@@ -154,8 +161,9 @@ def dsa_indexer_topk(q_idx, k_idx, w, topk, *, block=4096, return_scores=False, 
     scores = torch.empty((B, L, topk), dtype=torch.float32, device=dev) if return_scores else None
 
     def call(ws, ws_bytes):
-        return lib().dsa_indexer_topk(B, L, N, Hi, Di, _ptr(q_idx), _ptr(k_idx), _ptr(w), int(topk), int(block),
-                                      _ptr(idx), _ptr(scores), ws, ws_bytes, _stream(dev))
+        with _on(dev):
+            return lib().dsa_indexer_topk(B, L, N, Hi, Di, _ptr(q_idx), _ptr(k_idx), _ptr(w), int(topk),
+                                          int(block), _ptr(idx), _ptr(scores), ws, ws_bytes, _stream(dev))
 
     if workspace is not None:
         _need_workspace(workspace, indexer_workspace_bytes(L, N, topk, block, Hi, Di), dev)
@@ -190,8 +198,9 @@ def mla_prefill_sparse(q, kv, idx, *, scale=None, query_block=1024, out=None):
     else:
         _need_out(out, "out", torch.bfloat16, (B, L, H, 512) if batched else (L, H, 512), q.device)
         out = out if batched else out[None]
-    st = lib().mla_prefill_sparse(B, L, N, H, _ptr(q), _ptr(kv), _ptr(idx), idx.shape[2], float(scale),
-                                  int(query_block), _ptr(out), None, None, _stream(q.device))
+    with _on(q.device):
+        st = lib().mla_prefill_sparse(B, L, N, H, _ptr(q), _ptr(kv), _ptr(idx), idx.shape[2], float(scale),
+                                      int(query_block), _ptr(out), None, None, _stream(q.device))
     check(st, "mla_prefill_sparse")
     return out if batched else out[0]
 
@@ -236,8 +245,9 @@ def mla_prefill_masked(q, kv, idx, *, scale=None, out=None, workspace=None):
     else:
         _need_workspace(workspace, nbytes, q.device)
     n = ctypes.c_size_t(workspace.numel())
-    st = lib().mla_prefill_masked(B, L, N, H, _ptr(q), _ptr(kv), _ptr(idx), idx.shape[2], float(scale), _ptr(out),
-                                  _ptr(workspace), ctypes.byref(n), _stream(q.device))
+    with _on(q.device):
+        st = lib().mla_prefill_masked(B, L, N, H, _ptr(q), _ptr(kv), _ptr(idx), idx.shape[2], float(scale),
+                                      _ptr(out), _ptr(workspace), ctypes.byref(n), _stream(q.device))
     check(st, "mla_prefill_masked")
     return out if batched else out[0]
 
@@ -280,8 +290,9 @@ def mla_decode_paged(q, kv_pages, page_table, seq_lens, *, scale=None, out=None,
     else:
         _need_workspace(workspace, nbytes, q.device)
     n = ctypes.c_size_t(workspace.numel())
-    st = lib().mla_decode_paged(B, H, P, ps, maxp, _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
-                                float(scale), _ptr(out), _ptr(workspace), ctypes.byref(n), _stream(q.device))
+    with _on(q.device):
+        st = lib().mla_decode_paged(B, H, P, ps, maxp, _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(seq_lens),
+                                    float(scale), _ptr(out), _ptr(workspace), ctypes.byref(n), _stream(q.device))
     check(st, "mla_decode_paged")
     return out
 
@@ -303,8 +314,10 @@ def mla_decode_paged_noalloc(q, kv_pages, page_table, seq_lens, *, scale=None, o
     _need_out(out, "out", torch.bfloat16, (B, H, 512), q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(576)
-    st = lib().mla_decode_paged_noalloc(B, H, P, ps, page_table.shape[1], _ptr(q), _ptr(kv_pages), _ptr(page_table),
-                                        _ptr(seq_lens), float(scale), _ptr(out), _stream(q.device))
+    with _on(q.device):
+        st = lib().mla_decode_paged_noalloc(B, H, P, ps, page_table.shape[1], _ptr(q), _ptr(kv_pages),
+                                            _ptr(page_table), _ptr(seq_lens), float(scale), _ptr(out),
+                                            _stream(q.device))
     check(st, "mla_decode_paged_noalloc")
     return out
 
@@ -387,8 +400,9 @@ def probe_mfma(grid=1024, iters=4096, reps=3, device="cuda"):
     khz = ctypes.c_int(0)
 
     def launch():
-        check(lib().dsa_mla_probe_mfma(grid, iters, _ptr(cyc), _ptr(wall), _ptr(sink), ctypes.byref(khz),
-                                       _stream(dev)), "dsa_mla_probe_mfma")
+        with _on(dev):
+            check(lib().dsa_mla_probe_mfma(grid, iters, _ptr(cyc), _ptr(wall), _ptr(sink), ctypes.byref(khz),
+                                           _stream(dev)), "dsa_mla_probe_mfma")
 
     ms = _event_ms(launch, dev, reps)
     c, w = cyc.double().mean().item(), wall.double().mean().item()
@@ -407,7 +421,9 @@ def probe_stream(nbytes=2 << 30, mode="copy", grid=2048, reps=3, device="cuda"):
     m = {"copy": 0, "read": 1}[mode]
 
     def launch():
-        check(lib().dsa_mla_probe_stream(m, _ptr(src), _ptr(dst), nbytes, grid, _stream(dev)), "dsa_mla_probe_stream")
+        with _on(dev):
+            check(lib().dsa_mla_probe_stream(m, _ptr(src), _ptr(dst), nbytes, grid, _stream(dev)),
+                  "dsa_mla_probe_stream")
 
     ms = _event_ms(launch, dev, reps)
     moved = nbytes * (2 if m == 0 else 1)
