@@ -24,7 +24,8 @@
  *   dsa_mla_trace_enable), and, per device, the fixed scratch array of
  *   mla_decode_paged_noalloc with its looked-up device address. All of it is
  *   guarded by locks; nothing else persists between calls.
- * Memory: every tensor argument is a DEVICE pointer owned by the caller,
+ * Memory: every tensor argument is a DEVICE pointer of the current device (the
+ *   one kernels are launched on), owned by the caller,
  *   contiguous row-major in the layout stated per call, with a 16-byte aligned
  *   base. Inputs are only read; outputs are fully overwritten.
  * bf16: passed as 16-bit storage (the upper half of an IEEE fp32). Arithmetic
