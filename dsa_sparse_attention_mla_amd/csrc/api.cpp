@@ -129,6 +129,7 @@ int mla_prefill_dense(int mode, int dtype, int B, int L, int N, int H, const voi
     if (q_rope != nullptr || k_rope != nullptr || v != nullptr) return DSA_MLA_INVALID_ARG;
     if (dtype != DSA_MLA_BF16) return DSA_MLA_UNSUPPORTED;
     if (H % 16 != 0) return DSA_MLA_UNSUPPORTED;
+    if ((long long)L * H > INT32_MAX) return DSA_MLA_UNSUPPORTED;   // (query, head) rows are 32-bit
   }
   const int wsr = workspace_step(0, ws, ws_bytes);
   if (wsr >= 0) return wsr;
@@ -200,6 +201,7 @@ int mla_prefill_masked(int B, int L, int N, int H, const void* q, const void* kv
   if (q == nullptr || kv == nullptr || idx == nullptr || out == nullptr) return DSA_MLA_INVALID_ARG;
   if (!aligned16(q) || !aligned16(kv) || !aligned4(idx) || !aligned16(out)) return DSA_MLA_INVALID_ARG;
   if (H % 16 != 0) return DSA_MLA_UNSUPPORTED;
+  if ((long long)L * H > INT32_MAX) return DSA_MLA_UNSUPPORTED;     // (query, head) rows are 32-bit
   const size_t words = (size_t)B * L * (size_t)((N + 31) / 32);
   const int wsr = workspace_step(words * 4, ws, ws_bytes);
   if (wsr >= 0) return wsr;

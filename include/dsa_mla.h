@@ -88,7 +88,8 @@ enum { DSA_MLA_F32 = 0, DSA_MLA_BF16 = 1 };
  * latent+rope row per position, shared by all heads):
  *   score[i,j] = scale * q[i,h,:] . kv[j,:]          out[i,h,:] = softmax . kv[:, 0:512]
  *   q  [B,L,H,576] (512 latent then 64 rope)  k = kv [B,N,576]  out [B,L,H,512]
- *   q_rope, k_rope and v must be NULL. dtype must be DSA_MLA_BF16; H a multiple of 16.
+ *   q_rope, k_rope and v must be NULL. dtype must be DSA_MLA_BF16; H a multiple of 16;
+ *   L * H < 2^31 (DSA_MLA_UNSUPPORTED otherwise).
  *
  * causal: 1 = bottom-right causal (see above; needs L <= N), 0 = every key.
  * B >= 1 is allowed. B == 0 or L == 0 is a no-op. A query that sees no key
@@ -161,7 +162,7 @@ int mla_prefill_sparse(int B, int L, int N, int H, const void* q, const void* kv
  * once, and a selected key past the causal limit stays masked. Every visible
  * key is visited: this is the dense cost the sparse call removes. A row with no
  * selected visible key gets zeros. Supported: B >= 1, 0 <= L <= N, H a multiple
- * of 16. Needs workspace: B*L*ceil(N/32) 32-bit words for the selection bitmaps
+ * of 16, L * H < 2^31. Needs workspace: B*L*ceil(N/32) 32-bit words for the selection bitmaps
  * (query its size with ws == NULL); the bitmaps are rebuilt on every call.
  */
 int mla_prefill_masked(int B, int L, int N, int H, const void* q, const void* kv, const int32_t* idx, int topk,

@@ -59,6 +59,7 @@ def _sparse(**kw):
     (dict(mode=1), _lib.INVALID_ARG),                                   # absorbed with rope/v pointers
     (dict(mode=1, q_rope=None, k_rope=None, v=None, dtype=0), _lib.UNSUPPORTED),
     (dict(mode=1, q_rope=None, k_rope=None, v=None, H=24), _lib.UNSUPPORTED),
+    (dict(mode=1, q_rope=None, k_rope=None, v=None, L=1 << 25, N=1 << 25, H=64), _lib.UNSUPPORTED),  # L*H >= 2^31
     (dict(), _lib.ARCH),                                                 # valid; no gfx950 device here
     (dict(L=0), _lib.OK), (dict(B=0), _lib.OK),                          # empty -> no-op
 ])
@@ -131,6 +132,7 @@ def _masked(**kw):
     (dict(H=24), _lib.UNSUPPORTED), (dict(topk=0), _lib.INVALID_ARG), (dict(idx=None), _lib.INVALID_ARG),
     (dict(L=65, N=64), _lib.INVALID_ARG), (dict(out=MIS), _lib.INVALID_ARG), (dict(kv=None), _lib.INVALID_ARG),
     (dict(scale=float("nan")), _lib.INVALID_ARG), (dict(), _lib.WORKSPACE), (dict(L=0), _lib.OK),
+    (dict(L=1 << 25, N=1 << 25), _lib.UNSUPPORTED),                      # L*H >= 2^31 (64 heads)
 ])
 def test_masked_validation(kw, code):
     assert _masked(**kw) == code
