@@ -125,6 +125,7 @@ int mla_prefill_dense(int mode, int dtype, int B, int L, int N, int H, const voi
   if (mode == DSA_MLA_MODE_NONABSORBED) {
     if (q_rope == nullptr || k_rope == nullptr || v == nullptr) return DSA_MLA_INVALID_ARG;
     if (!aligned16(q_rope) || !aligned16(k_rope) || !aligned16(v)) return DSA_MLA_INVALID_ARG;
+    if (H > 65535) return DSA_MLA_UNSUPPORTED;    // heads index a grid dimension; tile offsets are 32-bit
   } else {
     if (q_rope != nullptr || k_rope != nullptr || v != nullptr) return DSA_MLA_INVALID_ARG;
     if (dtype != DSA_MLA_BF16) return DSA_MLA_UNSUPPORTED;

@@ -81,7 +81,7 @@ enum { DSA_MLA_F32 = 0, DSA_MLA_BF16 = 1 };
  *   q      [B,L,H,128]   q_rope [B,L,H,64]
  *   k      [B,N,H,128]   k_rope [B,N,64]     v [B,N,H,128]
  *   out    [B,L,H,128]
- *   dtype DSA_MLA_F32 or DSA_MLA_BF16 (all tensors the same dtype).
+ *   dtype DSA_MLA_F32 or DSA_MLA_BF16 (all tensors the same dtype); H <= 65535.
  *
  * mode DSA_MLA_MODE_ABSORBED ("Sparse prefill for GLM", section "Sparse
  * attention": attention in the absorbed latent space over one joined

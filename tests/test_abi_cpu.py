@@ -59,6 +59,7 @@ def _sparse(**kw):
     (dict(mode=1), _lib.INVALID_ARG),                                   # absorbed with rope/v pointers
     (dict(mode=1, q_rope=None, k_rope=None, v=None, dtype=0), _lib.UNSUPPORTED),
     (dict(mode=1, q_rope=None, k_rope=None, v=None, H=24), _lib.UNSUPPORTED),
+    (dict(H=65536), _lib.UNSUPPORTED),                                   # non-absorbed: heads past the grid limit
     (dict(mode=1, q_rope=None, k_rope=None, v=None, L=1 << 25, N=1 << 25, H=64), _lib.UNSUPPORTED),  # L*H >= 2^31
     (dict(), _lib.ARCH),                                                 # valid; no gfx950 device here
     (dict(L=0), _lib.OK), (dict(B=0), _lib.OK),                          # empty -> no-op
