@@ -13,8 +13,8 @@ The line also carries:
                 its bound, timed with HIP events on its launch stream;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                 workload on this host (per stage, with the CPU model and BLAS
-                library), and the oracle of the two dense configurations on a
-                few rows each;
+                library; the masked dense definition on two of the rows), and
+                the oracle of the two dense configurations on a few rows each;
   graph_ms_per_step  the same step captured once into a HIP graph and replayed
                 (value itself is the eagerly launched step);
   pages_protocol_ms  the step timed as the pages time theirs: the mean of
@@ -150,11 +150,18 @@ def cpu_baseline(g, sample):
     oracle.mla_sparse_gather(q64, kv64, idx, 1.0 / np.sqrt(576.0), rows=rows)
     t3 = time.perf_counter()
     dt = t3 - t0
+    # the dense path under the same selection (the definition the gather form equals), on
+    # two of the sampled rows: every one of the 131072 keys scored for each head
+    mrows = rows[:2]
+    t4 = time.perf_counter()
+    oracle.mla_masked_dense(q64, kv64, idx, 1.0 / np.sqrt(576.0), rows=mrows)
+    t5 = time.perf_counter()
     return {"value": sample / dt, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{sample} of the {L} query rows (evenly spaced) of the same workload: canonical fp64 indexer "
                       f"scores over all {N} keys, full stable-sort top-{TOPK}, fp64 gather attention over {H} heads; "
                       f"{dt:.1f} s",
             "stages_s": {"indexer_scores": t1 - t0, "topk_full_sort": t2 - t1, "sparse_gather_attention": t3 - t2},
+            "masked_dense_s_per_row": (t5 - t4) / len(mrows),
             "host": host_info()}
 
 
