@@ -938,6 +938,7 @@ struct RefineLds {
     double dh[64 * DH_ROW];                            // head dots of a band batch
   } u;
   uint16_t qrow[IH * Q_ROW];
+  float wrow[IH];
   double bscore[BAND_CAP];
   int bkey[BAND_CAP];
   float bval[BAND_CAP];
@@ -972,7 +973,7 @@ __device__ __forceinline__ double dmul_rounded(double a, double b) {
 }
 
 __device__ void canonical_scores_batch(const uint16_t* qrow_lds, const float* krows, int nkeys,
-                                       const float* __restrict__ wrow, double* dh, double* out) {
+                                       const float* wrow, double* dh, double* out) {
   const int tid = threadIdx.x, g = tid >> 5, l32 = tid & 31;
   const uint16_t* qh = qrow_lds + l32 * Q_ROW;
   double d[8];
@@ -996,10 +997,19 @@ __device__ void canonical_scores_batch(const uint16_t* qrow_lds, const float* kr
   for (int j = 0; j < 8; ++j) dh[(g + 8 * j) * DH_ROW + l32] = d[j];
   __syncthreads();
   if (tid < nkeys) {
+    // the weight products do not depend on the running sum: eight are formed at a
+    // time, then added in ascending head order
     double sc = 0.0;
-    for (int h = 0; h < IH; ++h) {
-      const double v = dh[tid * DH_ROW + h];
-      sc = sc + dmul_rounded((double)wrow[h], v > 0.0 ? v : 0.0);
+#pragma unroll
+    for (int h0 = 0; h0 < IH; h0 += 8) {
+      double pr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double v = dh[tid * DH_ROW + h0 + e];
+        pr[e] = dmul_rounded((double)wrow[h0 + e], v > 0.0 ? v : 0.0);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc = sc + pr[e];
     }
     out[tid] = sc;
   }
@@ -1254,7 +1264,7 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
         const int h = e / (ID / 8), c = e % (ID / 8);
         *(u32x4*)(sm.qrow + h * Q_ROW + 8 * c) = *(const u32x4*)(q + (size_t)i * IH * ID + 8 * e);
       }
-      const float* wrow = w + (size_t)i * IH;
+      if (tid < IH) sm.wrow[tid] = w[(size_t)i * IH + tid];
       float* krows = (float*)sm.bitmap;                 // 64 rows x 512 B, over the bitmap and the union
       for (int b0 = 0; b0 < nb; b0 += 64) {
         const int nk = min(64, nb - b0);
@@ -1274,24 +1284,30 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
           *(f32x4*)(krows + r * ID + 8 * c + 4) = hi;
         }
         __syncthreads();
-        canonical_scores_batch(sm.qrow, krows, nk, wrow, sm.u.dh, sm.bscore + b0);
+        canonical_scores_batch(sm.qrow, krows, nk, sm.wrow, sm.u.dh, sm.bscore + b0);
       }
-      // rank by (fp64 score desc, key asc); the best need_band are kept
+      // rank by (fp64 score desc, key asc); the best need_band are kept. Up to 64
+      // entries, thread (b, part) counts the entries o = part, part + 4, ... that
+      // precede entry b, and the four partial counts meet in LDS (the histograms are
+      // free by now)
       if (nb <= 64) {
-        if (wave == 0 && lane < 64) {
-          const double s0 = lane < nb ? sm.bscore[lane] : -INFINITY;
-          const int key = lane < nb ? sm.bkey[lane] : INT_MAX;
-          const uint64_t sb = (uint64_t)__double_as_longlong(s0);
-          int r = 0;
-          for (int o = 0; o < nb; ++o) {
-            const uint32_t lo32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sb, o);
-            const uint32_t hi32 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(sb >> 32), o);
-            const double so = __longlong_as_double((long long)(((uint64_t)hi32 << 32) | lo32));
-            const int ko = __builtin_amdgcn_readlane(key, o);
-            r += (so > s0) || (so == s0 && ko < key);
+        const int b = tid & 63, part = tid >> 6;
+        int r = 0;
+        if (b < nb) {
+          const double s0 = sm.bscore[b];
+          const int key = sm.bkey[b];
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            const int o = part + 4 * m;
+            if (o < nb) {
+              const double so = sm.bscore[o];
+              r += (so > s0) || (so == s0 && sm.bkey[o] < key);
+            }
           }
-          if (lane < nb) sm.bsel[lane] = r < need_band;
         }
+        sm.hist[part][b] = r;
+        __syncthreads();
+        if (tid < nb) sm.bsel[tid] = sm.hist[0][tid] + sm.hist[1][tid] + sm.hist[2][tid] + sm.hist[3][tid] < need_band;
       } else
       for (int b = tid; b < nb; b += 256) {
         const double s0 = sm.bscore[b];
