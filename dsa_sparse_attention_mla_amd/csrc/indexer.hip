@@ -57,8 +57,10 @@ constexpr int RANK_WORDS = 4096;        // bitmap words for ordering the output 
 static_assert(RANK_WORDS * 4 >= 64 * IH * 8, "band dots alias the word-prefix table");
 constexpr int BAND_CAP = 256;           // band entries re-scored and ranked in select_refine
 constexpr int BIN_CAP = 1024;           // entries of the threshold bin ranked in select_refine
-constexpr int SR_J = 48;                // candidates per thread (in registers) in select_refine
-constexpr int SR_MAX = SR_J * 256;      // candidates per query select_refine holds
+constexpr int SR_T = 512;               // threads of a select_refine workgroup (one query)
+constexpr int SR_W = SR_T / 64;         // its waves
+constexpr int SR_J = 24;                // candidates per thread (in registers) in select_refine
+constexpr int SR_MAX = SR_J * SR_T;     // candidates per query select_refine holds
 constexpr int NORM_BLOCKS = 1024;
 constexpr int FB_ROWS = 256;            // block size of the fallback kernel
 constexpr int FB_BLOCKS = 256;          // fallback workgroups: one per compute unit
@@ -915,11 +917,12 @@ __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 }
 
 // ---------------------------------------------------------------- 4. select + band refine
-// One workgroup (256 threads) per query. The query's candidates (the concatenated
-// split lists, M <= SR_MAX) sit in registers: thread t holds entries t + 256 j,
-// j < SR_J, with per-thread bit masks for "kept" and "in the band". The LDS holds
-// only the histograms, the band, the staged query and the rank bitmap (about 75 KB,
-// two workgroups per compute unit).
+// One workgroup (SR_T = 512 threads, eight waves) per query: every phase is a short
+// latency-bound step, so more waves per query shorten each of them. The query's
+// candidates (the concatenated split lists, M <= SR_MAX) sit in registers: thread t
+// holds entries t + SR_T j, j < SR_J, with per-thread bit masks for "kept" and "in
+// the band". The LDS holds only the histograms, the band, the staged query and the
+// rank bitmap (about 54 KB); at 128 VGPRs two workgroups share a compute unit.
 //   1. tk = the exact topk-th largest candidate score (linear histogram over
 //      [min, max], then an exact rank count inside the bin that holds it);
 //   2. scores above tk + band are kept, scores in [tk - band, tk + band] form the
@@ -945,20 +948,21 @@ struct RefineLds {
   float binv[BIN_CAP];
   unsigned char bsel[BAND_CAP];
   int hist[4][256];
-  int misc[16];
-  float red[8];
+  int misc[12 + 2 * SR_W];                             // 0-3 selection, 4.. output prefix, then per-wave max, min
+  float red[SR_W];
 };
 // a band batch of 64 fp32 key rows spans the bitmap and the union after it
 static_assert(offsetof(RefineLds, u) == sizeof(uint32_t) * RANK_WORDS, "the union follows the bitmap");
 static_assert(64 * ID * 4 <= sizeof(uint32_t) * RANK_WORDS + sizeof(RefineLds::u), "a band batch fits");
-static_assert(BAND_CAP <= 256, "one thread per band slot in the emit");
+static_assert(BAND_CAP <= SR_T, "one thread per band slot in the emit");
+constexpr int MISC_PRE = 4, MISC_MX = 4 + SR_W, MISC_MN = 4 + 2 * SR_W;
 static_assert(sizeof(RefineLds) <= 80 * 1024, "two refine workgroups per compute unit");
 }  // namespace
 
 // Canonical fp64 scores of up to 64 band keys whose rows are staged in LDS as
 // fp32 (krows, 512 B each; bf16 -> fp32 is exact, so each key value is widened once
-// when staged instead of once per head): lane l32 of 32-lane group g owns head l32 and keys
-// g, g+8, ..., g+56 (eight independent chains). d_h is summed over dims in
+// when staged instead of once per head): lane l32 of 32-lane group g (G = SR_T / 32
+// groups) owns head l32 and keys g, g+G, ... (64 / G independent chains). d_h is summed over dims in
 // ascending order; the head terms are then added in ascending head order by one
 // lane per key. A bf16 x bf16 product is exact in fp64, so the fused multiply-add
 // rounds exactly as a product followed by a sum; the weight products are rounded
@@ -974,27 +978,28 @@ __device__ __forceinline__ double dmul_rounded(double a, double b) {
 
 __device__ void canonical_scores_batch(const uint16_t* qrow_lds, const float* krows, int nkeys,
                                        const float* wrow, double* dh, double* out) {
+  constexpr int G = SR_T / 32, KPT = 64 / G;         // 32-lane groups, keys per thread
   const int tid = threadIdx.x, g = tid >> 5, l32 = tid & 31;
   const uint16_t* qh = qrow_lds + l32 * Q_ROW;
-  double d[8];
+  double d[KPT];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) d[j] = 0.0;
+  for (int j = 0; j < KPT; ++j) d[j] = 0.0;
   for (int c = 0; c < ID / 4; ++c) {
     const uint2 qv = *(const uint2*)(qh + 4 * c);
-    f32x4 kv[8];
+    f32x4 kv[KPT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kv[j] = *(const f32x4*)(krows + (size_t)(g + 8 * j) * ID + 4 * c);
+    for (int j = 0; j < KPT; ++j) kv[j] = *(const f32x4*)(krows + (size_t)(g + G * j) * ID + 4 * c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t qw = (e >> 1) ? qv.y : qv.x;
       const double qd = (double)bf_bits2f((uint16_t)((qw >> (16 * (e & 1))) & 0xFFFFu));
 #pragma unroll
-      for (int j = 0; j < 8; ++j) d[j] = __fma_rn(qd, (double)kv[j][e], d[j]);
+      for (int j = 0; j < KPT; ++j) d[j] = __fma_rn(qd, (double)kv[j][e], d[j]);
     }
   }
   __syncthreads();                      // the head dots overwrite the tail of the key rows
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dh[(g + 8 * j) * DH_ROW + l32] = d[j];
+  for (int j = 0; j < KPT; ++j) dh[(g + G * j) * DH_ROW + l32] = d[j];
   __syncthreads();
   if (tid < nkeys) {
     // the weight products do not depend on the running sum: eight are formed at a
@@ -1023,7 +1028,7 @@ __device__ __forceinline__ uint32_t ord_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(256, 2) void select_refine_kernel(
+__global__ __launch_bounds__(SR_T, 4) void select_refine_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int nsplit, int cap,
     const float* __restrict__ cand_s, const int* __restrict__ cand_i, const int* __restrict__ cand_n,
@@ -1043,7 +1048,7 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
   }
 
   // ---- candidates into registers. Split sp's list fills slots [pre4[sp], pre4[sp] +
-  // cnt rounded up to 4); thread t loads slot groups t + 256 u (4 slots each, one
+  // cnt rounded up to 4); thread t loads slot groups t + SR_T u (4 slots each, one
   // 16-byte load of scores and one of keys). Unused slots hold key -1.
   int cnt[4] = {0, 0, 0, 0}, pre4[5] = {0, 0, 0, 0, 0};
   bool overflow = nsplit > 4;
@@ -1062,7 +1067,7 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
   }
   constexpr int SR_U = SR_J / 4;
   // slot groups of this wave that hold anything: those below M4 / 4
-  const int uw = min(SR_U, (M4 / 4 - wave * 64 + 255) / 256);
+  const int uw = min(SR_U, (M4 / 4 - wave * 64 + SR_T - 1) / SR_T);
   float sc[SR_J];
   int ky[SR_J];
 #pragma unroll
@@ -1070,7 +1075,7 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
     float4 s4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     int4 k4 = {-1, -1, -1, -1};
     if (u < uw) {
-      const int slot = 4 * (tid + 256 * u);
+      const int slot = 4 * (tid + SR_T * u);
       if (slot < M4) {
         const int sp = (slot >= pre4[1]) + (slot >= pre4[2]) + (slot >= pre4[3]);
         const int off = slot - pre4[sp];
@@ -1127,15 +1132,17 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
     umx = wave_max_u32(umx);
     umn = wave_min_u32(umn);
     if (lane == 0) {
-      sm.misc[8 + wave] = (int)umx;
-      sm.misc[12 + wave] = (int)umn;
+      sm.misc[MISC_MX + wave] = (int)umx;
+      sm.misc[MISC_MN + wave] = (int)umn;
     }
-#pragma unroll
-    for (int x = 0; x < 4; ++x) sm.hist[x][tid] = 0;
+    for (int x = tid; x < 4 * 256; x += SR_T) (&sm.hist[0][0])[x] = 0;
     if (tid == 0) sm.misc[2] = 0;
     __syncthreads();
-    umx = max(max((uint32_t)sm.misc[8], (uint32_t)sm.misc[9]), max((uint32_t)sm.misc[10], (uint32_t)sm.misc[11]));
-    umn = min(min((uint32_t)sm.misc[12], (uint32_t)sm.misc[13]), min((uint32_t)sm.misc[14], (uint32_t)sm.misc[15]));
+#pragma unroll
+    for (int x = 0; x < SR_W; ++x) {
+      umx = max(umx, (uint32_t)sm.misc[MISC_MX + x]);
+      umn = min(umn, (uint32_t)sm.misc[MISC_MN + x]);
+    }
     // bin = (u - umn) >> shift with (umx - umn) >> shift < 256
     const uint32_t span = umx - umn;
     const int shift = span < 256u ? 0 : 32 - __clz((int)(span >> 8)) ;
@@ -1157,10 +1164,10 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
         for (int j = 0; j < SR_J; ++j)
           if (j < jw && ky[j] >= 0) {
             const uint64_t d = ord_bits(sc[j]) - umn;
-            if ((d >> hi_sh) == sel) atomicAdd(&sm.hist[wave][(int)((d >> sh) - base)], 1);
+            if ((d >> hi_sh) == sel) atomicAdd(&sm.hist[wave & 3][(int)((d >> sh) - base)], 1);
           }
         __syncthreads();
-        sm.hist[0][tid] += sm.hist[1][tid] + sm.hist[2][tid] + sm.hist[3][tid];
+        if (tid < 256) sm.hist[0][tid] += sm.hist[1][tid] + sm.hist[2][tid] + sm.hist[3][tid];
         __syncthreads();
         if (wave == 0) {
           int bin, above;
@@ -1179,8 +1186,7 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
         if (cnt <= BIN_CAP || sh == 0) break;
         sh = sh >= 8 ? sh - 8 : 0;
         __syncthreads();                  // every thread has read the histogram
-#pragma unroll
-        for (int x = 0; x < 4; ++x) sm.hist[x][tid] = 0;
+        for (int x = tid; x < 4 * 256; x += SR_T) (&sm.hist[0][0])[x] = 0;
         __syncthreads();
       }
       if (cnt > BIN_CAP) {
@@ -1198,7 +1204,7 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
         const int nbin = sm.misc[2];
         // the need-th largest inside the bin: the largest v with #{u >= v} >= need
         float best = -INFINITY;
-        for (int e = tid; e < nbin; e += 256) {
+        for (int e = tid; e < nbin; e += SR_T) {
           const float v = sm.binv[e];
           int c = 0, f = 0;
           for (; f + 4 <= nbin; f += 4) {
@@ -1211,7 +1217,9 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
         best = wave_max(best);
         if (lane == 0) sm.red[wave] = best;
         __syncthreads();
-        tk = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
+        tk = sm.red[0];
+#pragma unroll
+        for (int x = 1; x < SR_W; ++x) tk = fmaxf(tk, sm.red[x]);
       }
     }
     const float hw = band_halfwidth(eps, tk);
@@ -1260,7 +1268,7 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
       return;
     }
     if (nb > 0) {
-      for (int e = tid; e < IH * ID / 8; e += 256) {
+      for (int e = tid; e < IH * ID / 8; e += SR_T) {
         const int h = e / (ID / 8), c = e % (ID / 8);
         *(u32x4*)(sm.qrow + h * Q_ROW + 8 * c) = *(const u32x4*)(q + (size_t)i * IH * ID + 8 * e);
       }
@@ -1268,7 +1276,7 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
       float* krows = (float*)sm.bitmap;                 // 64 rows x 512 B, over the bitmap and the union
       for (int b0 = 0; b0 < nb; b0 += 64) {
         const int nk = min(64, nb - b0);
-        for (int x = tid; x < 64 * (ID / 8); x += 256) {  // row r, chunk c; missing rows repeat row 0
+        for (int x = tid; x < 64 * (ID / 8); x += SR_T) {  // row r, chunk c; missing rows repeat row 0
           const int r = x >> 4, c = x & 15;
           const int n = sm.bkey[b0 + (r < nk ? r : 0)];
           const u32x4 v = *(const u32x4*)(k + (size_t)n * ID + 8 * c);
@@ -1287,9 +1295,9 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
         canonical_scores_batch(sm.qrow, krows, nk, sm.wrow, sm.u.dh, sm.bscore + b0);
       }
       // rank by (fp64 score desc, key asc); the best need_band are kept. Up to 64
-      // entries, thread (b, part) counts the entries o = part, part + 4, ... that
-      // precede entry b, and the four partial counts meet in LDS (the histograms are
-      // free by now)
+      // entries, thread (b, part) counts the entries o = part, part + SR_W, ... that
+      // precede entry b, and the partial counts of the waves meet in LDS (the
+      // histograms are free by now)
       if (nb <= 64) {
         const int b = tid & 63, part = tid >> 6;
         int r = 0;
@@ -1297,19 +1305,25 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
           const double s0 = sm.bscore[b];
           const int key = sm.bkey[b];
 #pragma unroll
-          for (int m = 0; m < 16; ++m) {
-            const int o = part + 4 * m;
+          for (int m = 0; m < 64 / SR_W; ++m) {
+            const int o = part + SR_W * m;
             if (o < nb) {
               const double so = sm.bscore[o];
               r += (so > s0) || (so == s0 && sm.bkey[o] < key);
             }
           }
         }
-        sm.hist[part][b] = r;
+        int* cnts = &sm.hist[0][0];
+        cnts[64 * part + b] = r;
         __syncthreads();
-        if (tid < nb) sm.bsel[tid] = sm.hist[0][tid] + sm.hist[1][tid] + sm.hist[2][tid] + sm.hist[3][tid] < need_band;
+        if (tid < nb) {
+          int rank = 0;
+#pragma unroll
+          for (int x = 0; x < SR_W; ++x) rank += cnts[64 * x + tid];
+          sm.bsel[tid] = rank < need_band;
+        }
       } else
-      for (int b = tid; b < nb; b += 256) {
+      for (int b = tid; b < nb; b += SR_T) {
         const double s0 = sm.bscore[b];
         const int key = sm.bkey[b];
         int r = 0, o = 0;
@@ -1338,14 +1352,14 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
   for (int w0 = 0; w0 < N; w0 += RANK_WORDS * 32) {
     auto in_win = [&](int key) { return key >= w0 && key < w0 + RANK_WORDS * 32; };
     __syncthreads();                    // the band rows (or the last window) are no longer read
-    for (int x = tid; x < RANK_WORDS / 4; x += 256) ((u32x4*)sm.bitmap)[x] = u32x4{0u, 0u, 0u, 0u};
+    for (int x = tid; x < RANK_WORDS / 4; x += SR_T) ((u32x4*)sm.bitmap)[x] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < SR_J; ++j)
       if (((kept >> j) & 1) && in_win(ky[j])) atomicOr(&sm.bitmap[(ky[j] - w0) >> 5], 1u << ((ky[j] - w0) & 31));
     if (band_kept && in_win(bk)) atomicOr(&sm.bitmap[(bk - w0) >> 5], 1u << ((bk - w0) & 31));
     __syncthreads();
-    constexpr int WPT = RANK_WORDS / 256;        // consecutive words per thread
+    constexpr int WPT = RANK_WORDS / SR_T;       // consecutive words per thread
     u32x4 wv[WPT / 4];
     int own = 0;
 #pragma unroll
@@ -1359,10 +1373,10 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
       const int v = __shfl_up(incl, off);
       if (lane >= off) incl += v;
     }
-    if (lane == 63) sm.misc[4 + wave] = incl;
+    if (lane == 63) sm.misc[MISC_PRE + wave] = incl;
     __syncthreads();
     int run = incl - own;
-    for (int x = 0; x < wave; ++x) run += sm.misc[4 + x];
+    for (int x = 0; x < wave; ++x) run += sm.misc[MISC_PRE + x];
 #pragma unroll
     for (int x = 0; x < WPT / 4; ++x) {
       u32x4 pre;
@@ -1373,7 +1387,9 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
       }
       ((u32x4*)sm.u.wpre)[tid * (WPT / 4) + x] = pre;
     }
-    const int total = sm.misc[4] + sm.misc[5] + sm.misc[6] + sm.misc[7];
+    int total = 0;
+#pragma unroll
+    for (int x = 0; x < SR_W; ++x) total += sm.misc[MISC_PRE + x];
     __syncthreads();
     auto emit = [&](int key, float v) {
       const int word = (key - w0) >> 5, bit = (key - w0) & 31;
@@ -1389,7 +1405,7 @@ __global__ __launch_bounds__(256, 2) void select_refine_kernel(
     if (band_kept && in_win(bk)) emit(bk, sm.bval[tid]);
     done += total;
   }
-  for (int e = done + tid; e < topk; e += 256) {
+  for (int e = done + tid; e < topk; e += SR_T) {
     orow[e] = -1;
     if (srow) srow[e] = -INFINITY;
   }
@@ -1706,7 +1722,7 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
   }
   {
     KernelTrace kt("indexer_select_refine", stream);
-    hipLaunchKernelGGL(select_refine_kernel, dim3(L), dim3(256), 0, stream, q, k, w, eps, L, N, topk,
+    hipLaunchKernelGGL(select_refine_kernel, dim3(L), dim3(SR_T), 0, stream, q, k, w, eps, L, N, topk,
                        pl.nsplit, pl.cap, cand_s, cand_i, cand_n, cand_t, fb, idx_out, score_out);
   }
   {
