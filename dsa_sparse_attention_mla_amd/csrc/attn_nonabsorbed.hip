@@ -8,13 +8,12 @@
 // [K_nope(head) | K_rope] (192 entries), the query fragment is [Q_nope | Q_rope],
 // so S^T = K_row . Q^T is a single 192-deep contraction.
 //
-// Decomposition: one workgroup per (head, 64 queries); each of its 4 waves owns
-// 16 queries (one MFMA column each). Keys stream through LDS in tiles of 32,
-// double-buffered. The causal limit of the workgroup's last query bounds the
-// key loop; per-lane masks handle the diagonal.
-//
-// bf16 path: 16x16x32 bf16 MFMA; P is rounded to bf16 for the value product,
-// accumulation is fp32. fp32 path: 16x16x4 fp32 MFMA throughout.
+// fp32 path (the correctness configuration): one workgroup per (head, 16 queries),
+// one 16x16 MFMA column block. Its four waves take the key blocks of 16 in turn
+// (wave w: blocks w, w + 4, ...), each with its own online softmax, and merge their
+// (max, sum, output) through LDS in wave order at the end, so the longest query
+// block's chain of MFMAs is a quarter of its keys. 16x16x4 fp32 MFMA throughout.
+// The bf16 path is described with its kernel below.
 #include <type_traits>
 
 #include "common.h"
@@ -25,205 +24,175 @@ namespace dsa {
 namespace {
 constexpr int DN = 128, DR = 64, DQK = DN + DR, DVN = 128;
 static_assert(DVN == DN, "K_nope and V rows share one address formula");
-constexpr int T = 32;
+constexpr int F_QB = 16;                          // queries per workgroup
+constexpr int F_KB = 16;                          // keys per block
+constexpr int F_KROW = DQK * 4 + 16;              // LDS row [K_nope | K_rope] + pad (784 B)
+constexpr int F_VROW = DVN * 4 + 16;              // LDS V row + pad (528 B)
+constexpr int F_BLK = F_KB * (F_KROW + F_VROW);   // one key block in LDS
+constexpr int F_ROWCH = (DQK + DVN) * 4 / 16;     // 16-byte chunks of one key's K and V rows
+constexpr int F_PER = 4 * F_KB * F_ROWCH / 256;   // chunks per thread for a round of four blocks
+constexpr int F_OROW = DVN + 4;                   // merge record row (floats)
+static_assert(4 * F_KB * F_ROWCH % 256 == 0, "whole chunks per thread");
+static_assert((128 + 4 * F_QB * F_OROW) * 4 <= 4 * F_BLK, "merge records fit the staging area");
 }  // namespace
 
-template <bool BF16>
-struct NonAbsTraits {
-  static constexpr int ESZ = BF16 ? 2 : 4;
-  static constexpr int KN_CH = DN * ESZ / 16;        // 16-byte chunks from K_nope
-  static constexpr int KR_CH = DR * ESZ / 16;        // from K_rope
-  static constexpr int K_CH = KN_CH + KR_CH;
-  static constexpr int V_CH = DVN * ESZ / 16;
-  static constexpr int ROW_CH = K_CH + V_CH;
-  static constexpr int KROWB = K_CH * 16 + 16;       // padded LDS strides
-  static constexpr int VROWB = V_CH * 16 + 16;
-  static constexpr int STAGE = T * (KROWB + VROWB);
-};
-
-template <bool BF16>
-__global__ __launch_bounds__(256) void nonabsorbed_attn_kernel(
-    const void* __restrict__ qn_, const void* __restrict__ qr_, const void* __restrict__ kn_,
-    const void* __restrict__ kr_, const void* __restrict__ v_, void* __restrict__ out_, int L, int N, int H,
+__global__ __launch_bounds__(256) void nonabsorbed_f32_kernel(
+    const float* __restrict__ qn, const float* __restrict__ qr, const float* __restrict__ kn,
+    const float* __restrict__ kr, const float* __restrict__ vv, float* __restrict__ out, int L, int N, int H,
     int causal, float scale_log2) {
-  using Tr = NonAbsTraits<BF16>;
-  constexpr int ESZ = Tr::ESZ;
-  constexpr int NT = 256;
-  constexpr int PER = (T * Tr::ROW_CH + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2][Tr::STAGE];
-
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * F_BLK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int h = blockIdx.y, b = blockIdx.z;
-  // longest rows first: the last query tile is launched first
-  const int qt = gridDim.x - 1 - blockIdx.x;
-  const int i0 = qt * 64;
-  const int i = i0 + wave * 16 + c16;              // this lane's query (column)
+  const int qt = gridDim.x - 1 - blockIdx.x;        // longest rows first
+  const int i0 = qt * F_QB, i = i0 + c16;           // this lane's query (MFMA column)
   const bool qvalid = i < L;
   const int p = N - L + i;                          // its causal limit
-  const int wg_last = min(L - 1, i0 + 63);
-  const int count = causal ? (N - L + wg_last + 1) : N;
+  const int count = causal ? N - L + min(L - 1, i0 + F_QB - 1) + 1 : N;
+  const int nkb = (count + F_KB - 1) / F_KB, nround = (nkb + 3) / 4;
+  const float* knb = kn + (size_t)b * N * H * DN;
+  const float* krb = kr + (size_t)b * N * DR;
+  const float* vb = vv + (size_t)b * N * H * DVN;
 
-  const unsigned char* qn = (const unsigned char*)qn_;
-  const unsigned char* qr = (const unsigned char*)qr_;
-  const unsigned char* kn = (const unsigned char*)kn_ + (size_t)b * N * H * DN * ESZ;
-  const unsigned char* kr = (const unsigned char*)kr_ + (size_t)b * N * DR * ESZ;
-  const unsigned char* vv = (const unsigned char*)v_ + (size_t)b * N * H * DVN * ESZ;
-
-  // Query fragments (B operand): column = query, k = dims of [Q_nope | Q_rope].
-  constexpr int QREG = BF16 ? DQK / 32 : DQK / 4;
-  bf16x8 qb[BF16 ? QREG : 1];
-  float qf[BF16 ? 1 : QREG];
+  // Query fragments (B operand): column = query, k = dims 4 kc + g of [Q_nope | Q_rope].
+  float qf[DQK / 4];
   {
     const int ii = qvalid ? i : 0;
-    const size_t qoff_n = (((size_t)b * L + ii) * H + h) * DN;
-    const size_t qoff_r = (((size_t)b * L + ii) * H + h) * DR;
-    if constexpr (BF16) {
-      const uint16_t* pn = (const uint16_t*)qn + qoff_n + 8 * g;
-      const uint16_t* pr = (const uint16_t*)qr + qoff_r + 8 * g;
+    const float* pn = qn + (((size_t)b * L + ii) * H + h) * DN + g;
+    const float* pr = qr + (((size_t)b * L + ii) * H + h) * DR + g;
 #pragma unroll
-      for (int kc = 0; kc < QREG; ++kc) qb[kc] = kc < DN / 32 ? *(const bf16x8*)(pn + 32 * kc) : *(const bf16x8*)(pr + 32 * (kc - DN / 32));
-    } else {
-      const float* pn = (const float*)qn + qoff_n + g;
-      const float* pr = (const float*)qr + qoff_r + g;
-#pragma unroll
-      for (int kc = 0; kc < QREG; ++kc) qf[kc] = kc < DN / 4 ? pn[4 * kc] : pr[4 * (kc - DN / 4)];
-    }
+    for (int kc = 0; kc < DQK / 4; ++kc) qf[kc] = kc < DN / 4 ? pn[4 * kc] : pr[4 * (kc - DN / 4)];
   }
   f32x4 o[DVN / 16];
 #pragma unroll
   for (int db = 0; db < DVN / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
 
-  u32x4 stg[PER];
-  auto load_tile = [&](int t) {
+  // A round stages blocks 4 rd .. 4 rd + 3 (one per wave) through registers: chunk c
+  // is block c / (F_KB F_ROWCH), key row r of it, 16-byte chunk w of that key's
+  // [K_nope | K_rope | V]; keys past the visible range load zeros.
+  u32x4 stg[F_PER];
+  auto load_round = [&](int rd) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = tid + u * NT;
-      if (c < T * Tr::ROW_CH) {
-        const int r = c / Tr::ROW_CH, w = c - r * Tr::ROW_CH;
-        const int key = t * T + r;
-        u32x4 val = u32x4{0u, 0u, 0u, 0u};
-        if (key < count) {
-          const unsigned char* src;
-          if (w < Tr::KN_CH) src = kn + (((size_t)key * H + h) * DN) * ESZ + w * 16;
-          else if (w < Tr::K_CH) src = kr + ((size_t)key * DR) * ESZ + (w - Tr::KN_CH) * 16;
-          else src = vv + (((size_t)key * H + h) * DVN) * ESZ + (w - Tr::K_CH) * 16;
-          val = *(const u32x4*)src;
-        }
-        stg[u] = val;
+    for (int u = 0; u < F_PER; ++u) {
+      const int c = tid + 256 * u, kq = c / (F_KB * F_ROWCH), rem = c - kq * (F_KB * F_ROWCH);
+      const int r = rem / F_ROWCH, w = rem - r * F_ROWCH;
+      const int key = (4 * rd + kq) * F_KB + r;
+      u32x4 val = u32x4{0u, 0u, 0u, 0u};
+      if (key < count) {
+        const float* src = w < DN / 4 ? knb + ((size_t)key * H + h) * DN + 4 * w
+                         : w < DQK / 4 ? krb + (size_t)key * DR + 4 * (w - DN / 4)
+                                       : vb + ((size_t)key * H + h) * DVN + 4 * (w - DQK / 4);
+        val = *(const u32x4*)src;
       }
+      stg[u] = val;
     }
   };
-  auto store_tile = [&](int s) {
+  auto store_round = [&]() {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = tid + u * NT;
-      if (c < T * Tr::ROW_CH) {
-        const int r = c / Tr::ROW_CH, w = c - r * Tr::ROW_CH;
-        unsigned char* dst = w < Tr::K_CH ? smem[s] + r * Tr::KROWB + w * 16
-                                          : smem[s] + T * Tr::KROWB + r * Tr::VROWB + (w - Tr::K_CH) * 16;
-        *(u32x4*)dst = stg[u];
-      }
+    for (int u = 0; u < F_PER; ++u) {
+      const int c = tid + 256 * u, kq = c / (F_KB * F_ROWCH), rem = c - kq * (F_KB * F_ROWCH);
+      const int r = rem / F_ROWCH, w = rem - r * F_ROWCH;
+      unsigned char* blk = smem + kq * F_BLK;
+      unsigned char* dst = w < DQK / 4 ? blk + r * F_KROW + 16 * w : blk + F_KB * F_KROW + r * F_VROW + 16 * (w - DQK / 4);
+      *(u32x4*)dst = stg[u];
     }
   };
 
-  const int ntiles = (count + T - 1) / T;
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  if (nround > 0) {
+    load_round(0);
+    store_round();
   }
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int s = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const unsigned char* ks = smem[s];
-    const unsigned char* vs = smem[s] + T * Tr::KROWB;
-
-    f32x4 sacc[2];
+  for (int rd = 0; rd < nround; ++rd) {
+    if (rd + 1 < nround) load_round(rd + 1);
+    const int kb = 4 * rd + wave;                   // this wave's key block
+    if (kb < nkb) {
+      const unsigned char* ks = smem + wave * F_BLK;
+      const unsigned char* vs = ks + F_KB * F_KROW;
+      // S^T (16 keys x 16 queries): lane holds query c16, keys 4 g + j of the block
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float* rowp = (const float*)(ks + c16 * F_KROW) + g;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (BF16) {
-        const unsigned char* rowp = ks + (16 * kb + c16) * Tr::KROWB + 16 * g;
-#pragma unroll
-        for (int kc = 0; kc < QREG; ++kc) sacc[kb] = mfma16x16x32(*(const bf16x8*)(rowp + 64 * kc), qb[kc], sacc[kb]);
-      } else {
-        const float* rowp = (const float*)(ks + (16 * kb + c16) * Tr::KROWB) + g;
-#pragma unroll
-        for (int kc = 0; kc < QREG; ++kc) sacc[kb] = mfma16x16x4f32(rowp[4 * kc], qf[kc], sacc[kb]);
-      }
-    }
-    float x[8];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kc = 0; kc < DQK / 4; ++kc) sacc = mfma16x16x4f32(rowp[4 * kc], qf[kc], sacc);
+      float x[4];
+      float tmax = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int key = t * T + 16 * kb + 4 * g + j;
+        const int key = kb * F_KB + 4 * g + j;
         const bool v = key < count && (!causal || key <= p);
-        const float xv = v ? sacc[kb][j] * scale_log2 : -INFINITY;
-        x[kb * 4 + j] = xv;
-        tmax = fmaxf(tmax, xv);
+        x[j] = v ? sacc[j] * scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[j]);
       }
-    tmax = group4_max(tmax);
-    const float mnew = fmaxf(m, tmax);
-    float pv[8];
-    float alpha = 1.f, psum = 0.f;
-    if (mnew == -INFINITY) {
+      tmax = group4_max(tmax);
+      const float mnew = fmaxf(m, tmax);
+      float pv[4];
+      float alpha = 1.f, psum = 0.f;
+      if (mnew == -INFINITY) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = 0.f;
-    } else {
-      alpha = exp2_fast(m - mnew);
+        for (int j = 0; j < 4; ++j) pv[j] = 0.f;
+      } else {
+        alpha = exp2_fast(m - mnew);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pv[e] = exp2_fast(x[e] - mnew);
-        psum += pv[e];
+        for (int j = 0; j < 4; ++j) {
+          pv[j] = exp2_fast(x[j] - mnew);
+          psum += pv[j];
+        }
       }
-    }
-    psum = group4_sum(psum);
-    lsum = lsum * alpha + psum;
-    m = mnew;
-#pragma unroll
-    for (int db = 0; db < DVN / 16; ++db) o[db] *= alpha;
-    if constexpr (BF16) {
-      const bf16x8 pk = pack_bf16x8(pv);
-      const unsigned char* vb = vs + (4 * g + (c16 >> 2)) * Tr::VROWB + 8 * (c16 & 3);
+      psum = group4_sum(psum);
+      lsum = lsum * alpha + psum;
+      m = mnew;
+      // O^T += V^T P^T: MFMA j covers keys 4 g' + j of the lane groups g'; its B
+      // operand is this lane's own weight
 #pragma unroll
       for (int db = 0; db < DVN / 16; ++db) {
-        const short4v lo = lds_read_tr16(vb + 32 * db);
-        const short4v hi = lds_read_tr16(vb + 16 * Tr::VROWB + 32 * db);
-        o[db] = mfma16x16x32(join_bf16x8(lo, hi), pk, o[db]);
+        o[db] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = ((const float*)(vs + (4 * g + j) * F_VROW))[16 * db + c16];
+          o[db] = mfma16x16x4f32(a, pv[j], o[db]);
+        }
       }
-    } else {
-      // MFMA (kb, j) covers keys 16kb + 4g' + j for lane groups g'; its B operand is this lane's own p.
-#pragma unroll
-      for (int db = 0; db < DVN / 16; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float a = ((const float*)(vs + (16 * kb + 4 * g + j) * Tr::VROWB))[16 * db + c16];
-            o[db] = mfma16x16x4f32(a, pv[kb * 4 + j], o[db]);
-          }
     }
-    if (t + 1 < ntiles) store_tile(s ^ 1);
-    __syncthreads();
+    __syncthreads();                                // every wave is done with this round's blocks
+    if (rd + 1 < nround) {
+      store_round();
+      __syncthreads();
+    }
   }
 
-  if (qvalid) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const size_t ooff = (((size_t)b * L + i) * H + h) * DVN + 4 * g;
+  // Merge: wave w's record is its max and sum per query and its 16 x 128 partial
+  // output; wave w then finishes dims 32 w .. 32 w + 31 of the 16 queries.
+  float* rec = (float*)smem;
+  if (g == 0) {
+    rec[wave * F_QB + c16] = m;
+    rec[64 + wave * F_QB + c16] = lsum;
+  }
+  float* orec = rec + 128 + (wave * F_QB + c16) * F_OROW + 4 * g;
 #pragma unroll
-    for (int db = 0; db < DVN / 16; ++db) {
-      if constexpr (BF16) {
-        uint2 w;
-        w.x = (uint32_t)f2bf_bits(o[db][0] * inv) | ((uint32_t)f2bf_bits(o[db][1] * inv) << 16);
-        w.y = (uint32_t)f2bf_bits(o[db][2] * inv) | ((uint32_t)f2bf_bits(o[db][3] * inv) << 16);
-        *(uint2*)((uint16_t*)out_ + ooff + 16 * db) = w;
-      } else {
-        *(f32x4*)((float*)out_ + ooff + 16 * db) = o[db] * inv;
-      }
+  for (int db = 0; db < DVN / 16; ++db) *(f32x4*)(orec + 16 * db) = o[db];
+  __syncthreads();
+  float mw[4], mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = rec[w * F_QB + c16];
+    mx = fmaxf(mx, mw[w]);
+  }
+  float wt[4], lt = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wt[w] = mx == -INFINITY ? 0.f : exp2_fast(mw[w] - mx);
+    lt += rec[64 + w * F_QB + c16] * wt[w];
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qvalid) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int db = 2 * wave + e;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += *(const f32x4*)(rec + 128 + (w * F_QB + c16) * F_OROW + 16 * db + 4 * g) * wt[w];
+      *(f32x4*)(out + (((size_t)b * L + i) * H + h) * DVN + 16 * db + 4 * g) = acc * inv;
     }
   }
 }
@@ -636,9 +605,10 @@ hipError_t launch_nonabsorbed_attn(bool bf16, const void* qn, const void* qr, co
                        causal, scale_log2);
     return hipGetLastError();
   }
-  dim3 grid((L + 63) / 64, H, B), block(256);
+  dim3 grid((L + F_QB - 1) / F_QB, H, B), block(256);
   KernelTrace kt("nonabsorbed_attn_f32", stream);
-  hipLaunchKernelGGL((nonabsorbed_attn_kernel<false>), grid, block, 0, stream, qn, qr, kn, kr, v, out, L, N, H, causal, scale_log2);
+  hipLaunchKernelGGL(nonabsorbed_f32_kernel, grid, block, 0, stream, (const float*)qn, (const float*)qr,
+                     (const float*)kn, (const float*)kr, (const float*)v, (float*)out, L, N, H, causal, scale_log2);
   return hipGetLastError();
 }
 
