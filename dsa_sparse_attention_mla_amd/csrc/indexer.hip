@@ -39,6 +39,7 @@
 //                         visible key.
 // Output rows are in ascending key order, padded with -1.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -984,18 +985,33 @@ __device__ void canonical_scores_batch(const uint16_t* qrow_lds, const float* kr
   double d[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) d[j] = 0.0;
-  for (int c = 0; c < ID / 4; ++c) {
-    const uint2 qv = *(const uint2*)(qh + 4 * c);
-    f32x4 kv[KPT];
+  // chains whose rows lie past the batch for both groups of a wave are skipped: the
+  // wave runs its first kn chains, kn = #{j : 2 w + G j < nkeys}
+  auto chains = [&](auto KN) __attribute__((always_inline)) {
+    constexpr int kn = decltype(KN)::value;
+    for (int c = 0; c < ID / 4; ++c) {
+      const uint2 qv = *(const uint2*)(qh + 4 * c);
+      f32x4 kv[kn];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) kv[j] = *(const f32x4*)(krows + (size_t)(g + G * j) * ID + 4 * c);
+      for (int j = 0; j < kn; ++j) kv[j] = *(const f32x4*)(krows + (size_t)(g + G * j) * ID + 4 * c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t qw = (e >> 1) ? qv.y : qv.x;
-      const double qd = (double)bf_bits2f((uint16_t)((qw >> (16 * (e & 1))) & 0xFFFFu));
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t qw = (e >> 1) ? qv.y : qv.x;
+        const double qd = (double)bf_bits2f((uint16_t)((qw >> (16 * (e & 1))) & 0xFFFFu));
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) d[j] = __fma_rn(qd, (double)kv[j][e], d[j]);
+        for (int j = 0; j < kn; ++j) d[j] = __fma_rn(qd, (double)kv[j][e], d[j]);
+      }
     }
+  };
+  static_assert(KPT == 4, "one specialisation per chain count");
+  const int g0 = 2 * (tid >> 6);
+  const int kn = nkeys > g0 ? min(KPT, (nkeys - g0 + G - 1) / G) : 0;
+  switch (kn) {
+    case 4: chains(std::integral_constant<int, 4>{}); break;
+    case 3: chains(std::integral_constant<int, 3>{}); break;
+    case 2: chains(std::integral_constant<int, 2>{}); break;
+    case 1: chains(std::integral_constant<int, 1>{}); break;
+    default: break;
   }
   __syncthreads();                      // the head dots overwrite the tail of the key rows
 #pragma unroll
