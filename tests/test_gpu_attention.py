@@ -56,6 +56,26 @@ def test_nonabsorbed_fp32_noncausal():
     assert_close(got, ref, TOL_F32, "nonabs f32 non-causal")
 
 
+def test_nonabsorbed_fp32_batch_noncausal_more_queries():
+    """B = 2, non-causal, more queries than keys (L = 40, N = 23): each entry against the oracle."""
+    gs = [gen_nonabsorbed(s, 40, 23, H=5, dtype="f32") for s in (31, 32)]
+    t = {k: torch.stack([dev(g[k]) for g in gs]) for k in gs[0]}
+    out = dm.mla_prefill_dense(t["qn"], t["kn"], q_rope=t["qr"], k_rope=t["kr"], v=t["v"], causal=False)
+    torch.cuda.synchronize()
+    for bi, g in enumerate(gs):
+        f = {k: to_f64(v) for k, v in g.items()}
+        ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], 1 / math.sqrt(192), causal=False)
+        assert_close(host_f64(out[bi]), ref, TOL_F32, f"nonabs f32 batch entry {bi}")
+
+
+def test_nonabsorbed_fp32_long_keys():
+    """16 queries at the end of 1000 keys: 63 key blocks, sixteen rounds of the four-way split."""
+    t, f = _nonabs(33, 16, 1000, 2, "f32")
+    got = _run_nonabs(t)
+    ref = oracle.mla_nonabsorbed(f["qn"], f["qr"], f["kn"], f["kr"], f["v"], 1 / math.sqrt(192))
+    assert_close(got, ref, TOL_F32, "nonabs f32 long keys")
+
+
 def test_nonabsorbed_rope_only_shared_key():
     """Q_nope = 0: only the shared rope key drives the scores."""
     t, f = _nonabs(23, 64, 64, 16, "f32")

@@ -52,6 +52,24 @@ def test_indexer_exact_inputs_ties(L, N, topk):
     _check_rows(idx, ref, np.arange(L), f"exact-input indexer L={L} N={N}")
 
 
+@pytest.mark.parametrize("N,topk", [(5000, 100), (20000, 300)])
+def test_indexer_band_over_64_keys(N, topk):
+    """150 copies of query 0's k-th key share its score exactly, so the band around the
+    k-th score holds more than 64 keys (the refine step's second ranking path) and the
+    lower-index rule picks among the copies; N = 20000 runs the sampled-start kernel."""
+    L = 2
+    g = gen_indexer(130 + topk, L, N)
+    s0 = oracle.indexer_scores(to_f64(g["q_idx"]), to_f64(g["k_idx"]), to_f64(g["w"]), rows=[0])[0]
+    order = np.argsort(-s0[:N - L + 1], kind="stable")        # query 0's visible keys, best first
+    star = int(order[topk - 1])
+    pool = order[3 * topk:]
+    dup = np.random.default_rng(7).choice(pool, 150, replace=False)
+    g["k_idx"].data[dup] = g["k_idx"].data[star]
+    idx, _, ref, s = _run(g, topk)
+    assert int(np.sum(s[0] == s[0][star])) >= 151
+    _check_rows(idx, ref, np.arange(L), f"band over 64 keys N={N} k={topk}")
+
+
 def test_indexer_zero_query_all_ties():
     """q = 0: every visible score is 0, the set is the lowest topk visible indices (exact fallback path)."""
     g = gen_indexer(95, 6, 9000)
