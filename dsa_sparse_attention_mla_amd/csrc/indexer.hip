@@ -1452,7 +1452,7 @@ __global__ __launch_bounds__(FB_ROWS) void exact_fallback_kernel(
   // this block's rows i = blockIdx.x + gridDim.x e: all flags read at once first, so a
   // launch with no flagged row costs one load round trip
   int any = 0;
-  for (int e = tid; blockIdx.x + gridDim.x * e < L; e += FB_ROWS) any |= fb_flag[blockIdx.x + gridDim.x * e];
+  for (int e = tid; (int)blockIdx.x + (int)gridDim.x * e < L; e += FB_ROWS) any |= fb_flag[blockIdx.x + gridDim.x * e];
   if (!__syncthreads_or(any)) return;
   for (int i = blockIdx.x; i < L; i += gridDim.x) {
     if (fb_flag[i] == 0) continue;
@@ -1714,7 +1714,6 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
   float* cand_s = (float*)(base + pl.off_cand_s);
   int* cand_i = (int*)(base + pl.off_cand_i);
   double* scratch = (double*)(base + pl.off_scratch);
-  hipError_t e;
   {
     KernelTrace kt("key_norm_partial", stream);
     hipLaunchKernelGGL(key_norm_partial_kernel, dim3(NORM_BLOCKS), dim3(256), 0, stream, k, N, partial);
