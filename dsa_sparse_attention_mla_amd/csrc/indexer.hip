@@ -811,17 +811,23 @@ __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       auto sample_tile = [&](int t) {
         dma_tile([&](int r) { return (int)((long long)(t * GT + r) * nv_min / SAMPLE); }, t & 1);
       };
+      // pipelined like the main loop: the chain-b sums of tile t - 1 run under the
+      // chain-a MFMAs of tile t, so tile t - 1's scores are stored during tile t
+      auto store_sample = [&](int t, float sv) {
+        const int e = t * 64 + lane;
+        if (active) ss[kh == 0 ? e : SAMPLE - 1 - e] = sv;
+      };
       sample_tile(0);
+      float pa = 0.f;
       for (int t = 0; t < SAMPLE / GT; ++t) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();                  // tile t landed; every wave is done with tile t - 1
         if (t + 1 < SAMPLE / GT) sample_tile(t + 1);
-        phase_a(t & 1);
-        const float pa = phase_b(t & 1);
-        const float sv = combine(pa, tail_b());
-        const int e = t * 64 + lane;
-        if (active) ss[kh == 0 ? e : SAMPLE - 1 - e] = sv;
+        const float pb = phase_a(t & 1);   // + chain-b sums of tile t - 1
+        if (t > 0) store_sample(t - 1, combine(pa, pb));
+        pa = phase_b(t & 1);               // + chain-a sums of tile t
       }
+      store_sample(SAMPLE / GT - 1, combine(pa, tail_b()));
       float thr_q = -INFINITY;
       pair_compact<float, SAMPLE, GQ>(ss, (float*)nullptr, SAMPLE / 2, kh, active, rk, eps_in[ii], thr_q,
                                       hist + qi * 256, red, false);
