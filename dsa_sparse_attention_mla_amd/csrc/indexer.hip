@@ -53,7 +53,7 @@ constexpr int TK = 256;                 // keys per tile of the score kernel
 constexpr int IDX_STAGE = TK * ID * 2;  // the LDS key stage: 256 keys x 256 B (swizzled, unpadded)
 constexpr int QPB = 4;                  // queries per workgroup
 constexpr int IDX_NW = 8;               // waves per score workgroup: 2 per query
-constexpr int SAMPLE = 2048;            // keys scored up front to start the filter threshold
+constexpr int SAMPLE = 1024;            // keys scored up front to start the filter threshold
 constexpr int RANK_WORDS = 4096;        // bitmap words for ordering the output (131072 keys per window)
 static_assert(RANK_WORDS * 4 >= 64 * IH * 8, "band dots alias the word-prefix table");
 constexpr int BAND_CAP = 256;           // band entries re-scored and ranked in select_refine
