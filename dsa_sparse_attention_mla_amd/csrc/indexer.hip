@@ -16,8 +16,10 @@
 //  3. one score kernel, both with 32x32x16 bf16 MFMA scores for 32 heads and the
 //     ReLU, weight and head sum in registers; only candidates leave the chip:
 //     score_list (long contexts: every query of a group sees at least 8 * SAMPLE
-//                         keys): the workgroup scores SAMPLE keys spread over the
-//                         visible range, fixes each query's threshold just below
+//                         keys): the workgroup scores S keys (SAMPLE, or
+//                         SAMPLE_SMALL where the lists have room for the looser
+//                         start) spread over the visible range, fixes each query's
+//                         threshold just below
 //                         the sample's expected k-th largest, streams its key split
 //                         and appends every key at or above the threshold to the
 //                         query's list in memory (no list on chip, no compaction).
@@ -53,7 +55,8 @@ constexpr int TK = 256;                 // keys per tile of the score kernel
 constexpr int IDX_STAGE = TK * ID * 2;  // the LDS key stage: 256 keys x 256 B (swizzled, unpadded)
 constexpr int QPB = 4;                  // queries per workgroup
 constexpr int IDX_NW = 8;               // waves per score workgroup: 2 per query
-constexpr int SAMPLE = 1024;            // keys scored up front to start the filter threshold
+constexpr int SAMPLE = 2048;            // keys scored up front to start the filter threshold
+constexpr int SAMPLE_SMALL = 1024;      // the list kernel's smaller sample, where its lists have room
 constexpr int RANK_WORDS = 4096;        // bitmap words for ordering the output (131072 keys per window)
 static_assert(RANK_WORDS * 4 >= 64 * IH * 8, "band dots alias the word-prefix table");
 constexpr int BAND_CAP = 256;           // band entries re-scored and ranked in select_refine
@@ -639,13 +642,14 @@ constexpr int G_LOADS = G_STAGE / 1024;                  // 1 KB direct loads pe
 constexpr int G_CB = 128;                                // staged survivors per wave
 static_assert(G_LOADS * 1024 == G_STAGE, "tile loads cover the stage");
 static_assert(G_LOADS > 2 * GW && G_LOADS <= 3 * GW, "every wave issues two or three loads per tile");
-static_assert(SAMPLE * GQ * 4 <= 2 * G_STAGE, "sample scores fit two stages");
+static_assert(SAMPLE * GQ * 4 <= 2 * G_STAGE && SAMPLE_SMALL <= SAMPLE, "sample scores fit two stages");
 static_assert(G_NST >= 4, "the sampling prologue takes two stages for tiles and two for scores");
 static_assert(GQ * 256 <= GW * G_CB, "the prologue's histograms fit the staging buffer");
 static_assert(G_CB >= 128, "a half-full buffer still takes a whole tile of survivors");
 }  // namespace
 
 
+template <int S>
 __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_list_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w,
     const float* __restrict__ eps_in, int L, int N, int topk, int span, int nsplit, int cap,
@@ -795,7 +799,7 @@ __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   };
 
-  // Sampling prologue: SAMPLE keys spread evenly over the keys every query of the
+  // Sampling prologue: S keys spread evenly over the keys every query of the
   // group sees; the start threshold sits just below the rk-th largest sample score
   // (see score_filter_kernel). Sample tiles alternate between stages 0 and 1, one
   // tile ahead; the scores go to stages 2-3 as two segments per query (front wave
@@ -804,32 +808,32 @@ __global__ __launch_bounds__(64 * GW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   float thr = -INFINITY;
   {
     const int nv_min = min(N, N - L + (int)blockIdx.x * GQ + 1);
-    const float mean = (float)topk * SAMPLE / (float)max(nv_min, 1);
-    if (nv_min >= 8 * SAMPLE && mean <= SAMPLE / 8) {
-      const int rk = min(SAMPLE / 2, (int)ceilf(mean + 6.f * sqrtf(mean) + 8.f));
-      float* ss = (float*)(stage + 2 * G_STAGE) + qi * SAMPLE;
+    const float mean = (float)topk * S / (float)max(nv_min, 1);
+    if (nv_min >= 8 * S && mean <= S / 8) {
+      const int rk = min(S / 2, (int)ceilf(mean + 6.f * sqrtf(mean) + 8.f));
+      float* ss = (float*)(stage + 2 * G_STAGE) + qi * S;
       auto sample_tile = [&](int t) {
-        dma_tile([&](int r) { return (int)((long long)(t * GT + r) * nv_min / SAMPLE); }, t & 1);
+        dma_tile([&](int r) { return (int)((long long)(t * GT + r) * nv_min / S); }, t & 1);
       };
       // pipelined like the main loop: the chain-b sums of tile t - 1 run under the
       // chain-a MFMAs of tile t, so tile t - 1's scores are stored during tile t
       auto store_sample = [&](int t, float sv) {
         const int e = t * 64 + lane;
-        if (active) ss[kh == 0 ? e : SAMPLE - 1 - e] = sv;
+        if (active) ss[kh == 0 ? e : S - 1 - e] = sv;
       };
       sample_tile(0);
       float pa = 0.f;
-      for (int t = 0; t < SAMPLE / GT; ++t) {
+      for (int t = 0; t < S / GT; ++t) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();                  // tile t landed; every wave is done with tile t - 1
-        if (t + 1 < SAMPLE / GT) sample_tile(t + 1);
+        if (t + 1 < S / GT) sample_tile(t + 1);
         const float pb = phase_a(t & 1);   // + chain-b sums of tile t - 1
         if (t > 0) store_sample(t - 1, combine(pa, pb));
         pa = phase_b(t & 1);               // + chain-a sums of tile t
       }
-      store_sample(SAMPLE / GT - 1, combine(pa, tail_b()));
+      store_sample(S / GT - 1, combine(pa, tail_b()));
       float thr_q = -INFINITY;
-      pair_compact<float, SAMPLE, GQ>(ss, (float*)nullptr, SAMPLE / 2, kh, active, rk, eps_in[ii], thr_q,
+      pair_compact<float, S, GQ>(ss, (float*)nullptr, S / 2, kh, active, rk, eps_in[ii], thr_q,
                                       hist + qi * 256, red, false);
       thr = thr_q;
       lds_barrier();                    // scores and histograms read before the ring reuses them
@@ -1661,7 +1665,8 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
     // the exact fallback.
     const int nv0 = L > 0 ? std::min(N, N - L + 1) : N;
     const double mean = (double)topk * SAMPLE / std::max(nv0, 1);
-    const double expect = topk + 6.0 * std::sqrt((double)topk * nv0 / SAMPLE) + 8.0 * nv0 / SAMPLE;
+    auto expect_of = [&](int S) { return topk + 6.0 * std::sqrt((double)topk * nv0 / S) + 8.0 * nv0 / S; };
+    const double expect = expect_of(SAMPLE);
     auto fits = [&](int n_s, int c_sel) {
       return L > 0 && nv0 >= 8 * SAMPLE && mean <= SAMPLE / 8 && SAMPLE <= c_sel &&
              expect <= 0.6 * (double)n_s * c_sel;
@@ -1683,6 +1688,11 @@ IndexerPlan indexer_plan(int L, int N, int topk, int block) {
         pl.small_off = span <= 65536;
         pl.cap = cap_l;
       }
+      // Every key split of a group scores the same sample, so a smaller one shortens
+      // the prologue; its start is looser (more candidates: a list past its capacity
+      // costs the query the exact fallback), so it is taken only when even its
+      // expected count leaves the lists at most 40% full.
+      pl.sample = expect_of(SAMPLE_SMALL) <= 0.4 * (double)ns * pl.cap ? SAMPLE_SMALL : SAMPLE;
     }
   }
   pl.fb_blocks = L < FB_BLOCKS ? L : FB_BLOCKS;
@@ -1732,8 +1742,9 @@ hipError_t launch_indexer(const IndexerPlan& pl, const uint16_t* q, const uint16
     KernelTrace kt("indexer_score_filter", stream);
     const dim3 grid((L + QPB - 1) / QPB, pl.nsplit), block(64 * IDX_NW);
     if (pl.global_lists)
-      hipLaunchKernelGGL(score_list_kernel, dim3((L + GQ - 1) / GQ, pl.nsplit), dim3(64 * GW), 0, stream, q, k, w, eps, L, N, topk, pl.span, pl.nsplit,
-                         pl.cap, cand_s, cand_i, cand_n, cand_t);
+      hipLaunchKernelGGL(pl.sample == SAMPLE_SMALL ? score_list_kernel<SAMPLE_SMALL> : score_list_kernel<SAMPLE>,
+                         dim3((L + GQ - 1) / GQ, pl.nsplit), dim3(64 * GW), 0, stream, q, k, w, eps, L, N, topk,
+                         pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n, cand_t);
     else if (pl.small_off)
       hipLaunchKernelGGL((score_filter_kernel<uint16_t>), grid, block, 0, stream, q, k, w, eps, L, N,
                          topk, pl.span, pl.nsplit, pl.cap, cand_s, cand_i, cand_n, cand_t);

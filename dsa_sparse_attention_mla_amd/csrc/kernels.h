@@ -48,6 +48,7 @@ struct IndexerPlan {
   int nsplit = 1, span = 0, cap = 0, fb_blocks = 1, nstage = 3;
   bool small_off = false;   // candidate keys stored as 16-bit offsets within the split
   bool global_lists = false;  // long context: sampled start, candidate lists written straight to memory
+  int sample = 0;             // keys the list kernel samples for its start threshold
   size_t off_partial = 0, off_eps = 0, off_cand_n = 0, off_cand_t = 0, off_fb = 0, off_cand_s = 0, off_cand_i = 0, off_scratch = 0;
   size_t ws_bytes = 0, filter_lds = 0, select_lds = 0;
 };

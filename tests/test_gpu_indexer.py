@@ -94,7 +94,7 @@ def test_indexer_sampled_start_adversarial():
     """Keys at the sampled positions are scaled by 4, so the sampled start lands far
     above the true k-th score and the lists miss most of the top-k: the refine step
     must detect it and the exact fallback must still return the oracle's sets."""
-    L, N, topk, sample = 4, 20000, 2048, 1024      # sample: the score kernels' sample size
+    L, N, topk, sample = 4, 20000, 2048, 2048      # the 2048 positions include the 1024-key sample's
     g = gen_indexer(99, L, N)
     nv_min = N - L + 1                       # keys visible to every query of the group
     pos = (np.arange(sample, dtype=np.int64) * nv_min) // sample
@@ -263,7 +263,7 @@ def test_indexer_sampled_start_adversarial_full_size():
     sampled start lands far above its true k-th score; the affected rows must come back
     exact through the fallback. The call's time and the number of rows the fallback
     solved (their returned scores are the canonical ones) are printed."""
-    L, N, topk, sample, gq = 1024, 131072, 2048, 1024, 8   # sample: the score kernels' sample size
+    L, N, topk, sample, gq = 1024, 131072, 2048, 2048, 8   # the sample this workload takes
     g = gen_indexer(1070, L, N)
     nv_min = N - L + 1                       # keys every query of the first group sees
     pos = (np.arange(sample, dtype=np.int64) * nv_min) // sample
