@@ -958,7 +958,7 @@ struct RefineLds {
   float bval[BAND_CAP];
   float binv[BIN_CAP];
   unsigned char bsel[BAND_CAP];
-  int hist[4][256];
+  int hist[4][256];                                    // 256-bin histograms; waves w and w + 4 share one
   int misc[12 + 2 * SR_W];                             // 0-3 selection, 4.. output prefix, then per-wave max, min
   float red[SR_W];
 };
